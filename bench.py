@@ -1,0 +1,348 @@
+"""Benchmark of the paged-KV-attention hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+                    [--extra] [--only decode|mixed|prefix|long] [--splits S]
+
+A step is one pass of the whole path over one batch: slot mapping of the new
+tokens, reshape_and_cache of their K/V, then attention (decode for the decode
+batch, mixed for the chunked-prefill batch).  Inputs are resident in HBM
+before timing starts; several copies of the KV pool are rotated so that
+successive steps do not hit in the 256 MB Infinity Cache.
+
+Headline (`value`): algorithmic HBM bytes per decode step / step time, on the
+64-request Llama-3-8B-layer decode batch.  Also reported: tokens/s of the
+mixed chunked-prefill step, the roofline of the attention call (HIP events on
+the launch stream), and the CPU oracle timed on a bounded sample.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged-attn decode HBM GB/s (% peak) + mixed-step tokens/sec, 1 MI355X"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+WORKLOADS = {
+    "decode": "decode_bf16_64req",
+    "mixed": "mixed_chunked_prefill_bf16",
+    "prefix": "prefix_shared_decode_bf16",
+    "long": "long_context_decode_bf16",
+}
+
+DESCR = {
+    "decode_bf16_64req": "Llama-3-8B layer decode (Hq 32, Hkv 8, D 128, bf16, block 16): 64 requests, "
+                         "seq_len ~ U[512,4096], pool 20000 blocks, 1 new token each",
+    "mixed_chunked_prefill_bf16": "Llama-3-8B layer chunked-prefill step: 512-token chunk on 1024 cached, "
+                                  "2 x 10-token prefills, 61 decodes at 2048 (593 query tokens)",
+    "prefix_shared_decode_bf16": "Llama-3-8B layer decode, 256 requests sharing a 1024-token prefix "
+                                 "(64 blocks) + private suffix U[64,512]",
+    "long_context_decode_bf16": "Llama-3-8B layer decode, 16 requests at 32768 tokens, pool 36000 blocks",
+}
+
+
+# --------------------------------------------------------------------------
+# algorithmic byte / flop counts (what the method itself must move)
+# --------------------------------------------------------------------------
+
+
+def alg_counts(w):
+    """Bytes each part of one step must move, and the attention's flops."""
+    esz = 4 if w.dtype == "f32" else 2
+    Hq, Hkv, D, B = w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size
+    T, R = w.num_tokens, w.num_seqs
+    kb = 2 * Hkv * D * esz                       # K+V bytes per token per layer
+    ql = w.q_lens
+    rows = ql > 0
+    keys_read = int(w.seq_lens[rows].astype(np.int64).sum())
+    # unique KV bytes: shared physical blocks counted once
+    used_tokens = 0
+    seen = set()
+    for r in np.nonzero(rows)[0]:
+        L = int(w.seq_lens[r])
+        nb = -(-L // B)
+        for j in range(nb):
+            blk = int(w.block_table[r, j])
+            n_tok = min(B, L - j * B)
+            if blk in seen:
+                continue
+            seen.add(blk)
+            used_tokens += n_tok
+    nblocks = int(sum(-(-int(L) // B) for L in w.seq_lens[rows]))
+    attn_bytes_logical = keys_read * kb + 2 * T * Hq * D * esz + nblocks * 4 + R * 4 * 3
+    attn_bytes_unique = used_tokens * kb + 2 * T * Hq * D * esz + nblocks * 4 + R * 4 * 3
+    scatter_bytes = 2 * T * kb + T * 8
+    slot_bytes = T * 4 + R * 8 + T * 8
+    # flops: 4*D per (query head, visible key) pair (QK^T and PV)
+    pairs = 0
+    for r in np.nonzero(rows)[0]:
+        c, n = int(w.num_computed[r]), int(ql[r])
+        pairs += n * c + n * (n + 1) // 2
+    flops = 4 * D * Hq * pairs
+    chunk_pairs = 0
+    for r in np.nonzero(ql > 1)[0]:
+        c, n = int(w.num_computed[r]), int(ql[r])
+        chunk_pairs += n * c + n * (n + 1) // 2
+    return dict(attn_logical=attn_bytes_logical, attn_unique=attn_bytes_unique,
+                scatter=scatter_bytes, slots=slot_bytes, flops=flops,
+                chunk_flops=4 * D * Hq * chunk_pairs, kv_bytes_per_token=kb)
+
+
+# --------------------------------------------------------------------------
+# GPU side
+# --------------------------------------------------------------------------
+
+
+class Stepper:
+    """Device copies of one workload and the step of the hot path over them."""
+
+    def __init__(self, w, rotations: int, splits: int):
+        import torch
+        import paged_kv_attention_07_amd as pa
+        self.pa, self.torch, self.w, self.splits = pa, torch, w, splits
+        tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[w.dtype]
+
+        def dev(a):
+            if w.dtype == "f32":
+                return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(tdt).cuda()
+
+        def i32(a):
+            return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+
+        base = dev(w.pool)
+        self.pools = [base] + [base.clone() for _ in range(rotations - 1)]
+        self.q, self.kn, self.vn = dev(w.q), dev(w.k_new), dev(w.v_new)
+        self.bt, self.sl = i32(w.block_table), i32(w.seq_lens)
+        self.qsl, self.nc = i32(w.query_start_loc), i32(w.num_computed)
+        self.out = torch.empty_like(self.q)
+        self.slots = torch.empty(w.num_tokens, dtype=torch.int64, device="cuda")
+        nbytes = pa.pa_attention_workspace_size(w.num_seqs, w.num_tokens, w.num_q_heads,
+                                                w.num_kv_heads, w.head_dim, w.max_seq_len,
+                                                w.max_query_len, splits)
+        self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device="cuda")
+        self.decode = w.is_decode_only
+
+    def attention(self, kv):
+        w, pa = self.w, self.pa
+        if self.decode:
+            pa.pa_attention_decode(self.q, kv, self.bt, self.sl, w.scale, w.max_seq_len,
+                                   out=self.out, workspace=self.ws, num_splits=self.splits)
+        else:
+            pa.pa_attention_mixed(self.q, kv, self.bt, self.sl, self.qsl, self.nc, w.scale,
+                                  w.max_query_len, w.max_seq_len, out=self.out,
+                                  workspace=self.ws, num_splits=self.splits)
+
+    def step(self, i, ev=None):
+        pa, w = self.pa, self.w
+        kv = self.pools[i % len(self.pools)]
+        pa.pa_compute_slot_mapping(self.bt, self.qsl, self.nc, w.num_tokens, w.block_size,
+                                   out=self.slots)
+        pa.pa_reshape_and_cache(self.kn, self.vn, kv, self.slots)
+        if ev is not None:
+            ev[0].record()
+        self.attention(kv)
+        if ev is not None:
+            ev[1].record()
+
+    def run(self, steps: int, warmup: int):
+        torch = self.torch
+        for i in range(warmup):
+            self.step(i)
+        torch.cuda.synchronize()
+        events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            self.step(warmup + i, events[i])
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        attn_ms = [a.elapsed_time(b) for a, b in events]
+        return (t1 - t0) * 1e3 / steps, attn_ms
+
+
+def gpu_info():
+    import torch
+    p = torch.cuda.get_device_properties(0)
+    return {"name": p.name, "gcn_arch": getattr(p, "gcnArchName", ""),
+            "cus": p.multi_processor_count, "hbm_gb": round(p.total_memory / 2**30, 1)}
+
+
+# --------------------------------------------------------------------------
+# CPU oracle baseline (bounded sample)
+# --------------------------------------------------------------------------
+
+
+def cpu_baseline(w, budget_s: float = 12.0):
+    """Time the oracle (as it stands, BLAS limited to one thread) on the
+    first n requests of the same batch, n chosen so the run takes about
+    `budget_s`; scaled to the same unit as the GPU figure (GB/s of
+    algorithmic attention bytes)."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    try:
+        if ctx is not None:
+            ctx.__enter__()
+        slots = oracle.slot_mapping(w.block_table, w.query_start_loc, w.num_computed, w.block_size)
+        t0 = time.perf_counter()
+        pool = oracle.reshape_and_cache(w.pool, w.k_new, w.v_new, slots)
+        t_scatter = time.perf_counter() - t0
+        order = [r for r in range(w.num_seqs) if w.q_lens[r] > 0]
+        # requests one at a time, in batch order, until the time budget is used
+        sample, t_attn = [], 0.0
+        for r in order:
+            t0 = time.perf_counter()
+            oracle.paged_attention(w.q, pool, w.block_table, w.seq_lens, w.query_start_loc,
+                                   w.num_computed, w.scale, w.dtype, requests=[r])
+            t_attn += time.perf_counter() - t0
+            sample.append(r)
+            if t_attn >= budget_s:
+                break
+        n = len(sample)
+    finally:
+        if ctx is not None:
+            ctx.__exit__(None, None, None)
+    esz = 4 if w.dtype == "f32" else 2
+    kb = 2 * w.num_kv_heads * w.head_dim * esz
+    keys = int(sum(int(w.seq_lens[r]) for r in sample))
+    toks = int(sum(int(w.q_lens[r]) for r in sample))
+    byts = keys * kb + 2 * toks * w.num_q_heads * w.head_dim * esz
+    # scatter of the sample's tokens is charged pro rata
+    t_total = t_attn + t_scatter * toks / max(1, w.num_tokens)
+    return {
+        "value": round(byts / t_total / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+        "sample": f"{n} of {len(order)} requests of {w.name} (slot mapping excluded, "
+                  f"scatter charged pro rata): {toks} query tokens, {keys} keys, "
+                  f"{t_total:.2f} s fp64 numpy, BLAS 1 thread",
+        "tokens_per_s": round(toks / t_total, 3),
+        "cpu": platform.processor() or platform.machine(),
+        "host_cores_available": len(os.sched_getaffinity(0)),
+    }
+
+
+# --------------------------------------------------------------------------
+
+
+def measure(name, args, rotations):
+    from workloads import make_workload
+    t0 = time.perf_counter()
+    w = make_workload(name)
+    print(f"[bench] {name}: generated in {time.perf_counter() - t0:.1f}s", file=sys.stderr,
+          flush=True)
+    st = Stepper(w, rotations, args.splits)
+    ms_step, attn_ms = st.run(args.steps, args.warmup)
+    c = alg_counts(w)
+    attn_avg = float(np.mean(attn_ms))
+    res = dict(w=w, counts=c, ms_step=ms_step, attn_ms_avg=attn_avg,
+               attn_ms_p10=float(np.percentile(attn_ms, 10)),
+               attn_ms_p90=float(np.percentile(attn_ms, 90)))
+    print(f"[bench] {name}: {ms_step * 1e3:.1f} us/step, attention {attn_avg * 1e3:.1f} us",
+          file=sys.stderr, flush=True)
+    del st
+    import torch
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--splits", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--extra", action="store_true", help="also time the prefix-shared and "
+                    "long-context decode batches")
+    ap.add_argument("--only", choices=sorted(WORKLOADS), default=None)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    rot = 4
+    names = [args.only] if args.only else ["decode", "mixed"] + (["prefix", "long"] if args.extra else [])
+    results = {k: measure(WORKLOADS[k], args, rot if k != "long" else 2) for k in names}
+
+    head = results.get("decode") or next(iter(results.values()))
+    w, c = head["w"], head["counts"]
+    step_bytes = c["attn_logical"] + c["scatter"] + c["slots"]
+    value = step_bytes / (head["ms_step"] * 1e-3) / 1e9
+    achieved = c["attn_logical"] / (head["attn_ms_avg"] * 1e-3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "description": DESCR.get(w.name, ""),
+                   "num_seqs": w.num_seqs, "query_tokens": w.num_tokens,
+                   "keys": int(w.seq_lens.sum()), "pool_blocks": w.num_blocks,
+                   "step": "slot_mapping + reshape_and_cache + attention",
+                   "pool_rotation": rot, "num_splits": args.splits or "auto"},
+        "pct_peak_hbm": round(100 * value / HBM_PEAK_GBS, 2),
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "pa_attention_decode (decode_split_kernel + decode_merge_kernel)",
+            "alg_bytes_per_launch": int(c["attn_logical"]),
+            "avg_launch_us": round(head["attn_ms_avg"] * 1e3, 2),
+            "p10_us": round(head["attn_ms_p10"] * 1e3, 2),
+            "p90_us": round(head["attn_ms_p90"] * 1e3, 2),
+        },
+        "gpu": gpu_info(),
+    }
+    if "mixed" in results:
+        m = results["mixed"]
+        mw, mc = m["w"], m["counts"]
+        mbytes = mc["attn_logical"] + mc["scatter"] + mc["slots"]
+        line["mixed_step"] = {
+            "workload": mw.name, "tokens_per_s": round(mw.num_tokens / (m["ms_step"] * 1e-3), 1),
+            "ms_per_step": round(m["ms_step"], 5), "query_tokens": mw.num_tokens,
+            "hbm_gbs": round(mbytes / (m["ms_step"] * 1e-3) / 1e9, 1),
+            "pct_peak_hbm": round(100 * mbytes / (m["ms_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+            "attention_avg_us": round(m["attn_ms_avg"] * 1e3, 2),
+            "chunk_gflop": round(mc["chunk_flops"] / 1e9, 3),
+        }
+    for key in ("prefix", "long"):
+        if key in results:
+            r = results[key]
+            rw, rc = r["w"], r["counts"]
+            line[f"{key}_decode"] = {
+                "workload": rw.name,
+                "attention_avg_us": round(r["attn_ms_avg"] * 1e3, 2),
+                "hbm_gbs_unique": round(rc["attn_unique"] / (r["attn_ms_avg"] * 1e-3) / 1e9, 1),
+                "effective_gbs_logical": round(rc["attn_logical"] / (r["attn_ms_avg"] * 1e-3) / 1e9, 1),
+                "ms_per_step": round(r["ms_step"], 5),
+            }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,181 @@
+/*
+ * pa.h -- C ABI of the MI355X (gfx950) paged-KV-attention library (libpa.so).
+ *
+ * Sources for what each call computes (web pages, cited by title + section):
+ *   [P1] "vLLM 架构源码解析（一）：从 API 请求到 Token 生成"
+ *   [P2] "Inside vLLM: Anatomy of a High-Throughput LLM Inference System"
+ *   [P4] "vllm v1 源码精读（三）：KV Cache 管理、Chunked Prefill 与异步架构"
+ *
+ * Conventions shared by every entry point
+ *   - Pointers are DEVICE pointers owned by the caller unless marked (host).
+ *     The library keeps no pointer after a call returns and never allocates.
+ *   - Every call is asynchronous on `stream` (a hipStream_t passed as void*;
+ *     NULL = the default stream) and never synchronises.
+ *   - Tensors are dense, row-major, with the shapes given below.
+ *   - KV cache: one tensor [num_blocks, 2, block_size, num_kv_heads, head_dim]
+ *     ([P4] §3.2/§3.3); kv_cache[b][0] is block b's K, kv_cache[b][1] its V.
+ *     block_size must be 16; head_dim 64 or 128; dtype one of pa_dtype.
+ *     Queries, new keys/values and outputs have the cache's dtype.
+ *   - Host-visible arguments (sizes, dtype, alignment, workspace size) are
+ *     checked before anything is launched; a failed check launches nothing
+ *     and returns a negative pa_status.  Device-resident metadata (tables,
+ *     lengths, slots) is trusted, as the pages' model runner trusts its
+ *     scheduler: preconditions are listed per call; violating them gives
+ *     unspecified results (never a write outside `out`/`kv_cache`/workspace,
+ *     as long as table entries for positions < seq_len are valid block ids).
+ *   - Thread safety: no global mutable state; concurrent calls on different
+ *     streams must not share `out`, `kv_cache` slots being written, or
+ *     `workspace`.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_F16 = 2 } pa_dtype;
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = -1, /* null pointer, negative size, bad stride/shape   */
+  PA_ERR_UNSUPPORTED = -2, /* block_size != 16, head_dim, dtype, head grouping */
+  PA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required      */
+  PA_ERR_HIP = -4          /* a HIP launch reported an error                  */
+} pa_status;
+
+/* Static, NUL-terminated description of a status code. */
+const char* pa_status_string(int status);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int pa_version(void);
+
+/*
+ * pa_compute_slot_mapping -- physical slot of every query token of a step.
+ *   [P4] §3.4: slot = block_table[r][pos / block_size] * block_size
+ *                     + pos % block_size,
+ *   with pos = num_computed_tokens[r] + i for the i-th new token of request r
+ *   ([P1] §3.3.2: prefill positions start at the computed count).
+ *
+ *   slot_mapping        out [num_tokens] int64, varlen token order.
+ *   block_table         [num_seqs, block_table_stride] int32, -1 = unused.
+ *   query_start_loc     [num_seqs + 1] int32, prefix sums of per-request
+ *                       query counts; precondition qsl[0] = 0,
+ *                       qsl[num_seqs] = num_tokens, non-decreasing.
+ *   num_computed_tokens [num_seqs] int32.
+ *   A token whose table entry is -1 gets a negative slot (skipped by
+ *   pa_reshape_and_cache).
+ */
+int pa_compute_slot_mapping(int64_t* slot_mapping, const int32_t* block_table,
+                            int32_t block_table_stride,
+                            const int32_t* query_start_loc,
+                            const int32_t* num_computed_tokens, int32_t num_seqs,
+                            int32_t num_tokens, int32_t block_size, void* stream);
+
+/*
+ * pa_reshape_and_cache -- scatter this step's K/V rows into their slots.
+ *   [P1] §3.3.3 (write into the KV cache by slot_mapping before attention),
+ *   [P4] §3.4 (reshape_and_cache_flash: key/value scattered to physical slots).
+ *   For every t with s = slot_mapping[t] >= 0:
+ *     kv_cache[s / 16][0][s % 16][:][:] = key[t][:][:]
+ *     kv_cache[s / 16][1][s % 16][:][:] = value[t][:][:]
+ *   The copy is bit-exact; nothing else in the cache changes.
+ *
+ *   key, value    [num_tokens, num_kv_heads, head_dim], cache dtype.
+ *   kv_cache      [num_blocks, 2, block_size, num_kv_heads, head_dim].
+ *   slot_mapping  [num_tokens] int64; negative = padding token, skipped.
+ *   Preconditions: 0 <= slot < num_blocks * block_size or slot < 0; slots
+ *   distinct within one call.  All three tensors 16-byte aligned.
+ */
+int pa_reshape_and_cache(const void* key, const void* value, void* kv_cache,
+                         const int64_t* slot_mapping, int32_t num_tokens,
+                         int64_t num_blocks, int32_t block_size,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                         void* stream);
+
+/*
+ * pa_attention_workspace_size -- bytes of fp32 scratch the attention calls
+ * need for their split-KV partial results (max, sum, unnormalised output per
+ * query head and partition).  Pure function of its arguments; returns 0 for
+ * arguments the attention calls would reject.  `num_splits` = 0 selects the
+ * library's own partition count (the same value the attention call uses).
+ */
+size_t pa_attention_workspace_size(int32_t num_seqs, int32_t num_tokens,
+                                   int32_t num_q_heads, int32_t num_kv_heads,
+                                   int32_t head_dim, int32_t max_seq_len,
+                                   int32_t max_query_len, int32_t num_splits);
+
+/*
+ * pa_attention_decode -- paged attention for one new query token per request.
+ *   [P1] §3.3.3 / §4.2 (paged_attention(q, kv_cache, block_tables,
+ *   context_lens)), [P2] §3.3 (decode reads the cached history).
+ *   For request r and query head h (kv head g = h / (num_q_heads /
+ *   num_kv_heads)), with L = seq_lens[r] keys at positions 0..L-1 stored at
+ *   kv_cache[block_table[r][j/16]][.][j%16][g]:
+ *     out[r][h] = sum_j softmax_j(scale * <q[r][h], K_j>) * V_j.
+ *   Long contexts are split over work-groups and merged exactly
+ *   (partition-and-reduce); the split is balanced over the whole batch.
+ *
+ *   out, q        [num_seqs, num_q_heads, head_dim], cache dtype.
+ *   block_table   [num_seqs, block_table_stride] int32.
+ *   seq_lens      [num_seqs] int32; precondition 1 <= seq_lens[r] <=
+ *                 max_seq_len (a 0 length leaves that row unwritten).
+ *   max_seq_len   (host) bound used to size the split.
+ *   num_q_heads   multiple of num_kv_heads, group size 1, 2, 4 or 8.
+ *   workspace     >= pa_attention_workspace_size(num_seqs, num_seqs, ...,
+ *                 max_seq_len, 1, num_splits) bytes, 256-byte aligned; its
+ *                 contents on entry do not matter.
+ *   num_splits    partitions of the batch per kv head; 0 = library choice.
+ */
+int pa_attention_decode(void* out, const void* q, const void* kv_cache,
+                        int64_t num_blocks, int32_t block_size,
+                        int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                        const int32_t* block_table, int32_t block_table_stride,
+                        const int32_t* seq_lens, int32_t num_seqs,
+                        int32_t max_seq_len, int32_t num_q_heads, float scale,
+                        void* workspace, size_t workspace_bytes,
+                        int32_t num_splits, void* stream);
+
+/*
+ * pa_attention_mixed -- attention for a chunked-prefill mixed batch.
+ *   [P4] §4.2 (prefill chunks and decodes packed in one 1-D varlen batch;
+ *   each sequence handled by its own bounds; a chunk attends its cached
+ *   history plus the earlier tokens of the chunk), [P2] §3.4 step 3
+ *   (each sequence attends only to its own tokens).
+ *   Token i of request r is row t = query_start_loc[r] + i at absolute
+ *   position pos = num_computed_tokens[r] + i; it attends keys 0..pos:
+ *     out[t][h] = sum_{j<=pos} softmax_j(scale * <q[t][h], K_j>) * V_j.
+ *   Requests with one query take the decode path; longer ones the MFMA
+ *   tile path with a causal mask.
+ *
+ *   out, q              [num_tokens, num_q_heads, head_dim], cache dtype.
+ *   seq_lens            [num_seqs]: keys of the request's last query,
+ *                       = num_computed_tokens[r] + q_len[r].
+ *   query_start_loc     [num_seqs + 1]: qsl[0] = 0, qsl[num_seqs] =
+ *                       num_tokens; q_len = 0 requests produce no rows.
+ *   num_computed_tokens [num_seqs].
+ *   max_query_len, max_seq_len (host) bounds.
+ *   workspace           >= pa_attention_workspace_size(num_seqs, num_tokens,
+ *                       ..., max_seq_len, max_query_len, num_splits) bytes.
+ *   The new tokens' K/V must already be in the cache (pa_reshape_and_cache
+ *   on the same stream first, as in [P1] §3.3.3).
+ */
+int pa_attention_mixed(void* out, const void* q, const void* kv_cache,
+                       int64_t num_blocks, int32_t block_size,
+                       int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                       const int32_t* block_table, int32_t block_table_stride,
+                       const int32_t* seq_lens, const int32_t* query_start_loc,
+                       const int32_t* num_computed_tokens, int32_t num_seqs,
+                       int32_t num_tokens, int32_t max_query_len,
+                       int32_t max_seq_len, int32_t num_q_heads, float scale,
+                       void* workspace, size_t workspace_bytes,
+                       int32_t num_splits, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

@@ -1,0 +1,220 @@
+"""Paged KV attention on MI355X (gfx950): Python binding of libpa.so.
+
+The functions here only marshal arguments: they check tensor metadata,
+allocate outputs / workspace with torch (device memory plumbing) and call the
+C ABI declared in include/pa.h on torch's current HIP stream.  Every step of
+the computation runs in the library's HIP kernels; there is no fallback.
+If libpa.so has not been built, importing this package raises ImportError.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+__all__ = [
+    "PAError", "lib", "library_path", "DTYPE_CODES",
+    "pa_compute_slot_mapping", "pa_reshape_and_cache",
+    "pa_attention_workspace_size", "pa_attention_decode", "pa_attention_mixed",
+    "pa_status_string", "pa_version",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libpa.so")
+
+if not os.path.exists(library_path):
+    raise ImportError(
+        f"{library_path} is missing: build the HIP library first "
+        "(python -m paged_kv_attention_07_amd.build)")
+
+# torch is imported before the library is loaded: libpa.so needs
+# libamdhip64.so.7, and torch bundles its own copy under that soname.  Loading
+# torch first makes the loader reuse torch's HIP runtime, so the device memory
+# and streams torch hands over belong to the runtime that launches the
+# kernels.  Loading libpa.so first would map a second HIP/HSA runtime into the
+# process, and torch's allocations would be invalid for it.
+import torch as _torch_module  # noqa: E402,F401
+
+lib = ctypes.CDLL(library_path)
+
+_i32, _i64, _sz, _f32, _vp = (ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t,
+                              ctypes.c_float, ctypes.c_void_p)
+
+lib.pa_status_string.argtypes = [ctypes.c_int]
+lib.pa_status_string.restype = ctypes.c_char_p
+lib.pa_version.argtypes = []
+lib.pa_version.restype = ctypes.c_int
+lib.pa_compute_slot_mapping.argtypes = [_vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _vp]
+lib.pa_compute_slot_mapping.restype = ctypes.c_int
+lib.pa_reshape_and_cache.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32, _i32, _vp]
+lib.pa_reshape_and_cache.restype = ctypes.c_int
+lib.pa_attention_workspace_size.argtypes = [_i32] * 8
+lib.pa_attention_workspace_size.restype = _sz
+lib.pa_attention_decode.argtypes = [
+    _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32,   # out q kv NB B Hkv D dtype
+    _vp, _i32, _vp, _i32, _i32, _i32, _f32,          # bt stride seq_lens R max_L Hq scale
+    _vp, _sz, _i32, _vp]                             # ws ws_bytes splits stream
+lib.pa_attention_decode.restype = ctypes.c_int
+lib.pa_attention_mixed.argtypes = [
+    _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32,   # out q kv NB B Hkv D dtype
+    _vp, _i32, _vp, _vp, _vp, _i32, _i32,            # bt stride seq_lens qsl nc R T
+    _i32, _i32, _i32, _f32,                          # max_q max_L Hq scale
+    _vp, _sz, _i32, _vp]                             # ws ws_bytes splits stream
+lib.pa_attention_mixed.restype = ctypes.c_int
+
+PA_F32, PA_BF16, PA_F16 = 0, 1, 2
+DTYPE_CODES = {"f32": PA_F32, "bf16": PA_BF16, "f16": PA_F16}
+
+
+class PAError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: {lib.pa_status_string(status).decode()} (status {status})")
+
+
+def pa_status_string(status: int) -> str:
+    return lib.pa_status_string(status).decode()
+
+
+def pa_version() -> int:
+    return lib.pa_version()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise PAError(fn, status)
+
+
+def _torch():
+    import torch  # deferred so that the ABI can be loaded without torch's GPU state
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    m = {torch.float32: PA_F32, torch.bfloat16: PA_BF16, torch.float16: PA_F16}
+    if t.dtype not in m:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return m[t.dtype]
+
+
+def _dev(t, name: str, dtype=None, ndim: Optional[int] = None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    return t.data_ptr()
+
+
+def _stream():
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _cache_dims(kv_cache):
+    if kv_cache.dim() != 5 or kv_cache.shape[1] != 2:
+        raise ValueError("kv_cache must be [num_blocks, 2, block_size, num_kv_heads, head_dim]")
+    nb, _, bs, hkv, d = kv_cache.shape
+    return int(nb), int(bs), int(hkv), int(d)
+
+
+def pa_compute_slot_mapping(block_table, query_start_loc, num_computed_tokens,
+                            num_tokens: int, block_size: int = 16, out=None):
+    """Slot of every query token (int64 [num_tokens]); see pa.h."""
+    torch = _torch()
+    R = int(num_computed_tokens.shape[0])
+    if out is None:
+        out = torch.empty(num_tokens, dtype=torch.int64, device=block_table.device)
+    st = lib.pa_compute_slot_mapping(
+        _dev(out, "out", torch.int64, 1), _dev(block_table, "block_table", torch.int32, 2),
+        int(block_table.shape[1]), _dev(query_start_loc, "query_start_loc", torch.int32, 1),
+        _dev(num_computed_tokens, "num_computed_tokens", torch.int32, 1), R, int(num_tokens),
+        int(block_size), _stream())
+    _check("pa_compute_slot_mapping", st)
+    return out
+
+
+def pa_reshape_and_cache(key, value, kv_cache, slot_mapping) -> None:
+    """Scatter key/value [T, Hkv, D] into kv_cache at slot_mapping [T] (int64)."""
+    torch = _torch()
+    nb, bs, hkv, d = _cache_dims(kv_cache)
+    T = int(key.shape[0])
+    for name, t in (("key", key), ("value", value)):
+        if tuple(t.shape) != (T, hkv, d) or t.dtype != kv_cache.dtype:
+            raise ValueError(f"{name} must be [{T}, {hkv}, {d}] {kv_cache.dtype}")
+    if tuple(slot_mapping.shape) != (T,):
+        raise ValueError("slot_mapping must be [num_tokens]")
+    st = lib.pa_reshape_and_cache(
+        _dev(key, "key"), _dev(value, "value"), _dev(kv_cache, "kv_cache"),
+        _dev(slot_mapping, "slot_mapping", torch.int64, 1), T, nb, bs, hkv, d,
+        _dtype_code(kv_cache), _stream())
+    _check("pa_reshape_and_cache", st)
+
+
+def pa_attention_workspace_size(num_seqs: int, num_tokens: int, num_q_heads: int,
+                                num_kv_heads: int, head_dim: int, max_seq_len: int,
+                                max_query_len: int, num_splits: int = 0) -> int:
+    return int(lib.pa_attention_workspace_size(num_seqs, num_tokens, num_q_heads, num_kv_heads,
+                                               head_dim, max_seq_len, max_query_len, num_splits))
+
+
+def _workspace(nbytes: int, device, workspace):
+    torch = _torch()
+    if workspace is None:
+        return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+    if workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError(f"workspace too small: need {nbytes} bytes")
+    return workspace
+
+
+def pa_attention_decode(q, kv_cache, block_table, seq_lens, scale: float, max_seq_len: int,
+                        out=None, workspace=None, num_splits: int = 0):
+    """One query token per request: q [R, Hq, D] -> out [R, Hq, D]; see pa.h."""
+    torch = _torch()
+    nb, bs, hkv, d = _cache_dims(kv_cache)
+    R, hq = int(q.shape[0]), int(q.shape[1])
+    if q.dim() != 3 or int(q.shape[2]) != d or q.dtype != kv_cache.dtype:
+        raise ValueError("q must be [num_seqs, num_q_heads, head_dim] in the cache dtype")
+    if out is None:
+        out = torch.empty_like(q)
+    need = pa_attention_workspace_size(R, R, hq, hkv, d, max_seq_len, 1, num_splits)
+    ws = _workspace(need, q.device, workspace)
+    st = lib.pa_attention_decode(
+        _dev(out, "out"), _dev(q, "q"), _dev(kv_cache, "kv_cache"), nb, bs, hkv, d,
+        _dtype_code(kv_cache), _dev(block_table, "block_table", torch.int32, 2),
+        int(block_table.shape[1]), _dev(seq_lens, "seq_lens", torch.int32, 1), R,
+        int(max_seq_len), hq, float(scale), _dev(ws, "workspace"),
+        ws.numel() * ws.element_size(), int(num_splits), _stream())
+    _check("pa_attention_decode", st)
+    return out
+
+
+def pa_attention_mixed(q, kv_cache, block_table, seq_lens, query_start_loc,
+                       num_computed_tokens, scale: float, max_query_len: int,
+                       max_seq_len: int, out=None, workspace=None, num_splits: int = 0):
+    """Chunked-prefill mixed batch: q [T, Hq, D] varlen-packed -> out; see pa.h."""
+    torch = _torch()
+    nb, bs, hkv, d = _cache_dims(kv_cache)
+    T, hq = int(q.shape[0]), int(q.shape[1])
+    R = int(seq_lens.shape[0])
+    if q.dim() != 3 or int(q.shape[2]) != d or q.dtype != kv_cache.dtype:
+        raise ValueError("q must be [num_tokens, num_q_heads, head_dim] in the cache dtype")
+    if out is None:
+        out = torch.empty_like(q)
+    need = pa_attention_workspace_size(R, T, hq, hkv, d, max_seq_len, max_query_len, num_splits)
+    ws = _workspace(need, q.device, workspace)
+    st = lib.pa_attention_mixed(
+        _dev(out, "out"), _dev(q, "q"), _dev(kv_cache, "kv_cache"), nb, bs, hkv, d,
+        _dtype_code(kv_cache), _dev(block_table, "block_table", torch.int32, 2),
+        int(block_table.shape[1]), _dev(seq_lens, "seq_lens", torch.int32, 1),
+        _dev(query_start_loc, "query_start_loc", torch.int32, 1),
+        _dev(num_computed_tokens, "num_computed_tokens", torch.int32, 1), R, T,
+        int(max_query_len), int(max_seq_len), hq, float(scale), _dev(ws, "workspace"),
+        ws.numel() * ws.element_size(), int(num_splits), _stream())
+    _check("pa_attention_mixed", st)
+    return out

@@ -1,0 +1,232 @@
+// C-ABI front end of libpa.so: argument checks, work planning and dispatch.
+// The public contract of every function is documented in include/pa.h.
+#include <math.h>
+#include <stdint.h>
+
+#include "pa.h"
+#include "pa_kernels.h"
+
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+
+// Partition plan for the balanced split: enough wavefronts to fill the chip
+// (256 CUs, ~8 resident waves each), but no range shorter than a few blocks.
+constexpr int kTargetWaves = 256 * 8;
+constexpr int kMinBlocksPerRange = 4;
+
+int heads_per_wave(int group) { return group < 4 ? group : 4; }
+
+bool group_ok(int group) { return group == 1 || group == 2 || group == 4 || group == 8; }
+
+bool dtype_ok(int dtype) { return dtype == PA_F32 || dtype == PA_BF16 || dtype == PA_F16; }
+
+int elem_bytes(int dtype) { return dtype == PA_F32 ? 4 : 2; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int plan_chunks(int num_seqs, int num_kv_heads, int group, int max_seq_len, int num_splits) {
+  if (num_splits > 0) return num_splits;
+  const int hg = group / heads_per_wave(group);
+  const int64_t blocks_upper = (int64_t)num_seqs * ceil_div(max_seq_len, pa::kBlockSize);
+  int64_t n = ceil_div(kTargetWaves, (int64_t)num_kv_heads * hg);
+  const int64_t cap = ceil_div(blocks_upper, kMinBlocksPerRange);
+  if (n > cap) n = cap;
+  if (n < 1) n = 1;
+  return (int)n;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// workspace: [ (R + N) * Hq * 2 ] floats of (max, sum), then [ (R + N) * Hq * D ]
+void workspace_layout(int num_seqs, int num_q_heads, int head_dim, int chunks, size_t* ml_bytes,
+                      size_t* total) {
+  const size_t slots = (size_t)num_seqs + (size_t)chunks;
+  *ml_bytes = align256(slots * num_q_heads * 2 * sizeof(float));
+  *total = *ml_bytes + align256(slots * num_q_heads * (size_t)head_dim * sizeof(float));
+}
+
+int check_cache(const void* kv_cache, int64_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                int32_t head_dim, int32_t dtype) {
+  if (!kv_cache || num_blocks <= 0 || num_kv_heads <= 0) return PA_ERR_INVALID_ARG;
+  if (block_size != pa::kBlockSize) return PA_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (!dtype_ok(dtype)) return PA_ERR_UNSUPPORTED;
+  if (!aligned16(kv_cache)) return PA_ERR_INVALID_ARG;
+  return PA_OK;
+}
+
+int check_heads(int32_t num_q_heads, int32_t num_kv_heads) {
+  if (num_q_heads <= 0 || num_q_heads % num_kv_heads != 0) return PA_ERR_INVALID_ARG;
+  if (!group_ok(num_q_heads / num_kv_heads)) return PA_ERR_UNSUPPORTED;
+  return PA_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_string(int status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_INVALID_ARG: return "invalid argument";
+    case PA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case PA_ERR_WORKSPACE: return "workspace missing or too small";
+    case PA_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+int pa_version(void) { return kVersion; }
+
+int pa_compute_slot_mapping(int64_t* slot_mapping, const int32_t* block_table,
+                            int32_t block_table_stride, const int32_t* query_start_loc,
+                            const int32_t* num_computed_tokens, int32_t num_seqs,
+                            int32_t num_tokens, int32_t block_size, void* stream) {
+  if (num_tokens < 0 || num_seqs < 0 || block_table_stride < 0) return PA_ERR_INVALID_ARG;
+  if (block_size != pa::kBlockSize) return PA_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PA_OK;
+  if (num_seqs == 0) return PA_ERR_INVALID_ARG;
+  if (!slot_mapping || !block_table || !query_start_loc || !num_computed_tokens)
+    return PA_ERR_INVALID_ARG;
+  return hip_status(pa::launch_slot_mapping(slot_mapping, block_table, block_table_stride,
+                                            query_start_loc, num_computed_tokens, num_seqs,
+                                            num_tokens, static_cast<hipStream_t>(stream)));
+}
+
+int pa_reshape_and_cache(const void* key, const void* value, void* kv_cache,
+                         const int64_t* slot_mapping, int32_t num_tokens, int64_t num_blocks,
+                         int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t dtype, void* stream) {
+  int st = check_cache(kv_cache, num_blocks, block_size, num_kv_heads, head_dim, dtype);
+  if (st != PA_OK) return st;
+  if (num_tokens < 0) return PA_ERR_INVALID_ARG;
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !slot_mapping) return PA_ERR_INVALID_ARG;
+  if (!aligned16(key) || !aligned16(value)) return PA_ERR_INVALID_ARG;
+  const int row_bytes = num_kv_heads * head_dim * elem_bytes(dtype);
+  return hip_status(pa::launch_reshape_and_cache(key, value, kv_cache, slot_mapping, num_tokens,
+                                                 row_bytes, static_cast<hipStream_t>(stream)));
+}
+
+size_t pa_attention_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t max_seq_len,
+                                   int32_t max_query_len, int32_t num_splits) {
+  (void)num_tokens;
+  (void)max_query_len;
+  if (num_seqs <= 0 || num_kv_heads <= 0 || max_seq_len <= 0 || num_splits < 0) return 0;
+  if (head_dim != 64 && head_dim != 128) return 0;
+  if (check_heads(num_q_heads, num_kv_heads) != PA_OK) return 0;
+  const int group = num_q_heads / num_kv_heads;
+  const int chunks = plan_chunks(num_seqs, num_kv_heads, group, max_seq_len, num_splits);
+  size_t ml = 0, total = 0;
+  workspace_layout(num_seqs, num_q_heads, head_dim, chunks, &ml, &total);
+  return total;
+}
+
+static int attention_common(void* out, const void* q, const void* kv_cache, int64_t num_blocks,
+                            int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t dtype, const int32_t* block_table, int32_t bt_stride,
+                            const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len,
+                            int32_t num_q_heads, float scale, void* workspace,
+                            size_t workspace_bytes, int32_t num_splits, pa::DecodeArgs* a) {
+  int st = check_cache(kv_cache, num_blocks, block_size, num_kv_heads, head_dim, dtype);
+  if (st != PA_OK) return st;
+  st = check_heads(num_q_heads, num_kv_heads);
+  if (st != PA_OK) return st;
+  if (num_seqs < 0 || max_seq_len < 0 || bt_stride < 0 || num_splits < 0) return PA_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return PA_ERR_INVALID_ARG;
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !q || !block_table || !seq_lens) return PA_ERR_INVALID_ARG;
+  if (!aligned16(out) || !aligned16(q)) return PA_ERR_INVALID_ARG;
+  if (max_seq_len == 0) return PA_OK;
+  if (bt_stride < ceil_div(max_seq_len, pa::kBlockSize)) return PA_ERR_INVALID_ARG;
+  const int group = num_q_heads / num_kv_heads;
+  const int chunks = plan_chunks(num_seqs, num_kv_heads, group, max_seq_len, num_splits);
+  size_t ml = 0, total = 0;
+  workspace_layout(num_seqs, num_q_heads, head_dim, chunks, &ml, &total);
+  if (!workspace || workspace_bytes < total) return PA_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return PA_ERR_WORKSPACE;
+
+  a->out = out;
+  a->q = q;
+  a->kv = kv_cache;
+  a->block_table = block_table;
+  a->bt_stride = bt_stride;
+  a->seq_lens = seq_lens;
+  a->qsl = nullptr;
+  a->num_seqs = num_seqs;
+  a->num_kv_heads = num_kv_heads;
+  a->num_q_heads = num_q_heads;
+  a->num_chunks = chunks;
+  a->head_groups = group / heads_per_wave(group);
+  a->scale_log2 = scale * 1.4426950408889634f;
+  a->ws_ml = static_cast<float*>(workspace);
+  a->ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + ml);
+  return 1;  // proceed
+}
+
+int pa_attention_decode(void* out, const void* q, const void* kv_cache, int64_t num_blocks,
+                        int32_t block_size, int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                        const int32_t* block_table, int32_t block_table_stride,
+                        const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len,
+                        int32_t num_q_heads, float scale, void* workspace, size_t workspace_bytes,
+                        int32_t num_splits, void* stream) {
+  pa::DecodeArgs a{};
+  const int st = attention_common(out, q, kv_cache, num_blocks, block_size, num_kv_heads, head_dim,
+                                  dtype, block_table, block_table_stride, seq_lens, num_seqs,
+                                  max_seq_len, num_q_heads, scale, workspace, workspace_bytes,
+                                  num_splits, &a);
+  if (st <= 0) return st;
+  return hip_status(pa::launch_decode(a, dtype, head_dim, num_q_heads / num_kv_heads,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+int pa_attention_mixed(void* out, const void* q, const void* kv_cache, int64_t num_blocks,
+                       int32_t block_size, int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                       const int32_t* block_table, int32_t block_table_stride,
+                       const int32_t* seq_lens, const int32_t* query_start_loc,
+                       const int32_t* num_computed_tokens, int32_t num_seqs, int32_t num_tokens,
+                       int32_t max_query_len, int32_t max_seq_len, int32_t num_q_heads,
+                       float scale, void* workspace, size_t workspace_bytes, int32_t num_splits,
+                       void* stream) {
+  if (num_tokens < 0 || max_query_len < 0) return PA_ERR_INVALID_ARG;
+  pa::DecodeArgs a{};
+  const int st = attention_common(out, q, kv_cache, num_blocks, block_size, num_kv_heads, head_dim,
+                                  dtype, block_table, block_table_stride, seq_lens, num_seqs,
+                                  max_seq_len, num_q_heads, scale, workspace, workspace_bytes,
+                                  num_splits, &a);
+  if (st <= 0) return st;
+  if (num_tokens == 0) return PA_OK;
+  if (!query_start_loc || !num_computed_tokens) return PA_ERR_INVALID_ARG;
+  const int group = num_q_heads / num_kv_heads;
+  if (max_query_len > 1 && !pa::prefill_supported(dtype, head_dim, group))
+    return PA_ERR_UNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (max_query_len > 1) {
+    pa::PrefillArgs p{};
+    p.out = out;
+    p.q = q;
+    p.kv = kv_cache;
+    p.block_table = block_table;
+    p.bt_stride = block_table_stride;
+    p.seq_lens = seq_lens;
+    p.qsl = query_start_loc;
+    p.num_computed = num_computed_tokens;
+    p.num_seqs = num_seqs;
+    p.num_kv_heads = num_kv_heads;
+    p.num_q_heads = num_q_heads;
+    p.max_tiles = (int)(ceil_div(num_tokens, pa::kQueriesPerTile) + num_seqs);
+    p.scale_log2 = a.scale_log2;
+    const hipError_t e = pa::launch_prefill(p, dtype, head_dim, group, s);
+    if (e != hipSuccess) return PA_ERR_HIP;
+  }
+  a.qsl = query_start_loc;
+  return hip_status(pa::launch_decode(a, dtype, head_dim, group, s));
+}
+
+}  // extern "C"

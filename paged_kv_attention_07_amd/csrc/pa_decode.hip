@@ -1,0 +1,534 @@
+// Decode attention over a paged KV cache on gfx950, with a balanced
+// split-KV partition-and-reduce.
+//
+// What it computes ("vLLM 架构源码解析（一）" §3.3.3 and §4.2;
+// "Inside vLLM" §3.3): for each request with one new query token, softmax
+// attention of that token over its seq_len cached keys, read through the
+// request's block table.  Partial results over key ranges are merged with
+// the online-softmax identity (max, sum, unnormalised output), the
+// "Online Softmax" the first page names in §6.4.
+//
+// Work decomposition.  The blocks of all decode requests are laid end to end
+// (request 0's blocks, then request 1's, ...) and the list is cut into
+// `num_chunks` equal ranges.  One wavefront takes one range for one KV head
+// (and up to four query heads of its group), so every wavefront streams the
+// same number of bytes whatever the length mix; a range that covers a whole
+// request finishes it in place, a request cut by range boundaries leaves one
+// partial per range, and a small merge kernel combines them.  Partials of
+// (request r, range c) go to workspace slot r + c, which is unique because
+// both indices only grow along the list.
+//
+// Inside a wavefront (64 lanes).  Lane = (token group tg = lane / 8, column
+// ds = lane % 8).  For each 16-token block the lane loads tokens tg and tg+8;
+// the 8 lanes of a group read 128 contiguous bytes of a token's head row per
+// instruction (16 bytes each), so every load instruction touches 8 full
+// 128-byte lines.  Scores are 8-lane DPP sums of per-lane dot products
+// (bf16/f16: v_dot2 pairs, no conversion); each token group keeps its own
+// running max / sum / accumulator (no cross-group traffic in the loop), with
+// the accumulator rescaled only when the max grows by more than 2^8.  P*V
+// pairs the group's two tokens in one v_dot2 per output element.  At the end
+// of a range the 8 groups are merged and reduce-scattered so each lane owns
+// a few contiguous output elements.
+#include <math.h>
+
+#include "pa_common.h"
+#include "pa_kernels.h"
+
+namespace pa {
+namespace {
+
+template <typename E, int D, int HPW>
+struct Shape {
+  static constexpr int ESZ = E::bytes;
+  static constexpr int EPV = 16 / ESZ;    // elements per 16-byte vector
+  static constexpr int ROWB = D * ESZ;    // bytes of one token's row for one kv head
+  static constexpr int NCH = ROWB / 128;  // 16-byte vectors per lane per token
+  static constexpr int DPL = NCH * EPV;   // head dims owned by a lane
+  static constexpr int NV = HPW * DPL;    // accumulator floats per lane
+  static constexpr int NOUT = NV / 8;     // outputs per lane after the group merge
+  static constexpr int RUN = NOUT < EPV ? NOUT : EPV;  // contiguous dims per store
+  static_assert(NCH >= 1 && NOUT >= 1, "unsupported decode shape");
+};
+
+// head dim of lane-local element e for column ds
+template <class S>
+__device__ __forceinline__ int dim_of(int e, int ds) {
+  return (e / S::EPV) * (8 * S::EPV) + ds * S::EPV + (e % S::EPV);
+}
+
+struct ReqInfo {
+  int nb;   // blocks this request contributes to the decode list (0 = not a decode row)
+  int row;  // query/output row
+  int len;  // keys
+};
+
+__device__ __forceinline__ ReqInfo req_info(const DecodeArgs& a, int r) {
+  ReqInfo ri{0, 0, 0};
+  if (r < a.num_seqs) {
+    const int L = a.seq_lens[r];
+    bool active = L > 0;
+    int row = r;
+    if (a.qsl) {
+      const int q0 = a.qsl[r], q1 = a.qsl[r + 1];
+      active = active && (q1 - q0 == 1);
+      row = q0;
+    }
+    ri.nb = active ? (L + kBlockSize - 1) / kBlockSize : 0;
+    ri.row = row;
+    ri.len = L;
+  }
+  return ri;
+}
+
+__device__ __forceinline__ int total_blocks(const DecodeArgs& a) {
+  int W = 0;
+  for (int base = 0; base < a.num_seqs; base += kWave) W += wave_sum(req_info(a, base + lane_id()).nb);
+  return W;
+}
+
+__device__ __forceinline__ int64_t chunk_begin(int c, int W, int N) {
+  return (int64_t)c * W / N;
+}
+
+// the range holding flat block x (ranges may be empty when W < N)
+__device__ __forceinline__ int chunk_of(int64_t x, int W, int N) {
+  return (int)(((x + 1) * N + W - 1) / W) - 1;
+}
+
+template <typename E>
+__device__ __forceinline__ float to_f(uint32_t w, int half);
+
+template <>
+__device__ __forceinline__ float to_f<BF16>(uint32_t w, int half) {
+  return half ? bf16_hi(w) : bf16_lo(w);
+}
+template <>
+__device__ __forceinline__ float to_f<F16>(uint32_t w, int half) {
+  return half ? f16_hi(w) : f16_lo(w);
+}
+
+// Store RUN consecutive values (times `mul`) as element type E.
+template <typename E, int RUN>
+__device__ __forceinline__ void store_run(void* dst, const float* v, float mul) {
+  if constexpr (E::kind == F32::kind) {
+    float* p = static_cast<float*>(dst);
+    if constexpr (RUN % 4 == 0) {
+#pragma unroll
+      for (int i = 0; i < RUN; i += 4) {
+        f32x4_t x = {v[i] * mul, v[i + 1] * mul, v[i + 2] * mul, v[i + 3] * mul};
+        *reinterpret_cast<f32x4_t*>(p + i) = x;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < RUN; ++i) p[i] = v[i] * mul;
+    }
+  } else {
+    if constexpr (RUN % 2 == 0) {
+      uint32_t w[RUN / 2];
+#pragma unroll
+      for (int i = 0; i < RUN / 2; ++i) {
+        w[i] = (E::kind == BF16::kind) ? pack_bf16(v[2 * i] * mul, v[2 * i + 1] * mul)
+                                       : pack_f16(v[2 * i] * mul, v[2 * i + 1] * mul);
+      }
+      uint32_t* p = static_cast<uint32_t*>(dst);
+      if constexpr (RUN == 8) {
+        u32x4_t x = {w[0], w[1], w[2], w[3]};
+        store16(p, x);
+      } else {
+#pragma unroll
+        for (int i = 0; i < RUN / 2; ++i) p[i] = w[i];
+      }
+    } else {
+      const uint32_t w = (E::kind == BF16::kind) ? pack_bf16(v[0] * mul, 0.f)
+                                                 : pack_f16(v[0] * mul, 0.f);
+      *static_cast<uint16_t*>(dst) = (uint16_t)(w & 0xffffu);
+    }
+  }
+}
+
+template <int RUN>
+__device__ __forceinline__ void store_f32_run(float* p, const float* v) {
+  if constexpr (RUN % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < RUN; i += 4) {
+      f32x4_t x = {v[i], v[i + 1], v[i + 2], v[i + 3]};
+      *reinterpret_cast<f32x4_t*>(p + i) = x;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < RUN; ++i) p[i] = v[i];
+  }
+}
+
+template <typename E, int D, int HPW>
+struct BlockRegs {
+  using S = Shape<E, D, HPW>;
+  u32x4_t k0[S::NCH], k1[S::NCH], v0[S::NCH], v1[S::NCH];
+};
+
+template <typename E, int D, int HPW>
+__device__ __forceinline__ void load_block(BlockRegs<E, D, HPW>& b, const uint8_t* p,
+                                           int64_t tok8, int64_t half) {
+  using S = Shape<E, D, HPW>;
+#pragma unroll
+  for (int c = 0; c < S::NCH; ++c) {
+    b.k0[c] = load16(p + c * 128);
+    b.k1[c] = load16(p + tok8 + c * 128);
+  }
+#pragma unroll
+  for (int c = 0; c < S::NCH; ++c) {
+    b.v0[c] = load16(p + half + c * 128);
+    b.v1[c] = load16(p + half + tok8 + c * 128);
+  }
+}
+
+// Attention of one query row over keys [16*j0, min(16*j1, L)) of request r.
+template <typename E, int D, int HPW>
+__device__ __forceinline__ void process_range(const DecodeArgs& a, int r, int row, int L, int j0,
+                                              int j1, int h, int hq0, bool whole, int slot) {
+  using S = Shape<E, D, HPW>;
+  const int lane = lane_id();
+  const int tg = lane >> 3;
+  const int ds = lane & 7;
+
+  // this lane's slice of the HPW query vectors
+  u32x4_t qv[HPW][S::NCH];
+  {
+    const uint8_t* qb = static_cast<const uint8_t*>(a.q) +
+                        ((int64_t)row * a.num_q_heads + hq0) * S::ROWB + ds * 16;
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh)
+#pragma unroll
+      for (int c = 0; c < S::NCH; ++c) qv[hh][c] = load16(qb + hh * S::ROWB + c * 128);
+  }
+
+  const int64_t tok_stride = (int64_t)a.num_kv_heads * S::ROWB;
+  const int64_t half_stride = kBlockSize * tok_stride;
+  const int64_t blk_stride = 2 * half_stride;
+  const int64_t tok8 = 8 * tok_stride;
+  const uint8_t* kvh = static_cast<const uint8_t*>(a.kv) + (int64_t)h * S::ROWB +
+                       tg * tok_stride + ds * 16;
+  const int32_t* bt = a.block_table + (int64_t)r * a.bt_stride;
+  const int nb = (L + kBlockSize - 1) / kBlockSize;
+
+  float m[HPW], l[HPW], acc[HPW][S::DPL];
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) {
+    m[hh] = -INFINITY;
+    l[hh] = 0.f;
+#pragma unroll
+    for (int e = 0; e < S::DPL; ++e) acc[hh][e] = 0.f;
+  }
+
+  BlockRegs<E, D, HPW> cur, nxt;
+  load_block<E, D, HPW>(cur, kvh + (int64_t)bt[j0] * blk_stride, tok8, half_stride);
+
+  for (int j = j0; j < j1; ++j) {
+    if (j + 1 < j1) load_block<E, D, HPW>(nxt, kvh + (int64_t)bt[j + 1] * blk_stride, tok8,
+                                          half_stride);
+    // ---- scores of tokens tg and tg+8 for each head (log2 units)
+    float s0[HPW], s1[HPW];
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) {
+      float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+      for (int c = 0; c < S::NCH; ++c)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          if constexpr (E::kind == F32::kind) {
+            const float qf = __uint_as_float(qv[hh][c][w]);
+            a0 = fmaf(__uint_as_float(cur.k0[c][w]), qf, a0);
+            a1 = fmaf(__uint_as_float(cur.k1[c][w]), qf, a1);
+          } else if constexpr (E::kind == BF16::kind) {
+            a0 = dot2_bf16(cur.k0[c][w], qv[hh][c][w], a0);
+            a1 = dot2_bf16(cur.k1[c][w], qv[hh][c][w], a1);
+          } else {
+            a0 = dot2_f16(cur.k0[c][w], qv[hh][c][w], a0);
+            a1 = dot2_f16(cur.k1[c][w], qv[hh][c][w], a1);
+          }
+        }
+      s0[hh] = sum8(a0) * a.scale_log2;
+      s1[hh] = sum8(a1) * a.scale_log2;
+    }
+    // ---- partial last block: drop scores and values past the sequence end
+    if (j == nb - 1 && (L & (kBlockSize - 1))) {
+      const int nvalid = L - j * kBlockSize;
+      const bool ok0 = tg < nvalid, ok1 = tg + 8 < nvalid;
+#pragma unroll
+      for (int hh = 0; hh < HPW; ++hh) {
+        s0[hh] = ok0 ? s0[hh] : -INFINITY;
+        s1[hh] = ok1 ? s1[hh] : -INFINITY;
+      }
+#pragma unroll
+      for (int c = 0; c < S::NCH; ++c)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          cur.v0[c][w] = ok0 ? cur.v0[c][w] : 0u;
+          cur.v1[c][w] = ok1 ? cur.v1[c][w] : 0u;
+        }
+    }
+    // ---- running max; rescale only when it grows by more than 8 (log2 units)
+    bool grow = false;
+    float mn[HPW];
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) {
+      mn[hh] = fmaxf(m[hh], fmaxf(s0[hh], s1[hh]));
+      grow |= mn[hh] > m[hh] + 8.f;
+    }
+    if (__any(grow)) {
+#pragma unroll
+      for (int hh = 0; hh < HPW; ++hh) {
+        const float mu = (mn[hh] > m[hh] + 8.f) ? mn[hh] : m[hh];
+        const float alpha = (mu == m[hh]) ? 1.f : __builtin_amdgcn_exp2f(m[hh] - mu);
+        l[hh] *= alpha;
+#pragma unroll
+        for (int e = 0; e < S::DPL; ++e) acc[hh][e] *= alpha;
+        m[hh] = mu;
+      }
+    }
+    float p0[HPW], p1[HPW];
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) {
+      const float ms = (m[hh] == -INFINITY) ? 0.f : m[hh];
+      p0[hh] = __builtin_amdgcn_exp2f(s0[hh] - ms);
+      p1[hh] = __builtin_amdgcn_exp2f(s1[hh] - ms);
+      l[hh] += p0[hh] + p1[hh];
+    }
+    // ---- P * V
+    if constexpr (E::kind == F32::kind) {
+#pragma unroll
+      for (int c = 0; c < S::NCH; ++c)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float x0 = __uint_as_float(cur.v0[c][w]);
+          const float x1 = __uint_as_float(cur.v1[c][w]);
+#pragma unroll
+          for (int hh = 0; hh < HPW; ++hh)
+            acc[hh][c * 4 + w] = fmaf(p1[hh], x1, fmaf(p0[hh], x0, acc[hh][c * 4 + w]));
+        }
+    } else {
+      uint32_t pp[HPW];
+#pragma unroll
+      for (int hh = 0; hh < HPW; ++hh)
+        pp[hh] = (E::kind == BF16::kind) ? pack_bf16(p0[hh], p1[hh]) : pack_f16(p0[hh], p1[hh]);
+#pragma unroll
+      for (int c = 0; c < S::NCH; ++c)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t lo = pair_lo(cur.v0[c][w], cur.v1[c][w]);
+          const uint32_t hi = pair_hi(cur.v0[c][w], cur.v1[c][w]);
+          const int e = c * S::EPV + 2 * w;
+#pragma unroll
+          for (int hh = 0; hh < HPW; ++hh) {
+            if constexpr (E::kind == BF16::kind) {
+              acc[hh][e] = dot2_bf16(lo, pp[hh], acc[hh][e]);
+              acc[hh][e + 1] = dot2_bf16(hi, pp[hh], acc[hh][e + 1]);
+            } else {
+              acc[hh][e] = dot2_f16(lo, pp[hh], acc[hh][e]);
+              acc[hh][e + 1] = dot2_f16(hi, pp[hh], acc[hh][e + 1]);
+            }
+          }
+        }
+    }
+    cur = nxt;
+  }
+
+  // ---- merge the 8 token groups: common max, rescaled sums and accumulators
+  float Mh[HPW], Lh[HPW];
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) {
+    float M = m[hh];
+    M = fmaxf(M, shfl_xor(M, 8));
+    M = fmaxf(M, shfl_xor(M, 16));
+    M = fmaxf(M, shfl_xor(M, 32));
+    const float sc = (m[hh] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m[hh] - M);
+    float lt = l[hh] * sc;
+    lt += shfl_xor(lt, 8);
+    lt += shfl_xor(lt, 16);
+    lt += shfl_xor(lt, 32);
+#pragma unroll
+    for (int e = 0; e < S::DPL; ++e) acc[hh][e] *= sc;
+    Mh[hh] = M;
+    Lh[hh] = lt;
+  }
+  // reduce-scatter over the groups: lane keeps NOUT consecutive values of
+  // the flattened [HPW][DPL] accumulator, starting at `base`
+  float* v = &acc[0][0];
+  int base = 0;
+#pragma unroll
+  for (int st = 0; st < 3; ++st) {
+    const int n = S::NV >> st;
+    const int bit = (tg >> st) & 1;
+#pragma unroll
+    for (int i = 0; i < n / 2; ++i) {
+      const float lo = v[i], hi = v[i + n / 2];
+      const float send = bit ? lo : hi;
+      const float keep = bit ? hi : lo;
+      v[i] = keep + shfl_xor(send, 8 << st);
+    }
+    base += bit * (n / 2);
+  }
+  const int hsel = base / S::DPL;
+  const int e0 = base % S::DPL;
+  float lsel = Lh[0], msel = Mh[0];
+#pragma unroll
+  for (int hh = 1; hh < HPW; ++hh) {
+    lsel = (hsel == hh) ? Lh[hh] : lsel;
+    msel = (hsel == hh) ? Mh[hh] : msel;
+  }
+  const int hq = hq0 + hsel;
+  if (whole) {
+    uint8_t* ob = static_cast<uint8_t*>(a.out) + ((int64_t)row * a.num_q_heads + hq) * S::ROWB;
+    const float inv = 1.f / lsel;
+#pragma unroll
+    for (int r0 = 0; r0 < S::NOUT; r0 += S::RUN)
+      store_run<E, S::RUN>(ob + (int64_t)dim_of<S>(e0 + r0, ds) * S::ESZ, v + r0, inv);
+  } else {
+    const int64_t ps = (int64_t)slot * a.num_q_heads + hq;
+    float* ob = a.ws_o + ps * D;
+#pragma unroll
+    for (int r0 = 0; r0 < S::NOUT; r0 += S::RUN)
+      store_f32_run<S::RUN>(ob + dim_of<S>(e0 + r0, ds), v + r0);
+    // one lane per head writes (max, sum): the lane whose run starts the head
+    if (e0 == 0 && ds == 0) {
+      f32x2_t ml = {msel, lsel};
+      *reinterpret_cast<f32x2_t*>(a.ws_ml + ps * 2) = ml;
+    }
+  }
+}
+
+template <typename E, int D, int HPW>
+__global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
+  const int lane = lane_id();
+  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int per_chunk = a.num_kv_heads * a.head_groups;
+  if (item >= a.num_chunks * per_chunk) return;
+  const int c = item / per_chunk;
+  const int rem = item - c * per_chunk;
+  const int h = rem / a.head_groups;
+  const int hs = rem - h * a.head_groups;
+  const int group = a.num_q_heads / a.num_kv_heads;
+  const int hq0 = h * group + hs * HPW;
+
+  const int W = total_blocks(a);
+  if (W == 0) return;
+  const int64_t b0 = chunk_begin(c, W, a.num_chunks);
+  const int64_t b1 = chunk_begin(c + 1, W, a.num_chunks);
+  if (b0 >= b1) return;
+
+  int running = 0;
+  for (int base = 0; base < a.num_seqs && running < b1; base += kWave) {
+    const ReqInfo ri = req_info(a, base + lane);
+    const int incl = wave_incl_scan(ri.nb) + running;
+    const int excl = incl - ri.nb;
+    uint64_t mask = __ballot(ri.nb > 0 && excl < b1 && incl > b0);
+    while (mask) {
+      const int src = __builtin_ctzll(mask);
+      mask &= mask - 1;
+      const int s = readlane(excl, src), e = readlane(incl, src);
+      const int L = readlane(ri.len, src), row = readlane(ri.row, src);
+      const int j0 = (int)((b0 > s ? b0 : s) - s);
+      const int j1 = (int)((b1 < e ? b1 : e) - s);
+      const bool whole = (j0 == 0) && (j1 == e - s);
+      process_range<E, D, HPW>(a, base + src, row, L, j0, j1, h, hq0, whole, base + src + c);
+    }
+    running = readlane(incl, kWave - 1);
+  }
+}
+
+// Merge the partials of requests cut by range boundaries.  One wavefront per
+// (request, query head); lane owns D/64 consecutive dims.
+template <typename E, int D>
+__global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
+  const int lane = lane_id();
+  const int r = blockIdx.x / a.num_q_heads;
+  const int hq = blockIdx.x - r * a.num_q_heads;
+  int W = 0, s = 0, e = 0, row = 0;
+  for (int base = 0; base < a.num_seqs; base += kWave) {
+    const ReqInfo ri = req_info(a, base + lane);
+    const int incl = wave_incl_scan(ri.nb) + W;
+    if (r >= base && r < base + kWave) {
+      const int src = r - base;
+      e = readlane(incl, src);
+      s = e - readlane(ri.nb, src);
+      row = readlane(ri.row, src);
+    }
+    W = readlane(incl, kWave - 1);
+  }
+  if (e == s) return;
+  const int N = a.num_chunks;
+  const int cf = chunk_of(s, W, N), cl = chunk_of(e - 1, W, N);
+  if (cf == cl) return;  // finished in place by its range
+
+  constexpr int DPT = D / kWave;
+  float M = -INFINITY;
+  for (int c = cf; c <= cl; ++c) {
+    if (chunk_begin(c, W, N) == chunk_begin(c + 1, W, N)) continue;
+    M = fmaxf(M, a.ws_ml[((int64_t)(r + c) * a.num_q_heads + hq) * 2]);
+  }
+  float lsum = 0.f, acc[DPT];
+#pragma unroll
+  for (int i = 0; i < DPT; ++i) acc[i] = 0.f;
+  for (int c = cf; c <= cl; ++c) {
+    if (chunk_begin(c, W, N) == chunk_begin(c + 1, W, N)) continue;
+    const int64_t ps = (int64_t)(r + c) * a.num_q_heads + hq;
+    const float w = __builtin_amdgcn_exp2f(a.ws_ml[ps * 2] - M);
+    lsum += w * a.ws_ml[ps * 2 + 1];
+    const float* po = a.ws_o + ps * D + lane * DPT;
+#pragma unroll
+    for (int i = 0; i < DPT; ++i) acc[i] = fmaf(w, po[i], acc[i]);
+  }
+  uint8_t* ob = static_cast<uint8_t*>(a.out) +
+                (((int64_t)row * a.num_q_heads + hq) * D + lane * DPT) * E::bytes;
+  store_run<E, DPT>(ob, acc, 1.f / lsum);
+}
+
+template <typename E, int D, int HPW>
+hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
+  const int64_t items = (int64_t)a.num_chunks * a.num_kv_heads * a.head_groups;
+  const unsigned wgs = (unsigned)((items + 3) / 4);
+  hipLaunchKernelGGL((decode_split_kernel<E, D, HPW>), dim3(wgs), dim3(256), 0, stream, a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const unsigned merges = (unsigned)a.num_seqs * (unsigned)a.num_q_heads;
+  if (a.num_chunks > 1 && merges > 0) {
+    hipLaunchKernelGGL((decode_merge_kernel<E, D>), dim3(merges), dim3(64), 0, stream, a);
+    err = hipGetLastError();
+  }
+  return err;
+}
+
+template <typename E, int D>
+hipError_t launch_hpw(const DecodeArgs& a, int group, hipStream_t stream) {
+  switch (group) {
+    case 1: return launch_typed<E, D, 1>(a, stream);
+    case 2: return launch_typed<E, D, 2>(a, stream);
+    case 4:
+    case 8: return launch_typed<E, D, 4>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <typename E>
+hipError_t launch_dim(const DecodeArgs& a, int head_dim, int group, hipStream_t stream) {
+  switch (head_dim) {
+    case 64: return launch_hpw<E, 64>(a, group, stream);
+    case 128: return launch_hpw<E, 128>(a, group, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs& a, int dtype, int head_dim, int group,
+                         hipStream_t stream) {
+  if (a.num_chunks <= 0 || a.num_seqs <= 0) return hipSuccess;
+  switch (dtype) {
+    case F32::kind: return launch_dim<F32>(a, head_dim, group, stream);
+    case BF16::kind: return launch_dim<BF16>(a, head_dim, group, stream);
+    case F16::kind: return launch_dim<F16>(a, head_dim, group, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace pa

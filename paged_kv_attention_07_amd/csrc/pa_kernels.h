@@ -1,0 +1,68 @@
+// Internal launch interface between the C-ABI front end (pa_api.cpp) and the
+// HIP kernels.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+constexpr int kBlockSize = 16;  // tokens per paged block
+
+// Arguments shared by the decode (split-KV) kernel and its merge kernel.
+struct DecodeArgs {
+  void* out;                  // [rows, Hq, D]
+  const void* q;              // [rows, Hq, D]
+  const void* kv;             // [NB, 2, 16, Hkv, D]
+  const int32_t* block_table; // [R, bt_stride]
+  int32_t bt_stride;
+  const int32_t* seq_lens;    // [R]
+  const int32_t* qsl;         // [R+1] or null: row r = request r, all decode
+  int32_t num_seqs;
+  int32_t num_kv_heads;
+  int32_t num_q_heads;
+  int32_t num_chunks;         // partitions of the flattened block list per kv head
+  int32_t head_groups;        // waves per kv head (query heads split in groups)
+  float scale_log2;           // softmax scale * log2(e)
+  float* ws_ml;               // [(R + num_chunks), Hq, 2]  (max, sum) per partial
+  float* ws_o;                // [(R + num_chunks), Hq, D]  unnormalised partial outputs
+};
+
+// Arguments of the MFMA prefill-tile kernel.
+struct PrefillArgs {
+  void* out;                  // [T, Hq, D]
+  const void* q;              // [T, Hq, D]
+  const void* kv;
+  const int32_t* block_table;
+  int32_t bt_stride;
+  const int32_t* seq_lens;
+  const int32_t* qsl;
+  const int32_t* num_computed;
+  int32_t num_seqs;
+  int32_t num_kv_heads;
+  int32_t num_q_heads;
+  int32_t max_tiles;          // upper bound on the tile count (grid size)
+  float scale_log2;
+};
+
+constexpr int kQueriesPerTile = 16;  // query tokens per prefill tile
+
+hipError_t launch_slot_mapping(int64_t* slot_mapping, const int32_t* block_table,
+                               int32_t bt_stride, const int32_t* qsl,
+                               const int32_t* num_computed, int32_t num_seqs,
+                               int32_t num_tokens, hipStream_t stream);
+
+hipError_t launch_reshape_and_cache(const void* key, const void* value, void* kv_cache,
+                                    const int64_t* slot_mapping, int32_t num_tokens,
+                                    int32_t row_bytes, hipStream_t stream);
+
+// dtype: pa_dtype value; head_dim 64 | 128; group = Hq / Hkv in {1,2,4,8}.
+hipError_t launch_decode(const DecodeArgs& a, int dtype, int head_dim, int group,
+                         hipStream_t stream);
+
+hipError_t launch_prefill(const PrefillArgs& a, int dtype, int head_dim, int group,
+                          hipStream_t stream);
+
+bool prefill_supported(int dtype, int head_dim, int group);
+
+}  // namespace pa

@@ -1,0 +1,251 @@
+"""HIP path vs the fp64 oracle on the same seeded inputs, through the C ABI.
+
+Bars: slot mapping and reshape_and_cache bit-exact (whole pool, NaN payloads
+included); attention within 1e-5 max-abs for fp32 and within 2e-2 max-abs and
+2e-3 mean-abs for bf16/f16.  Slots attention must not read are NaN-poisoned,
+and so are the slots this step's tokens are written to, so a read of a stale
+or foreign slot shows up as a non-finite output.
+"""
+
+import functools
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from workloads import make_workload
+from workloads.gen import build_workload
+
+import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # collected on CPU hosts, never run there
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import paged_kv_attention_07_amd as pa  # noqa: E402  (fails loudly if libpa.so is missing)
+
+SMALL = ["tiny_f32_decode", "tiny_f32_decode_alt", "decode_bf16_small", "mixed_bf16_small",
+         "prefix_shared_small", "long_decode_small"]
+
+
+@functools.lru_cache(maxsize=4)
+def workload(name, seed=None):
+    print(f"[workload] {name} seed={seed}", flush=True)
+    return make_workload(name, seed)
+
+
+def full_check(w, requests=None, **kw):
+    print(f"[case] {w.name} seed={w.seed} R={w.num_seqs} T={w.num_tokens} {kw}", flush=True)
+    pool, g_slots, g_pool, g_out = gu.run_step(w, **kw)
+    r_slots, r_pool, r_out = gu.oracle_step(w, pool, requests=requests)
+    assert np.array_equal(g_slots, r_slots), "slot mapping differs"
+    assert np.array_equal(gu.bits(g_pool), gu.bits(r_pool)), "pool differs after the scatter"
+    rows = None if requests is None else gu.rows_of(w, requests)
+    return gu.check_close(w, g_out, r_out, rows=rows, what=w.name)
+
+
+# --------------------------------------------------------------------------
+# slot mapping + scatter
+# --------------------------------------------------------------------------
+
+
+def test_slot_mapping_worked_example():
+    """The printed example of the slot formula ("vllm v1 源码精读（三）" §3.4)."""
+    bt = gu.ints_to_device(np.array([[5, 12, -1], [3, -1, -1], [7, 21, 9]], np.int32), np.int32)
+    sel = gu.ints_to_device(np.array([[5, 12, -1], [7, 21, 9]], np.int32), np.int32)
+    qsl = gu.ints_to_device(np.array([0, 1, 2], np.int32), np.int32)
+    nc = gu.ints_to_device(np.array([17, 32], np.int32), np.int32)
+    got = pa.pa_compute_slot_mapping(sel, qsl, nc, 2, 16).cpu().numpy()
+    assert list(got) == [193, 144]
+    # a position whose table entry is -1 gets a negative slot
+    nc2 = gu.ints_to_device(np.array([0, 16, 40], np.int32), np.int32)
+    qsl3 = gu.ints_to_device(np.array([0, 1, 2, 3], np.int32), np.int32)
+    got = pa.pa_compute_slot_mapping(bt, qsl3, nc2, 3, 16).cpu().numpy()
+    assert got[0] == 5 * 16 and got[1] < 0 and got[2] == 9 * 16 + 8
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_small_configs(name):
+    full_check(workload(name))
+
+
+def test_reshape_and_cache_padding_and_dtypes():
+    """slot < 0 writes nothing; every other byte of the pool is untouched."""
+    for dtype, H, D in (("bf16", 8, 128), ("f32", 2, 64), ("f16", 4, 64)):
+        w = build_workload(f"rac_{dtype}", dtype=dtype, num_q_heads=H, num_kv_heads=H, head_dim=D,
+                           num_blocks=40, requests=[(3, 5), (20, 1), (0, 17)], seed=5,
+                           fill_unused="zero")
+        dev = gu.Device(w)
+        slots = oracle.slot_mapping(w.block_table, w.query_start_loc, w.num_computed, 16)
+        slots[[1, 7, 20]] = -1
+        dev.scatter(gu.ints_to_device(slots, np.int64))
+        want = oracle.reshape_and_cache(w.pool, w.k_new, w.v_new, slots)
+        got = gu.from_device(dev.kv, dtype)
+        assert np.array_equal(gu.bits(got), gu.bits(want)), dtype
+
+
+# --------------------------------------------------------------------------
+# decode: splits, determinism, invariances, head groupings, dtypes
+# --------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 17, 64, 333, 2000])
+def test_decode_any_split_count(splits):
+    full_check(workload("decode_bf16_small"), num_splits=splits)
+
+
+def test_decode_deterministic_and_mixed_entry_agrees():
+    w = workload("long_decode_small")
+    dev = gu.Device(w, gu.poisoned_pool(w))
+    dev.scatter(dev.slot_mapping())
+    a = gu.from_device(dev.attend(), w.dtype)
+    b = gu.from_device(dev.attend(), w.dtype)
+    c = gu.from_device(dev.attend(force_mixed=True), w.dtype)
+    assert np.array_equal(a, b), "two identical launches differ"
+    assert np.array_equal(a, c), "decode rows through the mixed entry differ"
+
+
+def test_decode_block_permutation_bit_identical():
+    """Relabelling physical blocks leaves the GPU result bit-identical."""
+    w = workload("decode_bf16_small")
+    pool = gu.poisoned_pool(w)
+    _, _, _, out1 = gu.run_step(w, poison=True)
+    rng = np.random.default_rng(99)
+    perm = rng.permutation(w.num_blocks).astype(np.int32)
+    pool2 = np.empty_like(pool)
+    pool2[perm] = pool
+    bt2 = np.where(w.block_table >= 0, perm[np.maximum(w.block_table, 0)], -1).astype(np.int32)
+    import dataclasses
+    w2 = dataclasses.replace(w, pool=pool2, block_table=bt2)
+    dev = gu.Device(w2, pool2)
+    dev.scatter(dev.slot_mapping())
+    out2 = gu.from_device(dev.attend(), w.dtype)
+    assert np.array_equal(out1, out2)
+
+
+def test_prefix_sharing_bit_identical_to_private_copies():
+    w = workload("prefix_shared_small")
+    pool = gu.poisoned_pool(w)
+    dev = gu.Device(w, pool)
+    dev.scatter(dev.slot_mapping())
+    shared = gu.from_device(dev.attend(), w.dtype)
+    # copy the shared blocks into free blocks, one private copy per request
+    S = 4
+    free = np.setdiff1d(np.arange(w.num_blocks), w.used_blocks)
+    assert free.size >= S * w.num_seqs
+    pool2, bt2, k = pool.copy(), w.block_table.copy(), 0
+    for r in range(w.num_seqs):
+        for j in range(S):
+            pool2[free[k]] = pool[w.block_table[r, j]]
+            bt2[r, j] = free[k]
+            k += 1
+    import dataclasses
+    w2 = dataclasses.replace(w, block_table=bt2)
+    dev2 = gu.Device(w2, pool2)
+    dev2.scatter(dev2.slot_mapping())
+    private = gu.from_device(dev2.attend(), w.dtype)
+    assert np.array_equal(shared, private)
+
+
+def _variant(dtype, Hq, Hkv, D, lens, seed, q_lens=None):
+    reqs = [(L - (1 if q_lens is None else q_lens[i]), 1 if q_lens is None else q_lens[i])
+            for i, L in enumerate(lens)]
+    return build_workload(f"var_{dtype}_{Hq}x{Hkv}x{D}", dtype=dtype, num_q_heads=Hq,
+                          num_kv_heads=Hkv, head_dim=D, num_blocks=300, requests=reqs, seed=seed)
+
+
+@pytest.mark.parametrize("dtype,Hq,Hkv,D", [
+    ("bf16", 8, 8, 128), ("bf16", 8, 4, 128), ("bf16", 16, 2, 128), ("bf16", 8, 2, 64),
+    ("bf16", 4, 4, 64), ("f16", 16, 4, 128), ("f16", 8, 1, 64), ("f32", 8, 2, 128),
+    ("f32", 4, 4, 64), ("f32", 16, 2, 64)])
+def test_decode_head_groupings_and_dtypes(dtype, Hq, Hkv, D):
+    lens = [1, 15, 16, 17, 33, 250, 600, 1000]
+    full_check(_variant(dtype, Hq, Hkv, D, lens, seed=11 + Hq + D))
+    full_check(_variant(dtype, Hq, Hkv, D, lens, seed=12 + Hq + D), num_splits=5)
+
+
+def test_decode_single_key_returns_v0():
+    w = _variant("bf16", 8, 2, 128, [1, 1, 1], seed=3)
+    pool, _, g_pool, out = gu.run_step(w)
+    for r in range(3):
+        blk = w.block_table[r, 0]
+        v0 = g_pool[blk, 1, 0]                 # [Hkv, D] bits written by the scatter
+        for h in range(8):
+            assert np.array_equal(out[r, h], v0[h // 4])
+
+
+# --------------------------------------------------------------------------
+# mixed (chunked-prefill) batches
+# --------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("dtype,Hq,Hkv,D", [
+    ("bf16", 32, 8, 128), ("bf16", 8, 8, 128), ("bf16", 8, 4, 64), ("f16", 16, 2, 128),
+    ("bf16", 16, 2, 64)])
+def test_mixed_groupings(dtype, Hq, Hkv, D):
+    lens = [40, 17, 300, 5, 64, 129, 1, 700]
+    q_lens = [40, 2, 33, 1, 16, 100, 1, 64]
+    full_check(_variant(dtype, Hq, Hkv, D, lens, seed=21 + Hq, q_lens=q_lens))
+
+
+def test_mixed_chunked_equivalence():
+    """A 1000-token prompt prefilled in chunks 254/254/254/238 ("vllm v1 源码精读（三）"
+    §4.2) gives, chunk by chunk, the rows of one full prefill (both vs the oracle)."""
+    L = 1000
+    full = _variant("bf16", 32, 8, 128, [L], seed=31, q_lens=[L])
+    pool = gu.poisoned_pool(full)
+    _, _, _, out_full = gu.run_step(full, poison=False)
+    _, r_pool, r_full = gu.oracle_step(full, full.pool)
+    gu.check_close(full, out_full, r_full, what="full prefill")
+    done = 0
+    import dataclasses
+    for n in oracle.chunk_schedule(L, 254):
+        w = dataclasses.replace(
+            full, q=full.q[done:done + n], k_new=full.k_new[done:done + n],
+            v_new=full.v_new[done:done + n], seq_lens=np.array([done + n], np.int32),
+            num_computed=np.array([done], np.int32),
+            query_start_loc=np.array([0, n], np.int32))
+        dev = gu.Device(w, r_pool)  # cache already holds every token's K/V
+        out = gu.from_device(dev.attend(force_mixed=True), w.dtype)
+        gu.check_close(w, out, r_full[done:done + n], what=f"chunk at {done}")
+        done += n
+
+
+def test_mixed_request_order_shuffled():
+    w = workload("mixed_bf16_small")
+    rng = np.random.default_rng(5)
+    order = rng.permutation(w.num_seqs)
+    ql = w.q_lens[order]
+    qsl = np.concatenate([[0], np.cumsum(ql)]).astype(np.int32)
+    rows = gu.rows_of(w, order)
+    import dataclasses
+    w2 = dataclasses.replace(w, q=w.q[rows], k_new=w.k_new[rows], v_new=w.v_new[rows],
+                             seq_lens=w.seq_lens[order], num_computed=w.num_computed[order],
+                             block_table=w.block_table[order], query_start_loc=qsl)
+    full_check(w2)
+
+
+# --------------------------------------------------------------------------
+# full-size configurations (sampled outputs where the oracle is slow)
+# --------------------------------------------------------------------------
+
+
+def test_full_decode_64req():
+    full_check(workload("decode_bf16_64req"))
+
+
+def test_full_mixed_step():
+    full_check(workload("mixed_chunked_prefill_bf16"))
+
+
+def test_full_prefix_shared():
+    w = workload("prefix_shared_decode_bf16")
+    full_check(w, requests=list(range(0, w.num_seqs, 8)))
+
+
+def test_full_long_context_sampled():
+    w = workload("long_context_decode_bf16")
+    full_check(w, requests=[0, 7, 15])

@@ -23,8 +23,10 @@ shows up in the result.  Nothing here computes slots, scatters or attends.
 
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
 import math
+import os
 from typing import Dict, List, Optional, Sequence, Tuple
 
 import numpy as np
@@ -80,6 +82,30 @@ def _to_storage(x: np.ndarray, dtype: str) -> np.ndarray:
 
 def _normal(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
     return _to_storage(rng.standard_normal(size=shape, dtype=np.float32), dtype)
+
+
+_FILL_CHUNK = 1024  # blocks per independently seeded chunk of pool values
+
+
+def _fill_blocks(pool: np.ndarray, ids: np.ndarray, seed: int, dtype: str) -> None:
+    """pool[ids] = N(0,1) values.  Chunk i of ``_FILL_CHUNK`` ids draws from its
+    own stream seeded by (seed, i), so the result does not depend on how many
+    threads fill the chunks."""
+    blk_shape = pool.shape[1:]
+    starts = list(range(0, ids.size, _FILL_CHUNK))
+
+    def work(i):
+        sub = ids[starts[i]:starts[i] + _FILL_CHUNK]
+        rng = np.random.default_rng(np.random.SeedSequence([seed, 0x5EED, i]))
+        pool[sub] = _normal(rng, (sub.size,) + blk_shape, dtype)
+
+    threads = min(16, os.cpu_count() or 1, max(1, len(starts)))
+    if threads <= 1:
+        for i in range(len(starts)):
+            work(i)
+    else:
+        with concurrent.futures.ThreadPoolExecutor(threads) as ex:
+            list(ex.map(work, range(len(starts))))
 
 
 # --------------------------------------------------------------------------
@@ -224,10 +250,7 @@ def build_workload(
         pool[unused_mask] = np.float32(np.nan) if dtype == "f32" else _NAN_BITS[dtype]
     else:
         pool[unused_mask] = 0
-    chunk = 2048
-    for i in range(0, used.size, chunk):
-        ids = used[i:i + chunk]
-        pool[ids] = _normal(rng, (ids.size,) + blk_shape, dtype)
+    _fill_blocks(pool, used, seed, dtype)
 
     T = int(qsl[-1])
     q = _normal(rng, (T, num_q_heads, head_dim), dtype)
