@@ -38,6 +38,7 @@ WORKLOADS = {
     "mixed": "mixed_chunked_prefill_bf16",
     "prefix": "prefix_shared_decode_bf16",
     "long": "long_context_decode_bf16",
+    "chunk": "prefill_chunk_bf16",
 }
 
 DESCR = {
@@ -48,6 +49,7 @@ DESCR = {
     "prefix_shared_decode_bf16": "Llama-3-8B layer decode, 256 requests sharing a 1024-token prefix "
                                  "(64 blocks) + private suffix U[64,512]",
     "long_context_decode_bf16": "Llama-3-8B layer decode, 16 requests at 32768 tokens, pool 36000 blocks",
+    "prefill_chunk_bf16": "Llama-3-8B layer prefill chunk alone: 512 new tokens on 1024 cached",
 }
 
 
@@ -278,7 +280,8 @@ def main():
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     rot = 4
-    names = [args.only] if args.only else ["decode", "mixed"] + (["prefix", "long"] if args.extra else [])
+    names = [args.only] if args.only else ["decode", "mixed", "chunk"] + (
+        ["prefix", "long"] if args.extra else [])
     results = {k: measure(WORKLOADS[k], args, rot if k != "long" else 2) for k in names}
 
     head = results.get("decode") or next(iter(results.values()))
@@ -327,6 +330,16 @@ def main():
             "pct_peak_hbm": round(100 * mbytes / (m["ms_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
             "attention_avg_us": round(m["attn_ms_avg"] * 1e3, 2),
             "chunk_gflop": round(mc["chunk_flops"] / 1e9, 3),
+        }
+    if "chunk" in results:
+        ch = results["chunk"]
+        cw, cc = ch["w"], ch["counts"]
+        tflops = cc["chunk_flops"] / (ch["attn_ms_avg"] * 1e-3) / 1e12
+        line["prefill_chunk"] = {
+            "workload": cw.name, "attention_avg_us": round(ch["attn_ms_avg"] * 1e3, 2),
+            "gflop": round(cc["chunk_flops"] / 1e9, 3), "tflops": round(tflops, 1),
+            "mfma_util": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "tokens_per_s": round(cw.num_tokens / (ch["ms_step"] * 1e-3), 1),
         }
     for key in ("prefix", "long"):
         if key in results:

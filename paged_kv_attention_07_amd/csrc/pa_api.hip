@@ -40,12 +40,20 @@ int plan_chunks(int num_seqs, int num_kv_heads, int group, int max_seq_len, int 
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// workspace: [ (R + N) * Hq * 2 ] floats of (max, sum), then [ (R + N) * Hq * D ]
-void workspace_layout(int num_seqs, int num_q_heads, int head_dim, int chunks, size_t* ml_bytes,
-                      size_t* total) {
+// workspace: [R] x int4 request metadata, then [(R + N) * Hq * 2] floats of
+// (max, sum), then [(R + N) * Hq * D] floats of partial outputs
+struct WsLayout {
+  size_t meta, ml, o, total;
+};
+
+WsLayout workspace_layout(int num_seqs, int num_q_heads, int head_dim, int chunks) {
   const size_t slots = (size_t)num_seqs + (size_t)chunks;
-  *ml_bytes = align256(slots * num_q_heads * 2 * sizeof(float));
-  *total = *ml_bytes + align256(slots * num_q_heads * (size_t)head_dim * sizeof(float));
+  WsLayout w;
+  w.meta = 0;
+  w.ml = align256((size_t)num_seqs * 4 * sizeof(int32_t));
+  w.o = w.ml + align256(slots * num_q_heads * 2 * sizeof(float));
+  w.total = w.o + align256(slots * num_q_heads * (size_t)head_dim * sizeof(float));
+  return w;
 }
 
 int check_cache(const void* kv_cache, int64_t num_blocks, int32_t block_size, int32_t num_kv_heads,
@@ -123,9 +131,7 @@ size_t pa_attention_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t
   if (check_heads(num_q_heads, num_kv_heads) != PA_OK) return 0;
   const int group = num_q_heads / num_kv_heads;
   const int chunks = plan_chunks(num_seqs, num_kv_heads, group, max_seq_len, num_splits);
-  size_t ml = 0, total = 0;
-  workspace_layout(num_seqs, num_q_heads, head_dim, chunks, &ml, &total);
-  return total;
+  return workspace_layout(num_seqs, num_q_heads, head_dim, chunks).total;
 }
 
 static int attention_common(void* out, const void* q, const void* kv_cache, int64_t num_blocks,
@@ -147,9 +153,8 @@ static int attention_common(void* out, const void* q, const void* kv_cache, int6
   if (bt_stride < ceil_div(max_seq_len, pa::kBlockSize)) return PA_ERR_INVALID_ARG;
   const int group = num_q_heads / num_kv_heads;
   const int chunks = plan_chunks(num_seqs, num_kv_heads, group, max_seq_len, num_splits);
-  size_t ml = 0, total = 0;
-  workspace_layout(num_seqs, num_q_heads, head_dim, chunks, &ml, &total);
-  if (!workspace || workspace_bytes < total) return PA_ERR_WORKSPACE;
+  const WsLayout lay = workspace_layout(num_seqs, num_q_heads, head_dim, chunks);
+  if (!workspace || workspace_bytes < lay.total) return PA_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return PA_ERR_WORKSPACE;
 
   a->out = out;
@@ -165,8 +170,10 @@ static int attention_common(void* out, const void* q, const void* kv_cache, int6
   a->num_chunks = chunks;
   a->head_groups = group / heads_per_wave(group);
   a->scale_log2 = scale * 1.4426950408889634f;
-  a->ws_ml = static_cast<float*>(workspace);
-  a->ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + ml);
+  char* ws = static_cast<char*>(workspace);
+  a->ws_meta = reinterpret_cast<int32_t*>(ws + lay.meta);
+  a->ws_ml = reinterpret_cast<float*>(ws + lay.ml);
+  a->ws_o = reinterpret_cast<float*>(ws + lay.o);
   return 1;  // proceed
 }
 

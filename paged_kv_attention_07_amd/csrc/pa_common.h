@@ -106,6 +106,20 @@ __device__ __forceinline__ float shfl_xor(float x, int mask) { return __shfl_xor
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// Mark a value the whole wavefront agrees on as uniform, so that the compiler
+// keeps it (and loop counters / addresses derived from it) in scalar
+// registers and uses scalar loads for addresses built from it.
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Load through the constant address space: for a wave-uniform address this
+// becomes a scalar (SMEM) load, which does not share the in-order vector
+// memory counter with the bulk K/V loads.  Only for memory no kernel of the
+// launch writes (block tables, lengths).
+template <typename T>
+__device__ __forceinline__ T load_scalar(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)p;
+}
+
 // Uniform value of `x` in lane `l` (l uniform).
 __device__ __forceinline__ int readlane(int x, int l) { return __builtin_amdgcn_readlane(x, l); }
 

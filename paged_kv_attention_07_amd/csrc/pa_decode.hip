@@ -82,7 +82,8 @@ __device__ __forceinline__ ReqInfo req_info(const DecodeArgs& a, int r) {
 
 __device__ __forceinline__ int total_blocks(const DecodeArgs& a) {
   int W = 0;
-  for (int base = 0; base < a.num_seqs; base += kWave) W += wave_sum(req_info(a, base + lane_id()).nb);
+  for (int base = 0; base < a.num_seqs; base += kWave)
+    W += uniform(wave_sum(req_info(a, base + lane_id()).nb));
   return W;
 }
 
@@ -182,6 +183,121 @@ __device__ __forceinline__ void load_block(BlockRegs<E, D, HPW>& b, const uint8_
   }
 }
 
+// One 16-token block of one request: scores of tokens tg and tg+8 of the
+// block for the wave's query heads, running-max update, and P*V.
+template <typename E, int D, int HPW>
+__device__ __forceinline__ void attend_block(BlockRegs<E, D, HPW>& b, int j, int nb, int L,
+                                             int tg, float scale_log2,
+                                             const u32x4_t (&qv)[HPW][Shape<E, D, HPW>::NCH],
+                                             float (&m)[HPW], float (&l)[HPW],
+                                             float (&acc)[HPW][Shape<E, D, HPW>::DPL]) {
+  using S = Shape<E, D, HPW>;
+  // ---- scores of tokens tg and tg+8 for each head (log2 units)
+  float s0[HPW], s1[HPW];
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) {
+    float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+    for (int c = 0; c < S::NCH; ++c)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        if constexpr (E::kind == F32::kind) {
+          const float qf = __uint_as_float(qv[hh][c][w]);
+          a0 = fmaf(__uint_as_float(b.k0[c][w]), qf, a0);
+          a1 = fmaf(__uint_as_float(b.k1[c][w]), qf, a1);
+        } else if constexpr (E::kind == BF16::kind) {
+          a0 = dot2_bf16(b.k0[c][w], qv[hh][c][w], a0);
+          a1 = dot2_bf16(b.k1[c][w], qv[hh][c][w], a1);
+        } else {
+          a0 = dot2_f16(b.k0[c][w], qv[hh][c][w], a0);
+          a1 = dot2_f16(b.k1[c][w], qv[hh][c][w], a1);
+        }
+      }
+    s0[hh] = sum8(a0) * scale_log2;
+    s1[hh] = sum8(a1) * scale_log2;
+  }
+  // ---- partial last block: drop scores and values past the sequence end
+  if (j == nb - 1 && (L & (kBlockSize - 1))) {
+    const int nvalid = L - j * kBlockSize;
+    const bool ok0 = tg < nvalid, ok1 = tg + 8 < nvalid;
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) {
+      s0[hh] = ok0 ? s0[hh] : -INFINITY;
+      s1[hh] = ok1 ? s1[hh] : -INFINITY;
+    }
+#pragma unroll
+    for (int c = 0; c < S::NCH; ++c)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        b.v0[c][w] = ok0 ? b.v0[c][w] : 0u;
+        b.v1[c][w] = ok1 ? b.v1[c][w] : 0u;
+      }
+  }
+  // ---- running max; rescale only when it grows by more than 8 (log2 units)
+  bool grow = false;
+  float mn[HPW];
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) {
+    mn[hh] = fmaxf(m[hh], fmaxf(s0[hh], s1[hh]));
+    grow |= mn[hh] > m[hh] + 8.f;
+  }
+  if (__any(grow)) {
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) {
+      const float mu = (mn[hh] > m[hh] + 8.f) ? mn[hh] : m[hh];
+      const float alpha = (mu == m[hh]) ? 1.f : __builtin_amdgcn_exp2f(m[hh] - mu);
+      l[hh] *= alpha;
+#pragma unroll
+      for (int e = 0; e < S::DPL; ++e) acc[hh][e] *= alpha;
+      m[hh] = mu;
+    }
+  }
+  float p0[HPW], p1[HPW];
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) {
+    const float ms = (m[hh] == -INFINITY) ? 0.f : m[hh];
+    p0[hh] = __builtin_amdgcn_exp2f(s0[hh] - ms);
+    p1[hh] = __builtin_amdgcn_exp2f(s1[hh] - ms);
+    l[hh] += p0[hh] + p1[hh];
+  }
+  // ---- P * V
+  if constexpr (E::kind == F32::kind) {
+#pragma unroll
+    for (int c = 0; c < S::NCH; ++c)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float x0 = __uint_as_float(b.v0[c][w]);
+        const float x1 = __uint_as_float(b.v1[c][w]);
+#pragma unroll
+        for (int hh = 0; hh < HPW; ++hh)
+          acc[hh][c * 4 + w] = fmaf(p1[hh], x1, fmaf(p0[hh], x0, acc[hh][c * 4 + w]));
+      }
+  } else {
+    uint32_t pp[HPW];
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh)
+      pp[hh] = (E::kind == BF16::kind) ? pack_bf16(p0[hh], p1[hh]) : pack_f16(p0[hh], p1[hh]);
+#pragma unroll
+    for (int c = 0; c < S::NCH; ++c)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t lo = pair_lo(b.v0[c][w], b.v1[c][w]);
+        const uint32_t hi = pair_hi(b.v0[c][w], b.v1[c][w]);
+        const int e = c * S::EPV + 2 * w;
+#pragma unroll
+        for (int hh = 0; hh < HPW; ++hh) {
+          if constexpr (E::kind == BF16::kind) {
+            acc[hh][e] = dot2_bf16(lo, pp[hh], acc[hh][e]);
+            acc[hh][e + 1] = dot2_bf16(hi, pp[hh], acc[hh][e + 1]);
+          } else {
+            acc[hh][e] = dot2_f16(lo, pp[hh], acc[hh][e]);
+            acc[hh][e + 1] = dot2_f16(hi, pp[hh], acc[hh][e + 1]);
+          }
+        }
+      }
+  }
+}
+
 // Attention of one query row over keys [16*j0, min(16*j1, L)) of request r.
 template <typename E, int D, int HPW>
 __device__ __forceinline__ void process_range(const DecodeArgs& a, int r, int row, int L, int j0,
@@ -220,117 +336,32 @@ __device__ __forceinline__ void process_range(const DecodeArgs& a, int r, int ro
     for (int e = 0; e < S::DPL; ++e) acc[hh][e] = 0.f;
   }
 
-  BlockRegs<E, D, HPW> cur, nxt;
-  load_block<E, D, HPW>(cur, kvh + (int64_t)bt[j0] * blk_stride, tok8, half_stride);
-
-  for (int j = j0; j < j1; ++j) {
-    if (j + 1 < j1) load_block<E, D, HPW>(nxt, kvh + (int64_t)bt[j + 1] * blk_stride, tok8,
-                                          half_stride);
-    // ---- scores of tokens tg and tg+8 for each head (log2 units)
-    float s0[HPW], s1[HPW];
-#pragma unroll
-    for (int hh = 0; hh < HPW; ++hh) {
-      float a0 = 0.f, a1 = 0.f;
-#pragma unroll
-      for (int c = 0; c < S::NCH; ++c)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          if constexpr (E::kind == F32::kind) {
-            const float qf = __uint_as_float(qv[hh][c][w]);
-            a0 = fmaf(__uint_as_float(cur.k0[c][w]), qf, a0);
-            a1 = fmaf(__uint_as_float(cur.k1[c][w]), qf, a1);
-          } else if constexpr (E::kind == BF16::kind) {
-            a0 = dot2_bf16(cur.k0[c][w], qv[hh][c][w], a0);
-            a1 = dot2_bf16(cur.k1[c][w], qv[hh][c][w], a1);
-          } else {
-            a0 = dot2_f16(cur.k0[c][w], qv[hh][c][w], a0);
-            a1 = dot2_f16(cur.k1[c][w], qv[hh][c][w], a1);
-          }
-        }
-      s0[hh] = sum8(a0) * a.scale_log2;
-      s1[hh] = sum8(a1) * a.scale_log2;
+  // three register buffers: blocks j+1 and j+2 are in flight while block j
+  // is processed; block ids are read one step before their loads are issued
+  BlockRegs<E, D, HPW> b0, b1, b2;
+  int id_next = (j0 + 2 < j1) ? load_scalar(bt + j0 + 2) : 0;
+  load_block<E, D, HPW>(b0, kvh + (int64_t)load_scalar(bt + j0) * blk_stride, tok8, half_stride);
+  if (j0 + 1 < j1)
+    load_block<E, D, HPW>(b1, kvh + (int64_t)load_scalar(bt + j0 + 1) * blk_stride, tok8,
+                          half_stride);
+  int j = j0;
+  auto issue = [&](BlockRegs<E, D, HPW>& b) {
+    // load block j + 2 into b, then fetch the id of block j + 3
+    if (j + 2 < j1) {
+      load_block<E, D, HPW>(b, kvh + (int64_t)id_next * blk_stride, tok8, half_stride);
+      id_next = (j + 3 < j1) ? load_scalar(bt + j + 3) : 0;
     }
-    // ---- partial last block: drop scores and values past the sequence end
-    if (j == nb - 1 && (L & (kBlockSize - 1))) {
-      const int nvalid = L - j * kBlockSize;
-      const bool ok0 = tg < nvalid, ok1 = tg + 8 < nvalid;
-#pragma unroll
-      for (int hh = 0; hh < HPW; ++hh) {
-        s0[hh] = ok0 ? s0[hh] : -INFINITY;
-        s1[hh] = ok1 ? s1[hh] : -INFINITY;
-      }
-#pragma unroll
-      for (int c = 0; c < S::NCH; ++c)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          cur.v0[c][w] = ok0 ? cur.v0[c][w] : 0u;
-          cur.v1[c][w] = ok1 ? cur.v1[c][w] : 0u;
-        }
-    }
-    // ---- running max; rescale only when it grows by more than 8 (log2 units)
-    bool grow = false;
-    float mn[HPW];
-#pragma unroll
-    for (int hh = 0; hh < HPW; ++hh) {
-      mn[hh] = fmaxf(m[hh], fmaxf(s0[hh], s1[hh]));
-      grow |= mn[hh] > m[hh] + 8.f;
-    }
-    if (__any(grow)) {
-#pragma unroll
-      for (int hh = 0; hh < HPW; ++hh) {
-        const float mu = (mn[hh] > m[hh] + 8.f) ? mn[hh] : m[hh];
-        const float alpha = (mu == m[hh]) ? 1.f : __builtin_amdgcn_exp2f(m[hh] - mu);
-        l[hh] *= alpha;
-#pragma unroll
-        for (int e = 0; e < S::DPL; ++e) acc[hh][e] *= alpha;
-        m[hh] = mu;
-      }
-    }
-    float p0[HPW], p1[HPW];
-#pragma unroll
-    for (int hh = 0; hh < HPW; ++hh) {
-      const float ms = (m[hh] == -INFINITY) ? 0.f : m[hh];
-      p0[hh] = __builtin_amdgcn_exp2f(s0[hh] - ms);
-      p1[hh] = __builtin_amdgcn_exp2f(s1[hh] - ms);
-      l[hh] += p0[hh] + p1[hh];
-    }
-    // ---- P * V
-    if constexpr (E::kind == F32::kind) {
-#pragma unroll
-      for (int c = 0; c < S::NCH; ++c)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const float x0 = __uint_as_float(cur.v0[c][w]);
-          const float x1 = __uint_as_float(cur.v1[c][w]);
-#pragma unroll
-          for (int hh = 0; hh < HPW; ++hh)
-            acc[hh][c * 4 + w] = fmaf(p1[hh], x1, fmaf(p0[hh], x0, acc[hh][c * 4 + w]));
-        }
-    } else {
-      uint32_t pp[HPW];
-#pragma unroll
-      for (int hh = 0; hh < HPW; ++hh)
-        pp[hh] = (E::kind == BF16::kind) ? pack_bf16(p0[hh], p1[hh]) : pack_f16(p0[hh], p1[hh]);
-#pragma unroll
-      for (int c = 0; c < S::NCH; ++c)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const uint32_t lo = pair_lo(cur.v0[c][w], cur.v1[c][w]);
-          const uint32_t hi = pair_hi(cur.v0[c][w], cur.v1[c][w]);
-          const int e = c * S::EPV + 2 * w;
-#pragma unroll
-          for (int hh = 0; hh < HPW; ++hh) {
-            if constexpr (E::kind == BF16::kind) {
-              acc[hh][e] = dot2_bf16(lo, pp[hh], acc[hh][e]);
-              acc[hh][e + 1] = dot2_bf16(hi, pp[hh], acc[hh][e + 1]);
-            } else {
-              acc[hh][e] = dot2_f16(lo, pp[hh], acc[hh][e]);
-              acc[hh][e + 1] = dot2_f16(hi, pp[hh], acc[hh][e + 1]);
-            }
-          }
-        }
-    }
-    cur = nxt;
+  };
+  while (true) {
+    issue(b2);
+    attend_block<E, D, HPW>(b0, j, nb, L, tg, a.scale_log2, qv, m, l, acc);
+    if (++j >= j1) break;
+    issue(b0);
+    attend_block<E, D, HPW>(b1, j, nb, L, tg, a.scale_log2, qv, m, l, acc);
+    if (++j >= j1) break;
+    issue(b1);
+    attend_block<E, D, HPW>(b2, j, nb, L, tg, a.scale_log2, qv, m, l, acc);
+    if (++j >= j1) break;
   }
 
   // ---- merge the 8 token groups: common max, rescaled sums and accumulators
@@ -398,9 +429,9 @@ __device__ __forceinline__ void process_range(const DecodeArgs& a, int r, int ro
 }
 
 template <typename E, int D, int HPW>
-__global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_split_kernel(DecodeArgs a) {
   const int lane = lane_id();
-  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int item = uniform(blockIdx.x * 4 + (threadIdx.x >> 6));
   const int per_chunk = a.num_kv_heads * a.head_groups;
   if (item >= a.num_chunks * per_chunk) return;
   const int c = item / per_chunk;
@@ -430,6 +461,12 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
       const int j0 = (int)((b0 > s ? b0 : s) - s);
       const int j1 = (int)((b1 < e ? b1 : e) - s);
       const bool whole = (j0 == 0) && (j1 == e - s);
+      if (j0 == 0 && h == 0 && hs == 0 && lane == 0) {
+        // the range holding the request's first block records how it was cut
+        const int cl = whole ? -1 : chunk_of(e - 1, W, a.num_chunks);
+        int4 meta = {whole ? -1 : c, cl, W, 0};
+        *reinterpret_cast<int4*>(a.ws_meta + 4 * (int64_t)(base + src)) = meta;
+      }
       process_range<E, D, HPW>(a, base + src, row, L, j0, j1, h, hq0, whole, base + src + c);
     }
     running = readlane(incl, kWave - 1);
@@ -437,47 +474,79 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 }
 
 // Merge the partials of requests cut by range boundaries.  One wavefront per
-// (request, query head); lane owns D/64 consecutive dims.
+// (request, query head); lane owns D/64 consecutive dims.  The split kernel
+// recorded, for each decode request, its first and last range and W.  The
+// (max, sum) pairs of all ranges are read at once, one range per lane, and the
+// partial outputs in batches of 8 ranges, so the merge costs a few memory
+// round trips whatever the number of ranges.
 template <typename E, int D>
 __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   const int lane = lane_id();
   const int r = blockIdx.x / a.num_q_heads;
   const int hq = blockIdx.x - r * a.num_q_heads;
-  int W = 0, s = 0, e = 0, row = 0;
-  for (int base = 0; base < a.num_seqs; base += kWave) {
-    const ReqInfo ri = req_info(a, base + lane);
-    const int incl = wave_incl_scan(ri.nb) + W;
-    if (r >= base && r < base + kWave) {
-      const int src = r - base;
-      e = readlane(incl, src);
-      s = e - readlane(ri.nb, src);
-      row = readlane(ri.row, src);
-    }
-    W = readlane(incl, kWave - 1);
+  bool active = a.seq_lens[r] > 0;
+  int row = r;
+  if (a.qsl) {
+    const int q0 = a.qsl[r], q1 = a.qsl[r + 1];
+    active = active && (q1 - q0 == 1);
+    row = q0;
   }
-  if (e == s) return;
+  const int4 meta = *reinterpret_cast<const int4*>(a.ws_meta + 4 * (int64_t)r);
+  if (!active || meta.x < 0) return;  // finished in place by its range
+  const int cf = uniform(meta.x), cl = uniform(meta.y), W = uniform(meta.z);
   const int N = a.num_chunks;
-  const int cf = chunk_of(s, W, N), cl = chunk_of(e - 1, W, N);
-  if (cf == cl) return;  // finished in place by its range
+  const int64_t base = (int64_t)r * a.num_q_heads + hq;  // slot (r + c) -> + c * Hq
+
+  // pass 1: global max and weighted sum over ranges, lanes in parallel
+  float M = -INFINITY;
+  for (int c0 = cf; c0 <= cl; c0 += kWave) {
+    const int c = c0 + lane;
+    float mc = -INFINITY;
+    if (c <= cl && chunk_begin(c, W, N) < chunk_begin(c + 1, W, N))
+      mc = a.ws_ml[(base + (int64_t)c * a.num_q_heads) * 2];
+    M = fmaxf(M, mc);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, shfl_xor(M, o));
 
   constexpr int DPT = D / kWave;
-  float M = -INFINITY;
-  for (int c = cf; c <= cl; ++c) {
-    if (chunk_begin(c, W, N) == chunk_begin(c + 1, W, N)) continue;
-    M = fmaxf(M, a.ws_ml[((int64_t)(r + c) * a.num_q_heads + hq) * 2]);
-  }
   float lsum = 0.f, acc[DPT];
 #pragma unroll
   for (int i = 0; i < DPT; ++i) acc[i] = 0.f;
-  for (int c = cf; c <= cl; ++c) {
-    if (chunk_begin(c, W, N) == chunk_begin(c + 1, W, N)) continue;
-    const int64_t ps = (int64_t)(r + c) * a.num_q_heads + hq;
-    const float w = __builtin_amdgcn_exp2f(a.ws_ml[ps * 2] - M);
-    lsum += w * a.ws_ml[ps * 2 + 1];
-    const float* po = a.ws_o + ps * D + lane * DPT;
+  for (int c0 = cf; c0 <= cl; c0 += kWave) {
+    const int c = c0 + lane;
+    float w = 0.f;
+    if (c <= cl && chunk_begin(c, W, N) < chunk_begin(c + 1, W, N)) {
+      const f32x2_t ml = *reinterpret_cast<const f32x2_t*>(
+          a.ws_ml + (base + (int64_t)c * a.num_q_heads) * 2);
+      w = __builtin_amdgcn_exp2f(ml[0] - M);
+      lsum += w * ml[1];
+    }
+    // pass 2: this group of up to 64 ranges, 8 loads in flight at a time
+    const int n = min(kWave, cl - c0 + 1);
+    for (int k0 = 0; k0 < n; k0 += 8) {
+      float v[8][DPT], wk[8];
 #pragma unroll
-    for (int i = 0; i < DPT; ++i) acc[i] = fmaf(w, po[i], acc[i]);
+      for (int k = 0; k < 8; ++k) {
+        wk[k] = __shfl(w, k0 + k < n ? k0 + k : 0, kWave);
+        wk[k] = k0 + k < n ? wk[k] : 0.f;
+#pragma unroll
+        for (int i = 0; i < DPT; ++i) v[k][i] = 0.f;
+        if (wk[k] != 0.f) {
+          const float* po = a.ws_o + (base + (int64_t)(c0 + k0 + k) * a.num_q_heads) * D +
+                            lane * DPT;
+#pragma unroll
+          for (int i = 0; i < DPT; ++i) v[k][i] = po[i];
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+#pragma unroll
+        for (int i = 0; i < DPT; ++i) acc[i] = fmaf(wk[k], v[k][i], acc[i]);
+    }
   }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) lsum += shfl_xor(lsum, o);
   uint8_t* ob = static_cast<uint8_t*>(a.out) +
                 (((int64_t)row * a.num_q_heads + hq) * D + lane * DPT) * E::bytes;
   store_run<E, DPT>(ob, acc, 1.f / lsum);

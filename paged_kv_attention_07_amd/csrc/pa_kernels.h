@@ -26,6 +26,7 @@ struct DecodeArgs {
   float scale_log2;           // softmax scale * log2(e)
   float* ws_ml;               // [(R + num_chunks), Hq, 2]  (max, sum) per partial
   float* ws_o;                // [(R + num_chunks), Hq, D]  unnormalised partial outputs
+  int32_t* ws_meta;           // [R, 4]: first range, last range (-1: no merge), W, 0
 };
 
 // Arguments of the MFMA prefill-tile kernel.

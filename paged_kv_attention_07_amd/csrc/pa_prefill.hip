@@ -49,6 +49,7 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 
 constexpr int kKeysPerIter = 64;  // keys staged per iteration (4 paged blocks)
 
+
 template <int D>
 struct TileShape {
   static constexpr int ROWB = D * 2;              // bytes of one token's head row
@@ -56,11 +57,6 @@ struct TileShape {
   static constexpr int VROW = kKeysPerIter * 2 + 8;  // padded LDS row of V^T
   static constexpr int NKS = D / 32;              // MFMA k-steps of Q K^T
   static constexpr int NMT = D / 16;              // 16-dim tiles of the output
-  static constexpr int KCHUNKS = kKeysPerIter * ROWB / 16;        // 16-byte pieces of K
-  static constexpr int KPT = KCHUNKS / 256;                         // per thread
-  static constexpr int VITEMS = (kKeysPerIter / 2) * (D / 8);       // key pairs x 8-dim chunks
-  static constexpr int VPT = VITEMS / 256;
-  static_assert(KPT >= 1 && VPT >= 1, "tile shape");
 };
 
 // One work-group = 4 waves = WPW query heads x (4 / WPW) token sub-tiles of 16.
@@ -69,13 +65,14 @@ __global__ __launch_bounds__(256) void prefill_tile_kernel(PrefillArgs a) {
   using S = TileShape<D>;
   constexpr int NQS = 4 / WPW;       // 16-token sub-tiles per work-group
   constexpr int QT = 16 * NQS;       // tokens per tile
-  __shared__ __attribute__((aligned(16))) uint8_t lds_k[kKeysPerIter * S::KROW];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_v[D * S::VROW];
+  // two stages: the next 64 keys are staged while the current ones are used
+  __shared__ __attribute__((aligned(16))) uint8_t lds_k[2][kKeysPerIter * S::KROW];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_v[2][D * S::VROW];
   __shared__ int s_tile[2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = uniform(tid >> 6);
   const int group = a.num_q_heads / a.num_kv_heads;
   const int hg = group / WPW;
   const int h = blockIdx.y / hg;
@@ -108,15 +105,14 @@ __global__ __launch_bounds__(256) void prefill_tile_kernel(PrefillArgs a) {
     }
   }
   __syncthreads();
-  const int r = s_tile[0];
+  const int r = uniform(s_tile[0]);
   if (r < 0) return;
-  const int tile = s_tile[1];
+  const int tile = uniform(s_tile[1]);
 
   const int q0 = a.qsl[r];
   const int qlen = a.qsl[r + 1] - q0;
   const int nc = a.num_computed[r];
   const int L = a.seq_lens[r];
-  const int nb = (L + kBlockSize - 1) / kBlockSize;
   const int tile_start = tile * QT;
   const int tile_valid = min(QT, qlen - tile_start);
   const int kend = min(L, nc + tile_start + tile_valid);  // keys this tile needs
@@ -151,61 +147,70 @@ __global__ __launch_bounds__(256) void prefill_tile_kernel(PrefillArgs a) {
   const uint8_t* kvh = static_cast<const uint8_t*>(a.kv) + (int64_t)h * S::ROWB;
   const int32_t* bt = a.block_table + (int64_t)r * a.bt_stride;
 
-  // staging registers for one 64-key iteration
-  u32x4_t kreg[S::KPT], vreg[S::VPT][2];
-  auto fetch = [&](int it) {
-    const int key0 = it * kKeysPerIter;
+  // Physical ids of the 4 blocks holding keys [64 it, 64 it + 64): uniform
+  // across the work-group (scalar loads), fetched two iterations ahead of use.
+  const int nb_need = (kend + kBlockSize - 1) / kBlockSize;
+  // id of the paged block this wavefront stages in iteration it (scalar load)
+  auto block_id = [&](int it) {
+    const int lb = it * 4 + wave;
+    return lb < nb_need ? load_scalar(bt + lb) : 0;
+  };
+
+  // Staging: wavefront w moves paged block w of the iteration (keys
+  // 16w .. 16w+15), so the block id it needs is wave-uniform.  K rows go to
+  // LDS as they are; V goes in transposed, two keys per 32-bit word.
+  // K: lane l, step i -> key 4i + l/16 (D=128) or 8i + l/8 (D=64), 16-byte
+  // column l % CPR.  V: lane l, step i -> key pair 4i + l/16 (D=128) or l/8.
+  constexpr int CPR = S::ROWB / 16;          // 16-byte columns per row
+  constexpr int KPT = 16 * CPR / kWave;      // K pieces per lane per block
+  constexpr int VPT = 8 * (D / 8) / kWave;   // V key-pair items per lane per block
+  u32x4_t kreg[KPT], vreg[VPT][2];
+  auto fetch = [&](int it, int phys) {
+    const int key0 = it * kKeysPerIter + 16 * wave;
+    const uint8_t* blk = kvh + (int64_t)phys * blk_stride;
 #pragma unroll
-    for (int i = 0; i < S::KPT; ++i) {
-      const int c = tid + i * 256;
-      const int k = c / (S::ROWB / 16);
-      const int dc = c % (S::ROWB / 16);
-      const int key = key0 + k;
+    for (int i = 0; i < KPT; ++i) {
+      const int c = i * kWave + lane;
+      const int kb = c / CPR, dc = c % CPR;
       u32x4_t z = {0u, 0u, 0u, 0u};
       kreg[i] = z;
-      if (key < L) {
-        const int64_t phys = bt[key / kBlockSize];
-        kreg[i] = load16(kvh + phys * blk_stride + (key % kBlockSize) * tok_stride + dc * 16);
-      }
+      if (key0 + kb < kend)  // keys past the tile's last query are never visible
+        kreg[i] = load16(blk + kb * tok_stride + dc * 16);
     }
 #pragma unroll
-    for (int i = 0; i < S::VPT; ++i) {
-      const int it2 = tid + i * 256;
-      const int kp = it2 / (D / 8);
-      const int dc = it2 % (D / 8);
+    for (int i = 0; i < VPT; ++i) {
+      const int c = i * kWave + lane;
+      const int kp = c / (D / 8), dc = c % (D / 8);
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        const int key = key0 + 2 * kp + e;
+        const int kb = 2 * kp + e;
         u32x4_t z = {0u, 0u, 0u, 0u};
         vreg[i][e] = z;
-        if (key < L) {
-          const int64_t phys = bt[key / kBlockSize];
-          vreg[i][e] = load16(kvh + phys * blk_stride + half_stride +
-                              (key % kBlockSize) * tok_stride + dc * 16);
-        }
+        if (key0 + kb < kend)
+          vreg[i][e] = load16(blk + half_stride + kb * tok_stride + dc * 16);
       }
     }
   };
-  auto stage = [&]() {
+  auto stage = [&](int buf) {
+    uint8_t* lk = lds_k[buf];
+    uint8_t* lv = lds_v[buf];
 #pragma unroll
-    for (int i = 0; i < S::KPT; ++i) {
-      const int c = tid + i * 256;
-      const int k = c / (S::ROWB / 16);
-      const int dc = c % (S::ROWB / 16);
-      *reinterpret_cast<u32x4_t*>(lds_k + k * S::KROW + dc * 16) = kreg[i];
+    for (int i = 0; i < KPT; ++i) {
+      const int c = i * kWave + lane;
+      const int kb = c / CPR, dc = c % CPR;
+      *reinterpret_cast<u32x4_t*>(lk + (16 * wave + kb) * S::KROW + dc * 16) = kreg[i];
     }
 #pragma unroll
-    for (int i = 0; i < S::VPT; ++i) {
-      const int it2 = tid + i * 256;
-      const int kp = it2 / (D / 8);
-      const int dc = it2 % (D / 8);
+    for (int i = 0; i < VPT; ++i) {
+      const int c = i * kWave + lane;
+      const int kp = 8 * wave + c / (D / 8), dc = c % (D / 8);
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         // dims 8dc + 2w (lo) and 8dc + 2w + 1 (hi), keys 2kp and 2kp + 1
         const uint32_t lo = pair_lo(vreg[i][0][w], vreg[i][1][w]);
         const uint32_t hi = pair_hi(vreg[i][0][w], vreg[i][1][w]);
-        *reinterpret_cast<uint32_t*>(lds_v + (8 * dc + 2 * w) * S::VROW + 4 * kp) = lo;
-        *reinterpret_cast<uint32_t*>(lds_v + (8 * dc + 2 * w + 1) * S::VROW + 4 * kp) = hi;
+        *reinterpret_cast<uint32_t*>(lv + (8 * dc + 2 * w) * S::VROW + 4 * kp) = lo;
+        *reinterpret_cast<uint32_t*>(lv + (8 * dc + 2 * w + 1) * S::VROW + 4 * kp) = hi;
       }
     }
   };
@@ -215,12 +220,19 @@ __global__ __launch_bounds__(256) void prefill_tile_kernel(PrefillArgs a) {
   for (int mt = 0; mt < S::NMT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, lsum = 0.f;
 
-  fetch(0);
+  // id_cur: block of iteration it + 1 (fetched during iteration it); id_nxt:
+  // iteration it + 2 -- block-table reads run two iterations ahead.
+  int id_cur = block_id(0), id_nxt;
+  fetch(0, id_cur);
+  stage(0);
+  id_cur = block_id(1);
+  id_nxt = block_id(2);
+  __syncthreads();
   for (int it = 0; it < niter; ++it) {
-    __syncthreads();
-    stage();
-    __syncthreads();
-    if (it + 1 < niter) fetch(it + 1);
+    const int buf = it & 1;
+    if (it + 1 < niter) fetch(it + 1, id_cur);
+    const uint8_t* lds_kc = lds_k[buf];
+    const uint8_t* lds_vc = lds_v[buf];
 
     // ---- S^T for 64 keys x 16 tokens: 4 tiles of 16 keys
     f32x4_t st[4];
@@ -229,7 +241,7 @@ __global__ __launch_bounds__(256) void prefill_tile_kernel(PrefillArgs a) {
       st[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < S::NKS; ++s) {
-        const u32x4_t ka = *reinterpret_cast<const u32x4_t*>(lds_k + (16 * t + n) * S::KROW +
+        const u32x4_t ka = *reinterpret_cast<const u32x4_t*>(lds_kc + (16 * t + n) * S::KROW +
                                                               s * 64 + g * 16);
         st[t] = mfma16x16x32<E>(ka, qf[s], st[t]);
       }
@@ -285,13 +297,19 @@ __global__ __launch_bounds__(256) void prefill_tile_kernel(PrefillArgs a) {
       pb[3] = pack2<E>(p[2 * s2 + 1][2], p[2 * s2 + 1][3]);
 #pragma unroll
       for (int mt = 0; mt < S::NMT; ++mt) {
-        const uint8_t* vp = lds_v + (16 * mt + n) * S::VROW + (32 * s2 + 4 * g) * 2;
+        const uint8_t* vp = lds_vc + (16 * mt + n) * S::VROW + (32 * s2 + 4 * g) * 2;
         const uint2 lo = *reinterpret_cast<const uint2*>(vp);
         const uint2 hi = *reinterpret_cast<const uint2*>(vp + 32);
         u32x4_t va = {lo.x, lo.y, hi.x, hi.y};
         acc[mt] = mfma16x16x32<E>(va, pb, acc[mt]);
       }
     }
+    if (it + 1 < niter) {
+      stage(buf ^ 1);
+      id_cur = id_nxt;
+      id_nxt = block_id(it + 3);
+    }
+    __syncthreads();
   }
 
   // ---- normalise and store: lane holds dims 16mt + 4g + (0..3) of token n

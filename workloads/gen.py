@@ -311,6 +311,13 @@ def _mixed_bf16(seed: int, values: bool = True) -> Workload:
                           values=values)
 
 
+def _prefill_chunk_bf16(seed: int, values: bool = True) -> Workload:
+    # the mixed step's prefill chunk alone: 512 new tokens on 1024 cached
+    return build_workload("prefill_chunk_bf16", **_LLAMA3, num_blocks=20000,
+                          requests=[(1024, 512)], seed=seed, table_width=128,
+                          values=values)
+
+
 def _prefix_shared_bf16(seed: int, values: bool = True) -> Workload:
     rng = np.random.default_rng(seed + 7_000_000)
     suffix = rng.integers(64, 512, size=256, endpoint=True)
@@ -370,6 +377,7 @@ _BUILDERS = {
     "decode_bf16_64req": (_decode_bf16, 1002),
     "mixed_chunked_prefill_bf16": (_mixed_bf16, 1003),
     "prefix_shared_decode_bf16": (_prefix_shared_bf16, 1004),
+    "prefill_chunk_bf16": (_prefill_chunk_bf16, 1006),
     "long_context_decode_bf16": (_long_split_bf16, 1005),
     "decode_bf16_small": (_decode_bf16_small, 2002),
     "mixed_bf16_small": (_mixed_bf16_small, 2003),
