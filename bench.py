@@ -132,7 +132,7 @@ class Stepper:
         nbytes = pa.pa_attention_workspace_size(w.num_seqs, w.num_tokens, w.num_q_heads,
                                                 w.num_kv_heads, w.head_dim, w.max_seq_len,
                                                 w.max_query_len, splits)
-        self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device="cuda")
+        self.ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device="cuda")
         self.decode = w.is_decode_only
 
     def attention(self, kv):
@@ -172,6 +172,23 @@ class Stepper:
         t1 = time.perf_counter()
         attn_ms = [a.elapsed_time(b) for a, b in events]
         return (t1 - t0) * 1e3 / steps, attn_ms
+
+
+def recorded_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    passes (profiles/traffic.json), or None if the kernel's sources changed
+    since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        rec = json.load(open(path))[kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    h = hashlib.sha256()
+    for src in rec["sources"]:
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    return rec["hbm_bytes_per_launch"] if h.hexdigest() == rec["sources_sha256"] else None
 
 
 def gpu_info():
@@ -216,6 +233,18 @@ def cpu_baseline(w, budget_s: float = 12.0):
             if t_attn >= budget_s:
                 break
         n = len(sample)
+        passes = 1
+        if n == len(order):
+            # the whole batch fit the budget: time more full passes, keep the best
+            best, spent = t_attn, t_attn
+            while passes < 3 and spent + best < budget_s:
+                t0 = time.perf_counter()
+                oracle.paged_attention(w.q, pool, w.block_table, w.seq_lens,
+                                       w.query_start_loc, w.num_computed, w.scale, w.dtype,
+                                       requests=order)
+                dt = time.perf_counter() - t0
+                best, spent, passes = min(best, dt), spent + dt, passes + 1
+            t_attn = best
     finally:
         if ctx is not None:
             ctx.__exit__(None, None, None)
@@ -230,7 +259,8 @@ def cpu_baseline(w, budget_s: float = 12.0):
         "value": round(byts / t_total / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
         "sample": f"{n} of {len(order)} requests of {w.name} (slot mapping excluded, "
                   f"scatter charged pro rata): {toks} query tokens, {keys} keys, "
-                  f"{t_total:.2f} s fp64 numpy, BLAS 1 thread",
+                  f"{t_total:.2f} s fp64 numpy, BLAS 1 thread"
+                  + (f", best of {passes} full passes" if passes > 1 else ""),
         "tokens_per_s": round(toks / t_total, 3),
         "cpu": platform.processor() or platform.machine(),
         "host_cores_available": len(os.sched_getaffinity(0)),
@@ -271,6 +301,9 @@ def main():
     ap.add_argument("--extra", action="store_true", help="also time the prefix-shared and "
                     "long-context decode batches")
     ap.add_argument("--only", choices=sorted(WORKLOADS), default=None)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="after timing, copy 1 GiB device-to-device 3 times (a kernel of "
+                         "known traffic, to calibrate the profiler's FETCH_SIZE/WRITE_SIZE)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -310,7 +343,9 @@ def main():
         "pct_peak_hbm": round(100 * value / HBM_PEAK_GBS, 2),
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": recorded_traffic("decode_split_kernel"),
+            "traffic_kernel": "decode_split_kernel (profiles/traffic.json)",
             "kernel": "pa_attention_decode (decode_split_kernel + decode_merge_kernel)",
             "alg_bytes_per_launch": int(c["attn_logical"]),
             "avg_launch_us": round(head["attn_ms_avg"] * 1e3, 2),
@@ -352,6 +387,15 @@ def main():
                 "effective_gbs_logical": round(rc["attn_logical"] / (r["attn_ms_avg"] * 1e-3) / 1e9, 1),
                 "ms_per_step": round(r["ms_step"], 5),
             }
+    if args.copy_probe:
+        # an elementwise kernel that reads 1 GiB and writes 1 GiB
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        line["copy_probe_bytes"] = 1 << 30
+        del src, dst
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(line), flush=True)

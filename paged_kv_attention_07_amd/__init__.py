@@ -87,8 +87,7 @@ def _check(fn: str, status: int) -> None:
 
 
 def _torch():
-    import torch  # deferred so that the ABI can be loaded without torch's GPU state
-    return torch
+    return _torch_module
 
 
 def _dtype_code(t) -> int:
@@ -164,9 +163,11 @@ def pa_attention_workspace_size(num_seqs: int, num_tokens: int, num_q_heads: int
 
 
 def _workspace(nbytes: int, device, workspace):
+    """A caller-supplied workspace, or a new one (its contents on entry do not
+    matter to the library; zero-filled here for reproducible debugging)."""
     torch = _torch()
     if workspace is None:
-        return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        return torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
     if workspace.numel() * workspace.element_size() < nbytes:
         raise ValueError(f"workspace too small: need {nbytes} bytes")
     return workspace

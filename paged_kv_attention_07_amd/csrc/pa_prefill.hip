@@ -59,20 +59,28 @@ struct TileShape {
   static constexpr int NMT = D / 16;              // 16-dim tiles of the output
 };
 
-// One work-group = 4 waves = WPW query heads x (4 / WPW) token sub-tiles of 16.
+// One work-group = 8 waves = 2 key halves x 4 waves; the 4 waves of a half
+// are WPW query heads x (4 / WPW) token sub-tiles of 16.  The two halves
+// split the tile's key range (iterations [0, n0) and [n0, n)), each with its
+// own double-buffered LDS stages, and are merged through LDS at the end.
 template <typename E, int D, int WPW>
-__global__ __launch_bounds__(256) void prefill_tile_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(512) void prefill_tile_kernel(PrefillArgs a) {
   using S = TileShape<D>;
   constexpr int NQS = 4 / WPW;       // 16-token sub-tiles per work-group
   constexpr int QT = 16 * NQS;       // tokens per tile
-  // two stages: the next 64 keys are staged while the current ones are used
-  __shared__ __attribute__((aligned(16))) uint8_t lds_k[2][kKeysPerIter * S::KROW];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_v[2][D * S::VROW];
+  constexpr int KBUF = kKeysPerIter * S::KROW;
+  constexpr int VBUF = D * S::VROW;
+  // [half][stage]: the next 64 keys of each half are staged while the
+  // current ones are used
+  __shared__ __attribute__((aligned(16))) uint8_t lds_k[2][2][KBUF];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_v[2][2][VBUF];
   __shared__ int s_tile[2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = uniform(tid >> 6);
+  const int half = wave >> 2;                // key half
+  const int w4 = wave & 3;                   // wave within the half
   const int group = a.num_q_heads / a.num_kv_heads;
   const int hg = group / WPW;
   const int h = blockIdx.y / hg;
@@ -117,9 +125,12 @@ __global__ __launch_bounds__(256) void prefill_tile_kernel(PrefillArgs a) {
   const int tile_valid = min(QT, qlen - tile_start);
   const int kend = min(L, nc + tile_start + tile_valid);  // keys this tile needs
   const int niter = (kend + kKeysPerIter - 1) / kKeysPerIter;
+  const int n0 = (niter + 1) / 2;            // iterations of half 0
+  const int it_begin = half ? n0 : 0;
+  const int my_iters = half ? niter - n0 : n0;  // n0 or n0 - 1 (or 0)
 
-  const int hw = wave % WPW;                 // head within the group
-  const int sub = wave / WPW;                // 16-token sub-tile
+  const int hw = w4 % WPW;                   // head within the group
+  const int sub = w4 / WPW;                  // 16-token sub-tile
   const int hq = h * group + hs * WPW + hw;
   const int n = lane & 15;                   // token column of this lane
   const int g = lane >> 4;                   // lane group
@@ -147,70 +158,69 @@ __global__ __launch_bounds__(256) void prefill_tile_kernel(PrefillArgs a) {
   const uint8_t* kvh = static_cast<const uint8_t*>(a.kv) + (int64_t)h * S::ROWB;
   const int32_t* bt = a.block_table + (int64_t)r * a.bt_stride;
 
-  // Physical ids of the 4 blocks holding keys [64 it, 64 it + 64): uniform
-  // across the work-group (scalar loads), fetched two iterations ahead of use.
+  // id of the paged block this wavefront stages in (global) iteration it
   const int nb_need = (kend + kBlockSize - 1) / kBlockSize;
-  // id of the paged block this wavefront stages in iteration it (scalar load)
   auto block_id = [&](int it) {
-    const int lb = it * 4 + wave;
+    const int lb = it * 4 + w4;
     return lb < nb_need ? load_scalar(bt + lb) : 0;
   };
 
-  // Staging: wavefront w moves paged block w of the iteration (keys
-  // 16w .. 16w+15), so the block id it needs is wave-uniform.  K rows go to
-  // LDS as they are; V goes in transposed, two keys per 32-bit word.
-  // K: lane l, step i -> key 4i + l/16 (D=128) or 8i + l/8 (D=64), 16-byte
-  // column l % CPR.  V: lane l, step i -> key pair 4i + l/16 (D=128) or l/8.
+  // Staging: wavefront w4 of a half moves paged block w4 of the half's
+  // iteration (keys 16 w4 .. 16 w4 + 15), so its block id is wave-uniform.
+  // K rows go to LDS unchanged (lane l, step i: key (64 i + l) / CPR, 16-byte
+  // column l % CPR).  V goes in transposed, two keys per 32-bit word: lane l,
+  // step i handles key pair l % 8 and 8-dim column 8 i + l / 8, so the lanes
+  // of one store write consecutive words.
   constexpr int CPR = S::ROWB / 16;          // 16-byte columns per row
   constexpr int KPT = 16 * CPR / kWave;      // K pieces per lane per block
-  constexpr int VPT = 8 * (D / 8) / kWave;   // V key-pair items per lane per block
-  u32x4_t kreg[KPT], vreg[VPT][2];
-  auto fetch = [&](int it, int phys) {
-    const int key0 = it * kKeysPerIter + 16 * wave;
+  constexpr int VPT = (D / 8) / 8;           // V column groups per lane per block
+  struct Regs {
+    u32x4_t k[KPT], v[VPT][2];
+  };
+  // Loads are issued unconditionally (every address stays inside a real
+  // block: ids past the table's end read block 0, rows past kend read their
+  // own block) and keys past kend are zeroed when staged, so the compiler can
+  // wait for exactly the loads a stage needs.
+  auto fetch = [&](Regs& R, int phys) {
     const uint8_t* blk = kvh + (int64_t)phys * blk_stride;
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int c = i * kWave + lane;
       const int kb = c / CPR, dc = c % CPR;
-      u32x4_t z = {0u, 0u, 0u, 0u};
-      kreg[i] = z;
-      if (key0 + kb < kend)  // keys past the tile's last query are never visible
-        kreg[i] = load16(blk + kb * tok_stride + dc * 16);
+      R.k[i] = load16(blk + kb * tok_stride + dc * 16);
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
-      const int c = i * kWave + lane;
-      const int kp = c / (D / 8), dc = c % (D / 8);
+      const int kp = lane & 7, dc = 8 * i + (lane >> 3);
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int kb = 2 * kp + e;
-        u32x4_t z = {0u, 0u, 0u, 0u};
-        vreg[i][e] = z;
-        if (key0 + kb < kend)
-          vreg[i][e] = load16(blk + half_stride + kb * tok_stride + dc * 16);
-      }
+      for (int e = 0; e < 2; ++e)
+        R.v[i][e] = load16(blk + half_stride + (2 * kp + e) * tok_stride + dc * 16);
     }
   };
-  auto stage = [&](int buf) {
-    uint8_t* lk = lds_k[buf];
-    uint8_t* lv = lds_v[buf];
+  auto stage = [&](const Regs& R, int it, int buf) {
+    uint8_t* lk = lds_k[half][buf];
+    uint8_t* lv = lds_v[half][buf];
+    const int key0 = it * kKeysPerIter + 16 * w4;
+    const u32x4_t z = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int c = i * kWave + lane;
       const int kb = c / CPR, dc = c % CPR;
-      *reinterpret_cast<u32x4_t*>(lk + (16 * wave + kb) * S::KROW + dc * 16) = kreg[i];
+      // keys past the tile's last query are never visible: store zeros
+      *reinterpret_cast<u32x4_t*>(lk + (16 * w4 + kb) * S::KROW + dc * 16) =
+          key0 + kb < kend ? R.k[i] : z;
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
-      const int c = i * kWave + lane;
-      const int kp = 8 * wave + c / (D / 8), dc = c % (D / 8);
+      const int kp = 8 * w4 + (lane & 7), dc = 8 * i + (lane >> 3);
+      const bool ok0 = key0 + 2 * (lane & 7) < kend, ok1 = key0 + 2 * (lane & 7) + 1 < kend;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         // dims 8dc + 2w (lo) and 8dc + 2w + 1 (hi), keys 2kp and 2kp + 1
-        const uint32_t lo = pair_lo(vreg[i][0][w], vreg[i][1][w]);
-        const uint32_t hi = pair_hi(vreg[i][0][w], vreg[i][1][w]);
-        *reinterpret_cast<uint32_t*>(lv + (8 * dc + 2 * w) * S::VROW + 4 * kp) = lo;
-        *reinterpret_cast<uint32_t*>(lv + (8 * dc + 2 * w + 1) * S::VROW + 4 * kp) = hi;
+        const uint32_t v0 = ok0 ? R.v[i][0][w] : 0u, v1 = ok1 ? R.v[i][1][w] : 0u;
+        *reinterpret_cast<uint32_t*>(lv + (8 * dc + 2 * w) * S::VROW + 4 * kp) = pair_lo(v0, v1);
+        *reinterpret_cast<uint32_t*>(lv + (8 * dc + 2 * w + 1) * S::VROW + 4 * kp) =
+            pair_hi(v0, v1);
       }
     }
   };
@@ -220,30 +230,20 @@ __global__ __launch_bounds__(256) void prefill_tile_kernel(PrefillArgs a) {
   for (int mt = 0; mt < S::NMT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, lsum = 0.f;
 
-  // id_cur: block of iteration it + 1 (fetched during iteration it); id_nxt:
-  // iteration it + 2 -- block-table reads run two iterations ahead.
-  int id_cur = block_id(0), id_nxt;
-  fetch(0, id_cur);
-  stage(0);
-  id_cur = block_id(1);
-  id_nxt = block_id(2);
-  __syncthreads();
-  for (int it = 0; it < niter; ++it) {
-    const int buf = it & 1;
-    if (it + 1 < niter) fetch(it + 1, id_cur);
-    const uint8_t* lds_kc = lds_k[buf];
-    const uint8_t* lds_vc = lds_v[buf];
-
+  // One 64-key iteration from LDS stage `buf`: S^T, online softmax, O^T.
+  auto compute = [&](int it, int buf) {
+    const uint8_t* lds_kc = lds_k[half][buf];
+    const uint8_t* lds_vc = lds_v[half][buf];
     // ---- S^T for 64 keys x 16 tokens: 4 tiles of 16 keys
     f32x4_t st[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      st[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int tt = 0; tt < 4; ++tt) {
+      st[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < S::NKS; ++s) {
-        const u32x4_t ka = *reinterpret_cast<const u32x4_t*>(lds_kc + (16 * t + n) * S::KROW +
-                                                              s * 64 + g * 16);
-        st[t] = mfma16x16x32<E>(ka, qf[s], st[t]);
+        const u32x4_t ka = *reinterpret_cast<const u32x4_t*>(
+            lds_kc + (16 * tt + n) * S::KROW + s * 64 + g * 16);
+        st[tt] = mfma16x16x32<E>(ka, qf[s], st[tt]);
       }
     }
     // ---- scale to log2 units and apply the causal mask on diagonal tiles
@@ -251,20 +251,20 @@ __global__ __launch_bounds__(256) void prefill_tile_kernel(PrefillArgs a) {
     float x[4][4];
     const bool diag = key0 + kKeysPerIter - 1 > nc + sub_start;
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        x[t][i] = st[t][i] * a.scale_log2;
+        x[tt][i] = st[tt][i] * a.scale_log2;
         if (diag) {
-          const int key = key0 + 16 * t + 4 * g + i;
-          x[t][i] = key <= pos ? x[t][i] : -INFINITY;
+          const int key = key0 + 16 * tt + 4 * g + i;
+          x[tt][i] = key <= pos ? x[tt][i] : -INFINITY;
         }
       }
     float mx = x[0][0];
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, x[t][i]);
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, x[tt][i]);
     mx = fmaxf(mx, shfl_xor(mx, 16));
     mx = fmaxf(mx, shfl_xor(mx, 32));
     const float mn = fmaxf(m, mx);
@@ -280,11 +280,11 @@ __global__ __launch_bounds__(256) void prefill_tile_kernel(PrefillArgs a) {
     const float ms = (m == -INFINITY) ? 0.f : m;
     float p[4][4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        p[t][i] = __builtin_amdgcn_exp2f(x[t][i] - ms);
-        lsum += p[t][i];
+        p[tt][i] = __builtin_amdgcn_exp2f(x[tt][i] - ms);
+        lsum += p[tt][i];
       }
     // ---- O^T += V^T P^T, 32 keys per MFMA: lane group g holds keys
     // 32s2 + 4g + (0..3) and 32s2 + 16 + 4g + (0..3)
@@ -304,17 +304,64 @@ __global__ __launch_bounds__(256) void prefill_tile_kernel(PrefillArgs a) {
         acc[mt] = mfma16x16x32<E>(va, pb, acc[mt]);
       }
     }
-    if (it + 1 < niter) {
-      stage(buf ^ 1);
-      id_cur = id_nxt;
-      id_nxt = block_id(it + 3);
-    }
+  };
+
+  // Both halves run n0 loop trips in lockstep (one barrier per trip); a half
+  // with fewer iterations idles on its last trip.  Trip t computes iteration
+  // it_begin + t from LDS stage t & 1, issues the loads of iteration
+  // it_begin + t + 2 into register set t & 1, and stages iteration
+  // it_begin + t + 1 from the other set (loaded one trip earlier).
+  Regs R0, R1;
+  fetch(R0, block_id(it_begin));
+  if (my_iters > 0) stage(R0, it_begin, 0);
+  fetch(R1, block_id(it_begin + 1));
+  int id_ahead = block_id(it_begin + 2);
+  __syncthreads();
+  auto trip = [&](int t, Regs& Rload, const Regs& Rstage) {
+    const int buf = t & 1;
+    const int it = it_begin + t;
+    fetch(Rload, id_ahead);  // unconditional: past the range it reads block 0, never staged
+    id_ahead = block_id(it + 3);
+    if (t < my_iters) compute(it, buf);
+    if (t + 1 < my_iters) stage(Rstage, it + 1, buf ^ 1);
     __syncthreads();
+  };
+  for (int t = 0; t < n0; t += 2) {
+    trip(t, R0, R1);
+    if (t + 1 < n0) trip(t + 1, R1, R0);
+  }
+
+  // ---- merge the halves: half 1 leaves (max, row sum, O^T) in LDS
+  lsum += shfl_xor(lsum, 16);
+  lsum += shfl_xor(lsum, 32);
+  constexpr int NF = S::NMT * 4 + 2;         // floats per lane
+  static_assert(4 * kWave * NF * 4 <= 2 * KBUF, "merge buffer must fit in half 1's K stages");
+  float* xch = reinterpret_cast<float*>(&lds_k[1][0][0]);  // half 1's stages, now free
+  if (half == 1) {
+    float* dst = xch + (w4 * kWave + lane) * NF;
+#pragma unroll
+    for (int mt = 0; mt < S::NMT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[4 * mt + i] = acc[mt][i];
+    dst[NF - 2] = m;
+    dst[NF - 1] = lsum;
+  }
+  __syncthreads();
+  if (half == 1) return;
+  {
+    const float* src = xch + (w4 * kWave + lane) * NF;
+    const float m1 = src[NF - 2], l1 = src[NF - 1];
+    const float M = fmaxf(m, m1);            // m is finite: key 0 is visible
+    const float a0 = __builtin_amdgcn_exp2f(m - M);
+    const float a1 = (m1 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m1 - M);
+    lsum = lsum * a0 + l1 * a1;
+#pragma unroll
+    for (int mt = 0; mt < S::NMT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[mt][i] = acc[mt][i] * a0 + src[4 * mt + i] * a1;
   }
 
   // ---- normalise and store: lane holds dims 16mt + 4g + (0..3) of token n
-  lsum += shfl_xor(lsum, 16);
-  lsum += shfl_xor(lsum, 32);
   if (n < sub_valid) {
     const float inv = 1.f / lsum;
     uint8_t* op = static_cast<uint8_t*>(a.out) +
@@ -333,7 +380,7 @@ template <typename E, int D, int WPW>
 hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream) {
   const int group = a.num_q_heads / a.num_kv_heads;
   const dim3 grid((unsigned)a.max_tiles, (unsigned)(a.num_kv_heads * (group / WPW)));
-  hipLaunchKernelGGL((prefill_tile_kernel<E, D, WPW>), grid, dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((prefill_tile_kernel<E, D, WPW>), grid, dim3(512), 0, stream, a);
   return hipGetLastError();
 }
 

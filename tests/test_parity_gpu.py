@@ -249,3 +249,32 @@ def test_full_prefix_shared():
 def test_full_long_context_sampled():
     w = workload("long_context_decode_bf16")
     full_check(w, requests=[0, 7, 15])
+
+
+def test_workspace_reused_across_calls():
+    """One workspace serves many calls with different batches and split
+    counts: nothing a call leaves in it affects the next call."""
+    import torch
+    cases = [(workload("decode_bf16_small"), 7), (workload("long_decode_small"), 0),
+             (workload("decode_bf16_small"), 333), (workload("mixed_bf16_small"), 5),
+             (workload("long_decode_small"), 64)]
+    nbytes = max(pa.pa_attention_workspace_size(w.num_seqs, w.num_tokens, w.num_q_heads,
+                                                w.num_kv_heads, w.head_dim, w.max_seq_len,
+                                                w.max_query_len, s) for w, s in cases)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    for rep in range(2):
+        for w, splits in cases:
+            pool = gu.poisoned_pool(w)
+            dev = gu.Device(w, pool)
+            dev.scatter(dev.slot_mapping())
+            if w.is_decode_only:
+                out = pa.pa_attention_decode(dev.q, dev.kv, dev.block_table, dev.seq_lens,
+                                             w.scale, w.max_seq_len, workspace=ws,
+                                             num_splits=splits)
+            else:
+                out = pa.pa_attention_mixed(dev.q, dev.kv, dev.block_table, dev.seq_lens,
+                                            dev.qsl, dev.num_computed, w.scale,
+                                            w.max_query_len, w.max_seq_len, workspace=ws,
+                                            num_splits=splits)
+            _, _, ref = gu.oracle_step(w, pool)
+            gu.check_close(w, gu.from_device(out, w.dtype), ref, what=f"{w.name}/{splits}")
