@@ -16,7 +16,8 @@ the earlier tokens of the chunk, a decode token attends all its history).
 The oracle gathers K/V through the block table and writes that definition out
 in float64.  Readings of points the pages leave open:
   * seq_lens[r] counts every key the request's last query sees, including the
-    tokens written this step ([P4] §4.2, "1 new + 754 history" = 755 keys);
+    tokens written this step ([P4] §4.2: a decode request with 754 cached
+    tokens attends 755 keys);
   * GQA query head h reads KV head h // (Hq / Hkv) (contiguous groups);
   * scale is an argument (1/sqrt(head_dim) in [P1] §4.2's sketch);
   * a negative slot means "padding token, write nothing";

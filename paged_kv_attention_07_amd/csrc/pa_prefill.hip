@@ -181,48 +181,68 @@ __global__ __launch_bounds__(512) void prefill_tile_kernel(PrefillArgs a) {
   // block: ids past the table's end read block 0, rows past kend read their
   // own block) and keys past kend are zeroed when staged, so the compiler can
   // wait for exactly the loads a stage needs.
+  // Per-lane byte offsets inside a block (32-bit): with the block base
+  // wave-uniform, every load is scalar base + vector offset.
+  uint32_t koff[KPT], voff[VPT][2];
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    const int c = i * kWave + lane;
+    koff[i] = (uint32_t)((c / CPR) * tok_stride + (c % CPR) * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < VPT; ++i)
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+      voff[i][e] = (uint32_t)(half_stride + (2 * (lane & 7) + e) * tok_stride +
+                              (8 * i + (lane >> 3)) * 16);
   auto fetch = [&](Regs& R, int phys) {
     const uint8_t* blk = kvh + (int64_t)phys * blk_stride;
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int c = i * kWave + lane;
-      const int kb = c / CPR, dc = c % CPR;
-      R.k[i] = load16(blk + kb * tok_stride + dc * 16);
-    }
+    for (int i = 0; i < KPT; ++i) R.k[i] = load16(blk + koff[i]);
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int kp = lane & 7, dc = 8 * i + (lane >> 3);
+    for (int i = 0; i < VPT; ++i)
 #pragma unroll
-      for (int e = 0; e < 2; ++e)
-        R.v[i][e] = load16(blk + half_stride + (2 * kp + e) * tok_stride + dc * 16);
-    }
+      for (int e = 0; e < 2; ++e) R.v[i][e] = load16(blk + voff[i][e]);
   };
-  auto stage = [&](const Regs& R, int it, int buf) {
+  // LDS offsets of this lane's staged pieces
+  uint32_t kdst[KPT], vdst[VPT];
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    const int c = i * kWave + lane;
+    kdst[i] = (uint32_t)((16 * w4 + c / CPR) * S::KROW + (c % CPR) * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < VPT; ++i)
+    vdst[i] = (uint32_t)((8 * (8 * i + (lane >> 3))) * S::VROW + 4 * (8 * w4 + (lane & 7)));
+  auto stage = [&](Regs& R, int it, int buf) {
     uint8_t* lk = lds_k[half][buf];
     uint8_t* lv = lds_v[half][buf];
     const int key0 = it * kKeysPerIter + 16 * w4;
-    const u32x4_t z = {0u, 0u, 0u, 0u};
+    if (key0 + 16 > kend) {
+      // the block crosses the tile's last visible key: zero what lies past it
+      const u32x4_t z = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int c = i * kWave + lane;
-      const int kb = c / CPR, dc = c % CPR;
-      // keys past the tile's last query are never visible: store zeros
-      *reinterpret_cast<u32x4_t*>(lk + (16 * w4 + kb) * S::KROW + dc * 16) =
-          key0 + kb < kend ? R.k[i] : z;
+      for (int i = 0; i < KPT; ++i)
+        R.k[i] = key0 + (i * kWave + lane) / CPR < kend ? R.k[i] : z;
+      const bool ok0 = key0 + 2 * (lane & 7) < kend, ok1 = key0 + 2 * (lane & 7) + 1 < kend;
+#pragma unroll
+      for (int i = 0; i < VPT; ++i) {
+        R.v[i][0] = ok0 ? R.v[i][0] : z;
+        R.v[i][1] = ok1 ? R.v[i][1] : z;
+      }
     }
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int kp = 8 * w4 + (lane & 7), dc = 8 * i + (lane >> 3);
-      const bool ok0 = key0 + 2 * (lane & 7) < kend, ok1 = key0 + 2 * (lane & 7) + 1 < kend;
+    for (int i = 0; i < KPT; ++i) *reinterpret_cast<u32x4_t*>(lk + kdst[i]) = R.k[i];
+#pragma unroll
+    for (int i = 0; i < VPT; ++i)
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         // dims 8dc + 2w (lo) and 8dc + 2w + 1 (hi), keys 2kp and 2kp + 1
-        const uint32_t v0 = ok0 ? R.v[i][0][w] : 0u, v1 = ok1 ? R.v[i][1][w] : 0u;
-        *reinterpret_cast<uint32_t*>(lv + (8 * dc + 2 * w) * S::VROW + 4 * kp) = pair_lo(v0, v1);
-        *reinterpret_cast<uint32_t*>(lv + (8 * dc + 2 * w + 1) * S::VROW + 4 * kp) =
-            pair_hi(v0, v1);
+        *reinterpret_cast<uint32_t*>(lv + vdst[i] + (2 * w) * S::VROW) =
+            pair_lo(R.v[i][0][w], R.v[i][1][w]);
+        *reinterpret_cast<uint32_t*>(lv + vdst[i] + (2 * w + 1) * S::VROW) =
+            pair_hi(R.v[i][0][w], R.v[i][1][w]);
       }
-    }
   };
 
   f32x4_t acc[S::NMT];
@@ -246,20 +266,19 @@ __global__ __launch_bounds__(512) void prefill_tile_kernel(PrefillArgs a) {
         st[tt] = mfma16x16x32<E>(ka, qf[s], st[tt]);
       }
     }
-    // ---- scale to log2 units and apply the causal mask on diagonal tiles
+    // ---- causal mask on diagonal tiles; scores stay unscaled (the scale,
+    // with log2(e) folded in, is applied inside the exponent below)
     const int key0 = it * kKeysPerIter;
-    float x[4][4];
-    const bool diag = key0 + kKeysPerIter - 1 > nc + sub_start;
+    float (&x)[4][4] = *reinterpret_cast<float (*)[4][4]>(&st[0]);
+    if (key0 + kKeysPerIter - 1 > nc + sub_start) {
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
+      for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x[tt][i] = st[tt][i] * a.scale_log2;
-        if (diag) {
+        for (int i = 0; i < 4; ++i) {
           const int key = key0 + 16 * tt + 4 * g + i;
           x[tt][i] = key <= pos ? x[tt][i] : -INFINITY;
         }
-      }
+    }
     float mx = x[0][0];
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt)
@@ -267,6 +286,7 @@ __global__ __launch_bounds__(512) void prefill_tile_kernel(PrefillArgs a) {
       for (int i = 0; i < 4; ++i) mx = fmaxf(mx, x[tt][i]);
     mx = fmaxf(mx, shfl_xor(mx, 16));
     mx = fmaxf(mx, shfl_xor(mx, 32));
+    mx *= a.scale_log2;  // scale > 0: max of scaled = scaled max
     const float mn = fmaxf(m, mx);
     const bool grow = mn > m + 8.f;
     if (__any(grow)) {
@@ -283,7 +303,7 @@ __global__ __launch_bounds__(512) void prefill_tile_kernel(PrefillArgs a) {
     for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        p[tt][i] = __builtin_amdgcn_exp2f(x[tt][i] - ms);
+        p[tt][i] = __builtin_amdgcn_exp2f(fmaf(x[tt][i], a.scale_log2, -ms));
         lsum += p[tt][i];
       }
     // ---- O^T += V^T P^T, 32 keys per MFMA: lane group g holds keys
@@ -317,7 +337,7 @@ __global__ __launch_bounds__(512) void prefill_tile_kernel(PrefillArgs a) {
   fetch(R1, block_id(it_begin + 1));
   int id_ahead = block_id(it_begin + 2);
   __syncthreads();
-  auto trip = [&](int t, Regs& Rload, const Regs& Rstage) {
+  auto trip = [&](int t, Regs& Rload, Regs& Rstage) {
     const int buf = t & 1;
     const int it = it_begin + t;
     fetch(Rload, id_ahead);  // unconditional: past the range it reads block 0, never staged
