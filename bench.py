@@ -39,6 +39,9 @@ WORKLOADS = {
     "prefix": "prefix_shared_decode_bf16",
     "long": "long_context_decode_bf16",
     "chunk": "prefill_chunk_bf16",
+    "prefill2k": "prefill_chunk_2048_bf16",
+    "prefill8k": "prefill_8192_bf16",
+    "prefillbatch": "prefill_batch_4x1024_bf16",
 }
 
 DESCR = {
@@ -50,6 +53,9 @@ DESCR = {
                                  "(64 blocks) + private suffix U[64,512]",
     "long_context_decode_bf16": "Llama-3-8B layer decode, 16 requests at 32768 tokens, pool 36000 blocks",
     "prefill_chunk_bf16": "Llama-3-8B layer prefill chunk alone: 512 new tokens on 1024 cached",
+    "prefill_chunk_2048_bf16": "Llama-3-8B layer prefill: 2048 new tokens on 2048 cached",
+    "prefill_8192_bf16": "Llama-3-8B layer prefill: fresh 8192-token prompt",
+    "prefill_batch_4x1024_bf16": "Llama-3-8B layer prefill: 4 requests x ~1024-token chunks",
 }
 
 
@@ -314,7 +320,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     rot = 4
     names = [args.only] if args.only else ["decode", "mixed", "chunk"] + (
-        ["prefix", "long"] if args.extra else [])
+        ["prefix", "long", "prefill2k", "prefill8k", "prefillbatch"] if args.extra else [])
     results = {k: measure(WORKLOADS[k], args, rot if k != "long" else 2) for k in names}
 
     head = results.get("decode") or next(iter(results.values()))
@@ -376,6 +382,17 @@ def main():
             "mfma_util": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
             "tokens_per_s": round(cw.num_tokens / (ch["ms_step"] * 1e-3), 1),
         }
+    for key in ("prefill2k", "prefill8k", "prefillbatch"):
+        if key in results:
+            r = results[key]
+            rw, rc = r["w"], r["counts"]
+            tf = rc["chunk_flops"] / (r["attn_ms_avg"] * 1e-3) / 1e12
+            line[key] = {
+                "workload": rw.name, "attention_avg_us": round(r["attn_ms_avg"] * 1e3, 2),
+                "gflop": round(rc["chunk_flops"] / 1e9, 2), "tflops": round(tf, 1),
+                "mfma_util": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                "tokens_per_s": round(rw.num_tokens / (r["ms_step"] * 1e-3), 1),
+            }
     for key in ("prefix", "long"):
         if key in results:
             r = results[key]

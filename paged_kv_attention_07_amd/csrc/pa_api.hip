@@ -228,6 +228,7 @@ int pa_attention_mixed(void* out, const void* q, const void* kv_cache, int64_t n
     p.num_kv_heads = num_kv_heads;
     p.num_q_heads = num_q_heads;
     p.max_tiles = (int)(ceil_div(num_tokens, pa::kQueriesPerTile) + num_seqs);
+    p.max_query_len = max_query_len;
     p.scale_log2 = a.scale_log2;
     const hipError_t e = pa::launch_prefill(p, dtype, head_dim, group, s);
     if (e != hipSuccess) return PA_ERR_HIP;

@@ -43,10 +43,11 @@ struct PrefillArgs {
   int32_t num_kv_heads;
   int32_t num_q_heads;
   int32_t max_tiles;          // upper bound on the tile count (grid size)
+  int32_t max_query_len;      // (host) longest chunk: picks the tile shape
   float scale_log2;
 };
 
-constexpr int kQueriesPerTile = 16;  // query tokens per prefill tile
+constexpr int kQueriesPerTile = 16;  // fewest query tokens per prefill tile (grid bound)
 
 hipError_t launch_slot_mapping(int64_t* slot_mapping, const int32_t* block_table,
                                int32_t bt_stride, const int32_t* qsl,

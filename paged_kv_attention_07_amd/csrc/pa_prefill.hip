@@ -7,11 +7,16 @@
 // inside the chunk).  Keys are read through the request's block table; the
 // new tokens' K/V were scattered into the cache beforehand.
 //
-// Tiling.  A work-group (4 wavefronts) owns one tile of query tokens of one
-// request and one group of query heads sharing a KV head: for GQA group 4 the
-// 4 waves are the 4 query heads of a KV head over the same 16 tokens, so each
-// K/V tile staged in LDS feeds 4 heads.  Keys are processed 64 at a time
-// (four 16-token blocks looked up in the block table).
+// Tiling.  A work-group owns one tile of query tokens of one request and one
+// group of query heads sharing a KV head.  Its waves form KSPLIT key parts of
+// 4 waves; within a part, for GQA group 4, the 4 waves are the 4 query heads
+// of the KV head over the same tokens, so each K/V tile staged in LDS feeds 4
+// heads.  A wave covers NT sub-tiles of 16 tokens: with NT = 2 every K and V
+// fragment read from LDS feeds two matrix-core products.  Keys are processed
+// 64 at a time (four 16-token blocks looked up in the block table), staged in
+// double-buffered LDS with global loads two iterations ahead.  With KSPLIT = 2
+// the parts split the tile's key range and are merged through LDS at the end
+// (more waves for chunks too short to fill the chip).
 //
 // Matrix-core mapping (v_mfma_f32_16x16x32_{bf16,f16}).  Scores are formed
 // transposed, S^T = K Q^T (keys x tokens), because the accumulator layout of
@@ -23,6 +28,7 @@
 // keys per 32-bit word) while it is staged.  The contraction order inside an
 // MFMA is a permutation of the keys; A and B use the same permutation.
 #include <math.h>
+#include <stdlib.h>
 
 #include "pa_common.h"
 #include "pa_kernels.h"
@@ -49,38 +55,38 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 
 constexpr int kKeysPerIter = 64;  // keys staged per iteration (4 paged blocks)
 
-
 template <int D>
 struct TileShape {
-  static constexpr int ROWB = D * 2;              // bytes of one token's head row
-  static constexpr int KROW = ROWB + 16;          // padded LDS row of K
+  static constexpr int ROWB = D * 2;                 // bytes of one token's head row
+  static constexpr int KROW = ROWB + 16;             // padded LDS row of K
   static constexpr int VROW = kKeysPerIter * 2 + 8;  // padded LDS row of V^T
-  static constexpr int NKS = D / 32;              // MFMA k-steps of Q K^T
-  static constexpr int NMT = D / 16;              // 16-dim tiles of the output
+  static constexpr int NKS = D / 32;                 // MFMA k-steps of Q K^T
+  static constexpr int NMT = D / 16;                 // 16-dim tiles of the output
+  static constexpr int KBUF = kKeysPerIter * KROW;
+  static constexpr int VBUF = D * VROW;
+  static constexpr int STAGE = KBUF + VBUF;          // one LDS stage: K then V^T
 };
 
-// One work-group = 8 waves = 2 key halves x 4 waves; the 4 waves of a half
-// are WPW query heads x (4 / WPW) token sub-tiles of 16.  The two halves
-// split the tile's key range (iterations [0, n0) and [n0, n)), each with its
-// own double-buffered LDS stages, and are merged through LDS at the end.
-template <typename E, int D, int WPW>
-__global__ __launch_bounds__(512) void prefill_tile_kernel(PrefillArgs a) {
+// Tokens per tile for a launch configuration.
+template <int WPW, int NT>
+constexpr int tile_tokens() {
+  return 16 * NT * (4 / WPW);
+}
+
+template <typename E, int D, int WPW, int NT, int KSPLIT>
+__global__ __launch_bounds__(256 * KSPLIT) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_tile_kernel(PrefillArgs a) {
   using S = TileShape<D>;
-  constexpr int NQS = 4 / WPW;       // 16-token sub-tiles per work-group
-  constexpr int QT = 16 * NQS;       // tokens per tile
-  constexpr int KBUF = kKeysPerIter * S::KROW;
-  constexpr int VBUF = D * S::VROW;
-  // [half][stage]: the next 64 keys of each half are staged while the
+  constexpr int QT = tile_tokens<WPW, NT>();   // tokens per tile
+  // [part][stage]: the next 64 keys of each part are staged while the
   // current ones are used
-  __shared__ __attribute__((aligned(16))) uint8_t lds_k[2][2][KBUF];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_v[2][2][VBUF];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[KSPLIT][2][S::STAGE];
   __shared__ int s_tile[2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = uniform(tid >> 6);
-  const int half = wave >> 2;                // key half
-  const int w4 = wave & 3;                   // wave within the half
+  const int part = wave >> 2;                  // key part
+  const int w4 = wave & 3;                     // wave within the part
   const int group = a.num_q_heads / a.num_kv_heads;
   const int hg = group / WPW;
   const int h = blockIdx.y / hg;
@@ -103,7 +109,9 @@ __global__ __launch_bounds__(512) void prefill_tile_kernel(PrefillArgs a) {
       if (hit) {
         const int src = __builtin_ctzll(hit);
         found_r = base + src;
-        found_t = want - readlane(excl, src);
+        // a request's tiles are handed out last-first: the tiles with the
+        // most keys start early and the short ones fill in behind them
+        found_t = readlane(incl, src) - 1 - want;
       }
       running = readlane(incl, kWave - 1);
     }
@@ -125,30 +133,32 @@ __global__ __launch_bounds__(512) void prefill_tile_kernel(PrefillArgs a) {
   const int tile_valid = min(QT, qlen - tile_start);
   const int kend = min(L, nc + tile_start + tile_valid);  // keys this tile needs
   const int niter = (kend + kKeysPerIter - 1) / kKeysPerIter;
-  const int n0 = (niter + 1) / 2;            // iterations of half 0
-  const int it_begin = half ? n0 : 0;
-  const int my_iters = half ? niter - n0 : n0;  // n0 or n0 - 1 (or 0)
+  const int n0 = (niter + KSPLIT - 1) / KSPLIT;           // trips of every part
+  const int it_begin = part * n0;
+  const int my_iters = max(0, min(n0, niter - it_begin));
 
-  const int hw = w4 % WPW;                   // head within the group
-  const int sub = w4 / WPW;                  // 16-token sub-tile
+  const int hw = w4 % WPW;                     // head within the group
+  const int sub = w4 / WPW;                    // token group of this wave
   const int hq = h * group + hs * WPW + hw;
-  const int n = lane & 15;                   // token column of this lane
-  const int g = lane >> 4;                   // lane group
-  const int sub_start = tile_start + sub * 16;
-  const int sub_valid = max(0, min(16, qlen - sub_start));
-  const int my_tok = min(n, max(sub_valid - 1, 0));
-  const int pos = nc + sub_start + my_tok;   // this column's last visible key
+  const int n = lane & 15;                     // token column of this lane
+  const int g = lane >> 4;                     // lane group
 
-  // Q^T fragments: token n, dims 32s + 8g .. +8
-  u32x4_t qf[S::NKS];
-  {
-    const bool ok = n < sub_valid;
+  // NT sub-tiles of 16 tokens: sub-tile j starts at token sub_start[j]
+  int sub_start[NT], sub_valid[NT], pos[NT];
+  u32x4_t qf[NT][S::NKS];                      // Q^T fragments: token n, dims 32s + 8g .. +8
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    sub_start[j] = tile_start + (sub * NT + j) * 16;
+    sub_valid[j] = max(0, min(16, qlen - sub_start[j]));
+    pos[j] = nc + sub_start[j] + min(n, max(sub_valid[j] - 1, 0));  // last visible key
+    const bool ok = n < sub_valid[j];
     const uint8_t* qp = static_cast<const uint8_t*>(a.q) +
-                        ((int64_t)(q0 + sub_start + n) * a.num_q_heads + hq) * S::ROWB + g * 16;
+                        ((int64_t)(q0 + sub_start[j] + n) * a.num_q_heads + hq) * S::ROWB +
+                        g * 16;
 #pragma unroll
     for (int s = 0; s < S::NKS; ++s) {
-      u32x4_t z = {0u, 0u, 0u, 0u};
-      qf[s] = ok ? load16(qp + s * 64) : z;
+      const u32x4_t z = {0u, 0u, 0u, 0u};
+      qf[j][s] = ok ? load16(qp + s * 64) : z;
     }
   }
 
@@ -165,22 +175,18 @@ __global__ __launch_bounds__(512) void prefill_tile_kernel(PrefillArgs a) {
     return lb < nb_need ? load_scalar(bt + lb) : 0;
   };
 
-  // Staging: wavefront w4 of a half moves paged block w4 of the half's
+  // Staging: wavefront w4 of a part moves paged block w4 of the part's
   // iteration (keys 16 w4 .. 16 w4 + 15), so its block id is wave-uniform.
   // K rows go to LDS unchanged (lane l, step i: key (64 i + l) / CPR, 16-byte
   // column l % CPR).  V goes in transposed, two keys per 32-bit word: lane l,
   // step i handles key pair l % 8 and 8-dim column 8 i + l / 8, so the lanes
   // of one store write consecutive words.
-  constexpr int CPR = S::ROWB / 16;          // 16-byte columns per row
-  constexpr int KPT = 16 * CPR / kWave;      // K pieces per lane per block
-  constexpr int VPT = (D / 8) / 8;           // V column groups per lane per block
+  constexpr int CPR = S::ROWB / 16;            // 16-byte columns per row
+  constexpr int KPT = 16 * CPR / kWave;        // K pieces per lane per block
+  constexpr int VPT = (D / 8) / 8;             // V column groups per lane per block
   struct Regs {
     u32x4_t k[KPT], v[VPT][2];
   };
-  // Loads are issued unconditionally (every address stays inside a real
-  // block: ids past the table's end read block 0, rows past kend read their
-  // own block) and keys past kend are zeroed when staged, so the compiler can
-  // wait for exactly the loads a stage needs.
   // Per-lane byte offsets inside a block (32-bit): with the block base
   // wave-uniform, every load is scalar base + vector offset.
   uint32_t koff[KPT], voff[VPT][2];
@@ -195,6 +201,10 @@ __global__ __launch_bounds__(512) void prefill_tile_kernel(PrefillArgs a) {
     for (int e = 0; e < 2; ++e)
       voff[i][e] = (uint32_t)(half_stride + (2 * (lane & 7) + e) * tok_stride +
                               (8 * i + (lane >> 3)) * 16);
+  // Loads are issued unconditionally (every address stays inside a real
+  // block: ids past the table's end read block 0, rows past kend read their
+  // own block) and keys past kend are zeroed when staged, so the compiler can
+  // wait for exactly the loads a stage needs.
   auto fetch = [&](Regs& R, int phys) {
     const uint8_t* blk = kvh + (int64_t)phys * blk_stride;
 #pragma unroll
@@ -213,10 +223,10 @@ __global__ __launch_bounds__(512) void prefill_tile_kernel(PrefillArgs a) {
   }
 #pragma unroll
   for (int i = 0; i < VPT; ++i)
-    vdst[i] = (uint32_t)((8 * (8 * i + (lane >> 3))) * S::VROW + 4 * (8 * w4 + (lane & 7)));
+    vdst[i] = (uint32_t)(S::KBUF + (8 * (8 * i + (lane >> 3))) * S::VROW +
+                         4 * (8 * w4 + (lane & 7)));
   auto stage = [&](Regs& R, int it, int buf) {
-    uint8_t* lk = lds_k[half][buf];
-    uint8_t* lv = lds_v[half][buf];
+    uint8_t* st = lds[part][buf];
     const int key0 = it * kKeysPerIter + 16 * w4;
     if (key0 + 16 > kend) {
       // the block crosses the tile's last visible key: zero what lies past it
@@ -232,101 +242,114 @@ __global__ __launch_bounds__(512) void prefill_tile_kernel(PrefillArgs a) {
       }
     }
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) *reinterpret_cast<u32x4_t*>(lk + kdst[i]) = R.k[i];
+    for (int i = 0; i < KPT; ++i) *reinterpret_cast<u32x4_t*>(st + kdst[i]) = R.k[i];
 #pragma unroll
     for (int i = 0; i < VPT; ++i)
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         // dims 8dc + 2w (lo) and 8dc + 2w + 1 (hi), keys 2kp and 2kp + 1
-        *reinterpret_cast<uint32_t*>(lv + vdst[i] + (2 * w) * S::VROW) =
+        *reinterpret_cast<uint32_t*>(st + vdst[i] + (2 * w) * S::VROW) =
             pair_lo(R.v[i][0][w], R.v[i][1][w]);
-        *reinterpret_cast<uint32_t*>(lv + vdst[i] + (2 * w + 1) * S::VROW) =
+        *reinterpret_cast<uint32_t*>(st + vdst[i] + (2 * w + 1) * S::VROW) =
             pair_hi(R.v[i][0][w], R.v[i][1][w]);
       }
   };
 
-  f32x4_t acc[S::NMT];
+  f32x4_t acc[NT][S::NMT];
+  float m[NT], lsum[NT];
 #pragma unroll
-  for (int mt = 0; mt < S::NMT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, lsum = 0.f;
+  for (int j = 0; j < NT; ++j) {
+    m[j] = -INFINITY;
+    lsum[j] = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < S::NMT; ++mt) acc[j][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
 
   // One 64-key iteration from LDS stage `buf`: S^T, online softmax, O^T.
   auto compute = [&](int it, int buf) {
-    const uint8_t* lds_kc = lds_k[half][buf];
-    const uint8_t* lds_vc = lds_v[half][buf];
-    // ---- S^T for 64 keys x 16 tokens: 4 tiles of 16 keys
-    f32x4_t st[4];
+    const uint8_t* lds_kc = lds[part][buf];
+    const uint8_t* lds_vc = lds[part][buf] + S::KBUF;
+    // ---- S^T for 64 keys x 16 tokens per sub-tile: 4 tiles of 16 keys
+    f32x4_t st[NT][4];
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
-      st[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < NT; ++j) st[j][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < S::NKS; ++s) {
         const u32x4_t ka = *reinterpret_cast<const u32x4_t*>(
             lds_kc + (16 * tt + n) * S::KROW + s * 64 + g * 16);
-        st[tt] = mfma16x16x32<E>(ka, qf[s], st[tt]);
+#pragma unroll
+        for (int j = 0; j < NT; ++j) st[j][tt] = mfma16x16x32<E>(ka, qf[j][s], st[j][tt]);
       }
     }
-    // ---- causal mask on diagonal tiles; scores stay unscaled (the scale,
-    // with log2(e) folded in, is applied inside the exponent below)
     const int key0 = it * kKeysPerIter;
-    float (&x)[4][4] = *reinterpret_cast<float (*)[4][4]>(&st[0]);
-    if (key0 + kKeysPerIter - 1 > nc + sub_start) {
+    u32x4_t pb[NT][2];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      // ---- causal mask on diagonal tiles; scores stay unscaled (the scale,
+      // with log2(e) folded in, is applied inside the exponent below)
+      float (&x)[4][4] = *reinterpret_cast<float (*)[4][4]>(&st[j][0]);
+      if (key0 + kKeysPerIter - 1 > nc + sub_start[j]) {
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = key0 + 16 * tt + 4 * g + i;
+            x[tt][i] = key <= pos[j] ? x[tt][i] : -INFINITY;
+          }
+      }
+      float mx = x[0][0];
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, x[tt][i]);
+      mx = fmaxf(mx, shfl_xor(mx, 16));
+      mx = fmaxf(mx, shfl_xor(mx, 32));
+      mx *= a.scale_log2;  // scale > 0: max of scaled = scaled max
+      const float mn = fmaxf(m[j], mx);
+      const bool grow = mn > m[j] + 8.f;
+      if (__any(grow)) {
+        const float mu = grow ? mn : m[j];
+        const float alpha = (mu == m[j]) ? 1.f : __builtin_amdgcn_exp2f(m[j] - mu);
+        lsum[j] *= alpha;
+#pragma unroll
+        for (int mt = 0; mt < S::NMT; ++mt) acc[j][mt] *= alpha;
+        m[j] = mu;
+      }
+      const float ms = (m[j] == -INFINITY) ? 0.f : m[j];
+      float p[4][4];
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int key = key0 + 16 * tt + 4 * g + i;
-          x[tt][i] = key <= pos ? x[tt][i] : -INFINITY;
+          p[tt][i] = __builtin_amdgcn_exp2f(fmaf(x[tt][i], a.scale_log2, -ms));
+          lsum[j] += p[tt][i];
         }
-    }
-    float mx = x[0][0];
+      // lane group g holds keys 32s2 + 4g + (0..3) and 32s2 + 16 + 4g + (0..3)
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, x[tt][i]);
-    mx = fmaxf(mx, shfl_xor(mx, 16));
-    mx = fmaxf(mx, shfl_xor(mx, 32));
-    mx *= a.scale_log2;  // scale > 0: max of scaled = scaled max
-    const float mn = fmaxf(m, mx);
-    const bool grow = mn > m + 8.f;
-    if (__any(grow)) {
-      const float mu = grow ? mn : m;
-      const float alpha = (mu == m) ? 1.f : __builtin_amdgcn_exp2f(m - mu);
-      lsum *= alpha;
-#pragma unroll
-      for (int mt = 0; mt < S::NMT; ++mt) acc[mt] *= alpha;
-      m = mu;
-    }
-    const float ms = (m == -INFINITY) ? 0.f : m;
-    float p[4][4];
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[tt][i] = __builtin_amdgcn_exp2f(fmaf(x[tt][i], a.scale_log2, -ms));
-        lsum += p[tt][i];
+      for (int s2 = 0; s2 < 2; ++s2) {
+        pb[j][s2][0] = pack2<E>(p[2 * s2][0], p[2 * s2][1]);
+        pb[j][s2][1] = pack2<E>(p[2 * s2][2], p[2 * s2][3]);
+        pb[j][s2][2] = pack2<E>(p[2 * s2 + 1][0], p[2 * s2 + 1][1]);
+        pb[j][s2][3] = pack2<E>(p[2 * s2 + 1][2], p[2 * s2 + 1][3]);
       }
-    // ---- O^T += V^T P^T, 32 keys per MFMA: lane group g holds keys
-    // 32s2 + 4g + (0..3) and 32s2 + 16 + 4g + (0..3)
+    }
+    // ---- O^T += V^T P^T, 32 keys per MFMA
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      u32x4_t pb;
-      pb[0] = pack2<E>(p[2 * s2][0], p[2 * s2][1]);
-      pb[1] = pack2<E>(p[2 * s2][2], p[2 * s2][3]);
-      pb[2] = pack2<E>(p[2 * s2 + 1][0], p[2 * s2 + 1][1]);
-      pb[3] = pack2<E>(p[2 * s2 + 1][2], p[2 * s2 + 1][3]);
+    for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
       for (int mt = 0; mt < S::NMT; ++mt) {
         const uint8_t* vp = lds_vc + (16 * mt + n) * S::VROW + (32 * s2 + 4 * g) * 2;
         const uint2 lo = *reinterpret_cast<const uint2*>(vp);
         const uint2 hi = *reinterpret_cast<const uint2*>(vp + 32);
-        u32x4_t va = {lo.x, lo.y, hi.x, hi.y};
-        acc[mt] = mfma16x16x32<E>(va, pb, acc[mt]);
+        const u32x4_t va = {lo.x, lo.y, hi.x, hi.y};
+#pragma unroll
+        for (int j = 0; j < NT; ++j) acc[j][mt] = mfma16x16x32<E>(va, pb[j][s2], acc[j][mt]);
       }
-    }
   };
 
-  // Both halves run n0 loop trips in lockstep (one barrier per trip); a half
+  // Every part runs n0 loop trips in lockstep (one barrier per trip); a part
   // with fewer iterations idles on its last trip.  Trip t computes iteration
   // it_begin + t from LDS stage t & 1, issues the loads of iteration
   // it_begin + t + 2 into register set t & 1, and stages iteration
@@ -351,57 +374,91 @@ __global__ __launch_bounds__(512) void prefill_tile_kernel(PrefillArgs a) {
     if (t + 1 < n0) trip(t + 1, R1, R0);
   }
 
-  // ---- merge the halves: half 1 leaves (max, row sum, O^T) in LDS
-  lsum += shfl_xor(lsum, 16);
-  lsum += shfl_xor(lsum, 32);
-  constexpr int NF = S::NMT * 4 + 2;         // floats per lane
-  static_assert(4 * kWave * NF * 4 <= 2 * KBUF, "merge buffer must fit in half 1's K stages");
-  float* xch = reinterpret_cast<float*>(&lds_k[1][0][0]);  // half 1's stages, now free
-  if (half == 1) {
-    float* dst = xch + (w4 * kWave + lane) * NF;
 #pragma unroll
-    for (int mt = 0; mt < S::NMT; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) dst[4 * mt + i] = acc[mt][i];
-    dst[NF - 2] = m;
-    dst[NF - 1] = lsum;
+  for (int j = 0; j < NT; ++j) {
+    lsum[j] += shfl_xor(lsum[j], 16);
+    lsum[j] += shfl_xor(lsum[j], 32);
   }
-  __syncthreads();
-  if (half == 1) return;
-  {
-    const float* src = xch + (w4 * kWave + lane) * NF;
-    const float m1 = src[NF - 2], l1 = src[NF - 1];
-    const float M = fmaxf(m, m1);            // m is finite: key 0 is visible
-    const float a0 = __builtin_amdgcn_exp2f(m - M);
-    const float a1 = (m1 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m1 - M);
-    lsum = lsum * a0 + l1 * a1;
+  if constexpr (KSPLIT == 2) {
+    // ---- merge the parts: part 1 leaves (max, row sum, O^T) in its LDS stages
+    constexpr int NF = NT * (S::NMT * 4 + 2);  // floats per lane
+    static_assert(4 * kWave * NF * 4 <= 2 * S::STAGE, "merge buffer must fit in part 1's stages");
+    float* xch = reinterpret_cast<float*>(&lds[1][0][0]) + (w4 * kWave + lane) * NF;
+    if (part == 1) {
 #pragma unroll
-    for (int mt = 0; mt < S::NMT; ++mt)
+      for (int j = 0; j < NT; ++j) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[mt][i] = acc[mt][i] * a0 + src[4 * mt + i] * a1;
+        for (int mt = 0; mt < S::NMT; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) xch[j * (S::NMT * 4 + 2) + 4 * mt + i] = acc[j][mt][i];
+        xch[j * (S::NMT * 4 + 2) + S::NMT * 4] = m[j];
+        xch[j * (S::NMT * 4 + 2) + S::NMT * 4 + 1] = lsum[j];
+      }
+    }
+    __syncthreads();
+    if (part == 1) return;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const float* src = xch + j * (S::NMT * 4 + 2);
+      const float m1 = src[S::NMT * 4], l1 = src[S::NMT * 4 + 1];
+      const float M = fmaxf(m[j], m1);         // m is finite: key 0 is visible
+      const float a0 = __builtin_amdgcn_exp2f(m[j] - M);
+      const float a1 = (m1 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m1 - M);
+      lsum[j] = lsum[j] * a0 + l1 * a1;
+#pragma unroll
+      for (int mt = 0; mt < S::NMT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[j][mt][i] = acc[j][mt][i] * a0 + src[4 * mt + i] * a1;
+    }
   }
 
   // ---- normalise and store: lane holds dims 16mt + 4g + (0..3) of token n
-  if (n < sub_valid) {
-    const float inv = 1.f / lsum;
-    uint8_t* op = static_cast<uint8_t*>(a.out) +
-                  ((int64_t)(q0 + sub_start + n) * a.num_q_heads + hq) * S::ROWB + g * 8;
 #pragma unroll
-    for (int mt = 0; mt < S::NMT; ++mt) {
-      uint2 w;
-      w.x = pack2<E>(acc[mt][0] * inv, acc[mt][1] * inv);
-      w.y = pack2<E>(acc[mt][2] * inv, acc[mt][3] * inv);
-      *reinterpret_cast<uint2*>(op + mt * 32) = w;
+  for (int j = 0; j < NT; ++j) {
+    if (n < sub_valid[j]) {
+      const float inv = 1.f / lsum[j];
+      uint8_t* op = static_cast<uint8_t*>(a.out) +
+                    ((int64_t)(q0 + sub_start[j] + n) * a.num_q_heads + hq) * S::ROWB + g * 8;
+#pragma unroll
+      for (int mt = 0; mt < S::NMT; ++mt) {
+        uint2 w;
+        w.x = pack2<E>(acc[j][mt][0] * inv, acc[j][mt][1] * inv);
+        w.y = pack2<E>(acc[j][mt][2] * inv, acc[j][mt][3] * inv);
+        *reinterpret_cast<uint2*>(op + mt * 32) = w;
+      }
     }
   }
 }
 
+// Tile shape of a launch: NT = 2 (32 tokens per wave, one key part) for long
+// chunks, NT = 1 with two key parts for short ones, which would leave most of
+// the chip idle otherwise.  PA_PREFILL_TOKENS_PER_WAVE=16|32 overrides the
+// choice (a tuning and testing knob).
+int choose_nt(const PrefillArgs& a) {
+  if (const char* env = getenv("PA_PREFILL_TOKENS_PER_WAVE")) {
+    const int v = atoi(env);
+    if (v == 16) return 1;
+    if (v == 32) return 2;
+  }
+  return a.max_query_len >= 1024 ? 2 : 1;
+}
+
+template <typename E, int D, int WPW, int NT, int KSPLIT>
+hipError_t launch_shape(const PrefillArgs& a, hipStream_t stream) {
+  const int group = a.num_q_heads / a.num_kv_heads;
+  // max_tiles bounds the tile count for 16-token tiles; scale it to this shape
+  constexpr int QT = tile_tokens<WPW, NT>();
+  const int tiles = ((a.max_tiles - a.num_seqs) * kQueriesPerTile + QT - 1) / QT + a.num_seqs;
+  const dim3 grid((unsigned)tiles, (unsigned)(a.num_kv_heads * (group / WPW)));
+  hipLaunchKernelGGL((prefill_tile_kernel<E, D, WPW, NT, KSPLIT>), grid, dim3(256 * KSPLIT), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
 template <typename E, int D, int WPW>
 hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream) {
-  const int group = a.num_q_heads / a.num_kv_heads;
-  const dim3 grid((unsigned)a.max_tiles, (unsigned)(a.num_kv_heads * (group / WPW)));
-  hipLaunchKernelGGL((prefill_tile_kernel<E, D, WPW>), grid, dim3(512), 0, stream, a);
-  return hipGetLastError();
+  return choose_nt(a) == 2 ? launch_shape<E, D, WPW, 2, 1>(a, stream)
+                           : launch_shape<E, D, WPW, 1, 2>(a, stream);
 }
 
 template <typename E, int D>

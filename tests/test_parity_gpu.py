@@ -278,3 +278,67 @@ def test_workspace_reused_across_calls():
                                             num_splits=splits)
             _, _, ref = gu.oracle_step(w, pool)
             gu.check_close(w, gu.from_device(out, w.dtype), ref, what=f"{w.name}/{splits}")
+
+
+# --------------------------------------------------------------------------
+# long prefill chunks (sampled rows) and both prefill tile shapes
+# --------------------------------------------------------------------------
+
+
+def sampled_rows_check(w, dev_out_bits, rows):
+    """Compare selected query rows with the oracle, each row computed as its
+    own one-token request at its absolute position (same table, same pool)."""
+    import dataclasses
+    qsl = w.query_start_loc
+    req_of = np.searchsorted(qsl, np.asarray(rows), side="right") - 1
+    nc = np.array([w.num_computed[r] + (t - qsl[r]) for t, r in zip(rows, req_of)], np.int32)
+    sub = dataclasses.replace(
+        w, q=w.q[rows], seq_lens=(nc + 1).astype(np.int32), num_computed=nc,
+        query_start_loc=np.arange(len(rows) + 1, dtype=np.int32),
+        block_table=w.block_table[req_of])
+    return sub
+
+
+def _large_prefill_check(name, tokens_per_wave, monkeypatch):
+    import dataclasses
+    monkeypatch.setenv("PA_PREFILL_TOKENS_PER_WAVE", str(tokens_per_wave))
+    w = workload(name)
+    pool = gu.poisoned_pool(w)
+    dev = gu.Device(w, pool)
+    slots = dev.slot_mapping()
+    dev.scatter(slots)
+    out = gu.from_device(dev.attend(force_mixed=True), w.dtype)
+    g_pool = gu.from_device(dev.kv, w.dtype)
+    r_slots = oracle.slot_mapping(w.block_table, w.query_start_loc, w.num_computed, 16)
+    assert np.array_equal(slots.cpu().numpy(), r_slots)
+    r_pool = oracle.reshape_and_cache(pool, w.k_new, w.v_new, r_slots)
+    assert np.array_equal(gu.bits(g_pool), gu.bits(r_pool))
+    rng = np.random.default_rng(17)
+    T = w.num_tokens
+    edge = [0, 1, 15, 16, 31, 32, 63, 64, T - 1, T - 2, T - 17]
+    rows = np.unique(np.concatenate([edge, rng.choice(T, 53, replace=False)]))
+    sub = sampled_rows_check(w, out, rows)
+    ref = oracle.paged_attention(sub.q, r_pool, sub.block_table, sub.seq_lens,
+                                 sub.query_start_loc, sub.num_computed, w.scale, w.dtype)
+    gu.check_close(w, out[rows], ref, what=f"{name}/{tokens_per_wave}")
+
+
+@pytest.mark.parametrize("tokens_per_wave", [16, 32])
+@pytest.mark.parametrize("name", ["prefill_chunk_2048_bf16", "prefill_batch_4x1024_bf16"])
+def test_large_prefill_sampled(name, tokens_per_wave, monkeypatch):
+    _large_prefill_check(name, tokens_per_wave, monkeypatch)
+
+
+def test_prefill_8k_sampled(monkeypatch):
+    _large_prefill_check("prefill_8192_bf16", 32, monkeypatch)
+
+
+@pytest.mark.parametrize("tokens_per_wave", [16, 32])
+def test_mixed_both_tile_shapes(tokens_per_wave, monkeypatch):
+    """Both prefill tile shapes on the small mixed batch and on odd groupings."""
+    monkeypatch.setenv("PA_PREFILL_TOKENS_PER_WAVE", str(tokens_per_wave))
+    full_check(workload("mixed_bf16_small"))
+    lens = [40, 17, 300, 5, 64, 129, 1, 700]
+    q_lens = [40, 2, 33, 1, 16, 100, 1, 64]
+    for dtype, Hq, Hkv, D in (("bf16", 8, 8, 128), ("f16", 16, 2, 64), ("bf16", 16, 8, 64)):
+        full_check(_variant(dtype, Hq, Hkv, D, lens, seed=41 + Hq, q_lens=q_lens))

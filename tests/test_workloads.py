@@ -8,7 +8,8 @@ import oracle
 from workloads import CONFIG_NAMES, make_workload
 
 BIG = {"decode_bf16_64req", "mixed_chunked_prefill_bf16", "prefix_shared_decode_bf16",
-       "long_context_decode_bf16"}
+       "long_context_decode_bf16", "prefill_chunk_2048_bf16", "prefill_8192_bf16",
+       "prefill_batch_4x1024_bf16", "prefill_chunk_bf16"}
 
 
 @pytest.mark.parametrize("name", CONFIG_NAMES)
@@ -57,6 +58,13 @@ def test_config_shapes():
     assert ids.size == 16 * 2048 and np.unique(ids).size == ids.size
     # the pool is larger than 2^31 bytes: offsets must be 64-bit
     assert c5.num_blocks * oracle.block_bytes(16, 8, 128, 2) > 2 ** 31
+    c6 = make_workload("prefill_chunk_2048_bf16", values=False)
+    assert list(c6.q_lens) == [2048] and list(c6.num_computed) == [2048]
+    c7 = make_workload("prefill_8192_bf16", values=False)
+    assert list(c7.q_lens) == [8192] and list(c7.num_computed) == [0]
+    c8 = make_workload("prefill_batch_4x1024_bf16", values=False)
+    assert list(c8.q_lens) == [1024, 1024, 1024, 1000]
+    assert list(c8.seq_lens) == [1024, 2048, 4024, 1512]
 
 
 @pytest.mark.parametrize("name", [n for n in CONFIG_NAMES if n not in BIG])

@@ -318,6 +318,28 @@ def _prefill_chunk_bf16(seed: int, values: bool = True) -> Workload:
                           values=values)
 
 
+def _prefill_2k_bf16(seed: int, values: bool = True) -> Workload:
+    # a 2048-token chunk on 2048 cached tokens (a token budget in the range the
+    # pages advise for max_num_batched_tokens)
+    return build_workload("prefill_chunk_2048_bf16", **_LLAMA3, num_blocks=20000,
+                          requests=[(2048, 2048)], seed=seed, table_width=256,
+                          values=values)
+
+
+def _prefill_8k_bf16(seed: int, values: bool = True) -> Workload:
+    # a fresh 8192-token prompt prefilled in one step
+    return build_workload("prefill_8192_bf16", **_LLAMA3, num_blocks=20000,
+                          requests=[(0, 8192)], seed=seed, table_width=512,
+                          values=values)
+
+
+def _prefill_batch_bf16(seed: int, values: bool = True) -> Workload:
+    # four requests prefilling 1024-token chunks on different histories
+    reqs = [(0, 1024), (1024, 1024), (3000, 1024), (512, 1000)]
+    return build_workload("prefill_batch_4x1024_bf16", **_LLAMA3, num_blocks=20000,
+                          requests=reqs, seed=seed, table_width=256, values=values)
+
+
 def _prefix_shared_bf16(seed: int, values: bool = True) -> Workload:
     rng = np.random.default_rng(seed + 7_000_000)
     suffix = rng.integers(64, 512, size=256, endpoint=True)
@@ -378,6 +400,9 @@ _BUILDERS = {
     "mixed_chunked_prefill_bf16": (_mixed_bf16, 1003),
     "prefix_shared_decode_bf16": (_prefix_shared_bf16, 1004),
     "prefill_chunk_bf16": (_prefill_chunk_bf16, 1006),
+    "prefill_chunk_2048_bf16": (_prefill_2k_bf16, 1007),
+    "prefill_8192_bf16": (_prefill_8k_bf16, 1008),
+    "prefill_batch_4x1024_bf16": (_prefill_batch_bf16, 1009),
     "long_context_decode_bf16": (_long_split_bf16, 1005),
     "decode_bf16_small": (_decode_bf16_small, 2002),
     "mixed_bf16_small": (_mixed_bf16_small, 2003),
