@@ -17,6 +17,7 @@ from .ref import (  # noqa: F401
     slot_of,
     slot_mapping,
     reshape_and_cache,
+    copy_blocks,
     gather_request_kv,
     paged_attention,
     paged_attention_partials,

@@ -142,6 +142,28 @@ def reshape_and_cache(pool: np.ndarray, key: np.ndarray, value: np.ndarray,
     return out
 
 
+def copy_blocks(pool: np.ndarray, pairs: np.ndarray) -> np.ndarray:
+    """Copy-on-write block fork ([P1] §4.3.2: samples of one prompt share its
+    blocks; a sample about to write into a shared block gets a private copy).
+    Return a copy of the pool where, for every (src, dst) row of `pairs`,
+    block dst holds block src's K and V bits.  A row with a negative entry is
+    skipped.  Precondition (the library's too): destinations are distinct and
+    none of them is also a source in the same call, so the order of the
+    copies does not matter."""
+    pairs = np.asarray(pairs, dtype=np.int64).reshape(-1, 2)
+    live = pairs[(pairs[:, 0] >= 0) & (pairs[:, 1] >= 0)]
+    if np.unique(live[:, 1]).size != live.shape[0]:
+        raise ValueError("copy_blocks: destinations must be distinct")
+    if np.isin(live[:, 1], live[:, 0]).any():
+        raise ValueError("copy_blocks: a destination is also a source")
+    if live.size and live.max() >= pool.shape[0]:
+        raise IndexError("copy_blocks: block id beyond the pool")
+    out = pool.copy()
+    for src, dst in live:
+        out[dst] = pool[src]
+    return out
+
+
 # --------------------------------------------------------------------------
 # read path: paged attention ([P1] §3.3.3 / §4.2, [P2] §3.4, [P4] §3.4 / §4.2)
 # --------------------------------------------------------------------------

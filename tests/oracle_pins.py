@@ -358,6 +358,58 @@ def check_reshape_and_cache(seed=7):
     assert np.array_equal(pool, fresh)
 
 
+def check_copy_on_write_fork(seed=9):
+    """[P1] §4.3.2 (parallel sampling): three samples share prompt blocks
+    [0, 1, 2]; before a sample writes into the shared, partly filled last
+    block it gets a private copy (block 10, 20 or 30).  Pinned by the
+    textbook result: each sample's attention after its own write equals plain
+    softmax attention over the prompt's keys plus that sample's key, laid out
+    contiguously; the shared blocks keep their bits."""
+    rng = np.random.default_rng(seed)
+    B, Hkv, G, D, NB = 16, 2, 2, 8, 40
+    prompt = 2 * B + 14                       # last prompt block 14/16 full
+    f32 = lambda shape: rng.standard_normal(shape).astype(np.float32)  # noqa: E731
+    pool = f32((NB, 2, B, Hkv, D))
+    K_p, V_p = f32((prompt, Hkv, D)), f32((prompt, Hkv, D))
+    for j in range(prompt):                   # prompt blocks 0, 1, 2 in order
+        pool[j // B, 0, j % B], pool[j // B, 1, j % B] = K_p[j], V_p[j]
+    shared_before = pool[:3].copy()
+    private = [10, 20, 30]
+    forked = ref.copy_blocks(pool, np.array([[2, d] for d in private]))
+    assert np.array_equal(forked[:3], shared_before)
+    for d in private:
+        assert np.array_equal(forked[d], pool[2])
+    # every sample writes its own new token at position `prompt`
+    k_new, v_new = f32((3, Hkv, D)), f32((3, Hkv, D))
+    tables = np.array([[0, 1, d] for d in private], np.int32)
+    qsl = np.arange(4, dtype=np.int32)
+    slots = oracle.slot_mapping(tables, qsl, np.full(3, prompt, np.int32), B)
+    assert list(slots) == [d * B + prompt - 2 * B for d in private]
+    after = oracle.reshape_and_cache(forked, k_new, v_new, slots)
+    assert np.array_equal(after[:3], shared_before)
+    q = f32((3, Hkv * G, D))
+    scale = 0.3
+    got = oracle.paged_attention(q, after, tables, np.full(3, prompt + 1, np.int32), qsl,
+                                 np.full(3, prompt, np.int32), scale, "f32")
+    for smp in range(3):
+        K = np.concatenate([K_p, k_new[smp:smp + 1]])
+        V = np.concatenate([V_p, v_new[smp:smp + 1]])
+        for h in range(Hkv * G):
+            s = scale * (K[:, h // G].astype(np.float64) @ q[smp, h].astype(np.float64))
+            p = np.exp(s - s.max())
+            want = (p / p.sum()) @ V[:, h // G].astype(np.float64)
+            assert np.max(np.abs(got[smp, h] - want)) < 1e-12
+    # the order of the copies does not matter, and rows with -1 are skipped
+    rev = ref.copy_blocks(pool, np.array([[2, 30], [-1, 5], [2, 20], [2, 10]]))
+    assert np.array_equal(rev, forked)
+    for bad in ([[2, 10], [3, 10]], [[2, 10], [10, 11]]):
+        try:
+            ref.copy_blocks(pool, np.array(bad))
+        except ValueError:
+            continue
+        raise AssertionError(f"precondition not enforced for {bad}")
+
+
 def check_element_decoding():
     """bfloat16 is the upper 16 bits of an IEEE-754 binary32; binary16 per IEEE-754."""
     bf = {0x3F80: 1.0, 0xC000: -2.0, 0x4049: 3.140625, 0x3E80: 0.25, 0x0000: 0.0,
@@ -399,6 +451,7 @@ ALL_CHECKS = [
     check_prefix_sharing_invariance,
     check_split_merge,
     check_reshape_and_cache,
+    check_copy_on_write_fork,
     check_element_decoding,
     check_bf16_paths_agree,
 ]

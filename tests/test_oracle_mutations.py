@@ -86,6 +86,26 @@ def _bad_rac_kv_swapped(pool, key, value, slots):
     return _orig_rac(pool, value, key, slots)
 
 
+_orig_copy = ref.copy_blocks
+
+
+def _bad_copy_k_only(pool, pairs):
+    out = _orig_copy(pool, pairs)
+    for src, dst in np.asarray(pairs).reshape(-1, 2):
+        if src >= 0 and dst >= 0:
+            out[dst, 1] = pool[dst, 1]
+    return out
+
+
+def _bad_copy_reversed(pool, pairs):
+    p = np.asarray(pairs).reshape(-1, 2)
+    out = pool.copy()
+    for src, dst in p:
+        if src >= 0 and dst >= 0:
+            out[src] = pool[dst]
+    return out
+
+
 MUTATIONS = {
     "gqa_interleaved": ("kv_head_of", _bad_gqa),
     "causal_strict": ("visible", _bad_causal_strict),
@@ -101,6 +121,8 @@ MUTATIONS = {
     "bf16_decode_shift": ("decode_bits", _bad_decode),
     "kv_bytes_missing_factor_2": ("kv_bytes_per_token", _bad_kv_bytes),
     "k_v_swapped_on_write": ("reshape_and_cache", _bad_rac_kv_swapped),
+    "copy_blocks_k_only": ("copy_blocks", _bad_copy_k_only),
+    "copy_blocks_direction": ("copy_blocks", _bad_copy_reversed),
 }
 
 
