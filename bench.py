@@ -297,6 +297,39 @@ def measure(name, args, rotations):
     return res
 
 
+def measure_copy(args, pairs_n: int, num_blocks: int = 20000):
+    """pa_copy_blocks on the decode pool's shape (64 KiB blocks): pairs_n
+    forks from distinct sources to distinct fresh blocks, on rotated pools."""
+    import torch
+    import paged_kv_attention_07_amd as pa
+    rng = np.random.default_rng(4242)
+    pools = [torch.empty((num_blocks, 2, 16, 8, 128), dtype=torch.bfloat16, device="cuda")
+             for _ in range(2)]
+    for p in pools:
+        p.normal_()
+    ids = rng.permutation(num_blocks)[:2 * pairs_n]
+    pairs = torch.from_numpy(np.stack([ids[:pairs_n], ids[pairs_n:]], 1).astype(np.int32)).cuda()
+    for i in range(args.warmup):
+        pa.pa_copy_blocks(pools[i % 2], pairs)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    for i in range(args.steps):
+        ev[i][0].record()
+        pa.pa_copy_blocks(pools[i % 2], pairs)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    block_bytes = 2 * 16 * 8 * 128 * 2
+    moved = 2 * pairs_n * block_bytes  # read src + write dst
+    print(f"[bench] copy_blocks {pairs_n} pairs: {ms * 1e3:.1f} us", file=sys.stderr, flush=True)
+    del pools
+    torch.cuda.empty_cache()
+    return {"pairs": pairs_n, "block_bytes": block_bytes, "avg_us": round(ms * 1e3, 2),
+            "gbs": round(moved / (ms * 1e-3) / 1e9, 1),
+            "pct_peak_hbm": round(100 * moved / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -306,7 +339,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--extra", action="store_true", help="also time the prefix-shared and "
                     "long-context decode batches")
-    ap.add_argument("--only", choices=sorted(WORKLOADS), default=None)
+    ap.add_argument("--only", choices=sorted(WORKLOADS) + ["copy"], default=None)
     ap.add_argument("--copy-probe", action="store_true",
                     help="after timing, copy 1 GiB device-to-device 3 times (a kernel of "
                          "known traffic, to calibrate the profiler's FETCH_SIZE/WRITE_SIZE)")
@@ -321,6 +354,11 @@ def main():
     rot = 4
     names = [args.only] if args.only else ["decode", "mixed", "chunk"] + (
         ["prefix", "long", "prefill2k", "prefill8k", "prefillbatch"] if args.extra else [])
+    copy_lines = []
+    if args.only == "copy" or (args.extra and not args.only):
+        copy_lines = [measure_copy(args, n) for n in (16, 256, 4096)]
+        if args.only == "copy":
+            names = ["decode"]
     results = {k: measure(WORKLOADS[k], args, rot if k != "long" else 2) for k in names}
 
     head = results.get("decode") or next(iter(results.values()))
@@ -404,6 +442,8 @@ def main():
                 "effective_gbs_logical": round(rc["attn_logical"] / (r["attn_ms_avg"] * 1e-3) / 1e9, 1),
                 "ms_per_step": round(r["ms_step"], 5),
             }
+    if copy_lines:
+        line["copy_blocks"] = copy_lines
     if args.copy_probe:
         # an elementwise kernel that reads 1 GiB and writes 1 GiB
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")

@@ -97,6 +97,25 @@ int pa_reshape_and_cache(const void* key, const void* value, void* kv_cache,
                          void* stream);
 
 /*
+ * pa_copy_blocks -- copy whole KV-cache blocks inside the cache.
+ *   [P1] §4.3.2 (copy-on-write: samples of one prompt share its blocks; a
+ *   sample that is about to write into a shared block first gets a private
+ *   copy of it).  For every pair p with src = block_pairs[2p] >= 0 and
+ *   dst = block_pairs[2p + 1] >= 0:
+ *     kv_cache[dst][0 | 1][:][:][:] = kv_cache[src][0 | 1][:][:][:]
+ *   bit-exact; a pair with a negative entry is skipped; nothing else in the
+ *   cache changes.
+ *
+ *   kv_cache     [num_blocks, 2, block_size, num_kv_heads, head_dim].
+ *   block_pairs  [num_pairs, 2] int32 (src, dst), device memory.
+ *   Preconditions: ids < num_blocks; destinations distinct; no destination is
+ *   also a source in the same call (the copies run in parallel, in no order).
+ */
+int pa_copy_blocks(void* kv_cache, const int32_t* block_pairs, int32_t num_pairs,
+                   int64_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                   int32_t head_dim, int32_t dtype, void* stream);
+
+/*
  * pa_attention_workspace_size -- bytes of fp32 scratch the attention calls
  * need for their split-KV partial results (max, sum, unnormalised output per
  * query head and partition).  Pure function of its arguments; returns 0 for

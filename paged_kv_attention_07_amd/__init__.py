@@ -15,7 +15,7 @@ from typing import Optional
 
 __all__ = [
     "PAError", "lib", "library_path", "DTYPE_CODES",
-    "pa_compute_slot_mapping", "pa_reshape_and_cache",
+    "pa_compute_slot_mapping", "pa_reshape_and_cache", "pa_copy_blocks",
     "pa_attention_workspace_size", "pa_attention_decode", "pa_attention_mixed",
     "pa_status_string", "pa_version",
 ]
@@ -26,7 +26,7 @@ library_path = os.path.join(_HERE, "libpa.so")
 if not os.path.exists(library_path):
     raise ImportError(
         f"{library_path} is missing: build the HIP library first "
-        "(python -m paged_kv_attention_07_amd.build)")
+        "(python paged_kv_attention_07_amd/build.py)")
 
 # torch is imported before the library is loaded: libpa.so needs
 # libamdhip64.so.7, and torch bundles its own copy under that soname.  Loading
@@ -49,6 +49,8 @@ lib.pa_compute_slot_mapping.argtypes = [_vp, _vp, _i32, _vp, _vp, _i32, _i32, _i
 lib.pa_compute_slot_mapping.restype = ctypes.c_int
 lib.pa_reshape_and_cache.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32, _i32, _vp]
 lib.pa_reshape_and_cache.restype = ctypes.c_int
+lib.pa_copy_blocks.argtypes = [_vp, _vp, _i32, _i64, _i32, _i32, _i32, _i32, _vp]
+lib.pa_copy_blocks.restype = ctypes.c_int
 lib.pa_attention_workspace_size.argtypes = [_i32] * 8
 lib.pa_attention_workspace_size.restype = _sz
 lib.pa_attention_decode.argtypes = [
@@ -153,6 +155,20 @@ def pa_reshape_and_cache(key, value, kv_cache, slot_mapping) -> None:
         _dev(slot_mapping, "slot_mapping", torch.int64, 1), T, nb, bs, hkv, d,
         _dtype_code(kv_cache), _stream())
     _check("pa_reshape_and_cache", st)
+
+
+def pa_copy_blocks(kv_cache, block_pairs) -> None:
+    """Copy whole cache blocks: kv_cache[dst] = kv_cache[src] for every
+    (src, dst) row of block_pairs [P, 2] (int32, on the cache's device)."""
+    torch = _torch()
+    nb, bs, hkv, d = _cache_dims(kv_cache)
+    if block_pairs.dim() != 2 or block_pairs.shape[1] != 2:
+        raise ValueError("block_pairs must be [num_pairs, 2]")
+    P = int(block_pairs.shape[0])
+    st = lib.pa_copy_blocks(_dev(kv_cache, "kv_cache"),
+                            _dev(block_pairs, "block_pairs", torch.int32, 2), P, nb, bs, hkv,
+                            d, _dtype_code(kv_cache), _stream())
+    _check("pa_copy_blocks", st)
 
 
 def pa_attention_workspace_size(num_seqs: int, num_tokens: int, num_q_heads: int,

@@ -1,6 +1,6 @@
 """Build libpa.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree.
 
-    python -m paged_kv_attention_07_amd.build [--verbose]
+    python paged_kv_attention_07_amd/build.py [--verbose]
 
 The library lands next to this file; the Python binding loads it from there.
 """

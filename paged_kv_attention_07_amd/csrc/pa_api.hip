@@ -121,6 +121,20 @@ int pa_reshape_and_cache(const void* key, const void* value, void* kv_cache,
                                                  row_bytes, static_cast<hipStream_t>(stream)));
 }
 
+int pa_copy_blocks(void* kv_cache, const int32_t* block_pairs, int32_t num_pairs,
+                   int64_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                   int32_t head_dim, int32_t dtype, void* stream) {
+  int st = check_cache(kv_cache, num_blocks, block_size, num_kv_heads, head_dim, dtype);
+  if (st != PA_OK) return st;
+  if (num_pairs < 0) return PA_ERR_INVALID_ARG;
+  if (num_pairs == 0) return PA_OK;
+  if (!block_pairs) return PA_ERR_INVALID_ARG;
+  const int64_t block_bytes =
+      (int64_t)2 * block_size * num_kv_heads * head_dim * elem_bytes(dtype);
+  return hip_status(pa::launch_copy_blocks(kv_cache, block_pairs, num_pairs, block_bytes,
+                                           static_cast<hipStream_t>(stream)));
+}
+
 size_t pa_attention_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
                                    int32_t num_kv_heads, int32_t head_dim, int32_t max_seq_len,
                                    int32_t max_query_len, int32_t num_splits) {

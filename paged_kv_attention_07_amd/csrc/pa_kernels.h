@@ -58,6 +58,9 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* kv
                                     const int64_t* slot_mapping, int32_t num_tokens,
                                     int32_t row_bytes, hipStream_t stream);
 
+hipError_t launch_copy_blocks(void* kv_cache, const int32_t* pairs, int32_t num_pairs,
+                              int64_t block_bytes, hipStream_t stream);
+
 // dtype: pa_dtype value; head_dim 64 | 128; group = Hq / Hkv in {1,2,4,8}.
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int head_dim, int group,
                          hipStream_t stream);

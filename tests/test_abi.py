@@ -29,7 +29,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for want in ("pa_reshape_and_cache", "pa_attention_decode", "pa_attention_mixed",
-                 "pa_compute_slot_mapping", "pa_attention_workspace_size", "pa_status_string"):
+                 "pa_compute_slot_mapping", "pa_attention_workspace_size", "pa_status_string",
+                 "pa_copy_blocks"):
         assert want in names
 
 
@@ -74,6 +75,18 @@ def test_reshape_and_cache_checks():
     assert rac(dtype=9) == UNSUPPORTED
     assert rac(key=ctypes.c_void_p(0x10008)) == INVALID   # not 16-byte aligned
     assert rac(T=0) == OK                                 # nothing to do, nothing launched
+
+
+def test_copy_blocks_checks():
+    f = lib.pa_copy_blocks
+    assert f(None, FAKE, 2, 64, 16, 2, 64, 1, None) == INVALID
+    assert f(FAKE, None, 2, 64, 16, 2, 64, 1, None) == INVALID
+    assert f(FAKE, FAKE, -1, 64, 16, 2, 64, 1, None) == INVALID
+    assert f(FAKE, FAKE, 2, 0, 16, 2, 64, 1, None) == INVALID
+    assert f(FAKE, FAKE, 2, 64, 8, 2, 64, 1, None) == UNSUPPORTED
+    assert f(FAKE, FAKE, 2, 64, 16, 2, 96, 1, None) == UNSUPPORTED
+    assert f(FAKE, FAKE, 2, 64, 16, 2, 64, 7, None) == UNSUPPORTED
+    assert f(FAKE, None, 0, 64, 16, 2, 64, 1, None) == OK   # nothing to copy
 
 
 def ws_size(R=4, T=4, Hq=4, Hkv=2, D=64, L=100, Q=1, S=0):

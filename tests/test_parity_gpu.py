@@ -342,3 +342,80 @@ def test_mixed_both_tile_shapes(tokens_per_wave, monkeypatch):
     q_lens = [40, 2, 33, 1, 16, 100, 1, 64]
     for dtype, Hq, Hkv, D in (("bf16", 8, 8, 128), ("f16", 16, 2, 64), ("bf16", 16, 8, 64)):
         full_check(_variant(dtype, Hq, Hkv, D, lens, seed=41 + Hq, q_lens=q_lens))
+
+
+# --------------------------------------------------------------------------
+# block copies (copy-on-write forks)
+# --------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("dtype,Hkv,D", [("bf16", 8, 128), ("f32", 2, 64), ("f16", 1, 64),
+                                         ("f32", 8, 128)])
+def test_copy_blocks_bit_exact(dtype, Hkv, D):
+    """Random pairs (with skipped -1 rows) on a pool with NaN payloads: the
+    copy is bit-exact and touches nothing but the destinations."""
+    import torch
+    rng = np.random.default_rng(23 + D + Hkv)
+    NB = 300
+    w = build_workload("copy", dtype=dtype, num_q_heads=Hkv, num_kv_heads=Hkv, head_dim=D,
+                       num_blocks=NB, requests=[(40, 1)], seed=5 + D, table_width=8)
+    pool = w.pool.copy()
+    ids = rng.permutation(NB)
+    src, dst = ids[:70], ids[70:140]
+    pairs = np.stack([src, dst], 1).astype(np.int32)
+    pairs[[3, 17], 0] = -1
+    pairs[[29], 1] = -1
+    kv = gu.to_device(pool, dtype)
+    pa.pa_copy_blocks(kv, gu.ints_to_device(pairs, np.int32))
+    got = gu.from_device(kv, dtype)
+    want = oracle.copy_blocks(pool, pairs)
+    assert np.array_equal(gu.bits(got), gu.bits(want))
+    # empty call is a no-op
+    pa.pa_copy_blocks(kv, gu.ints_to_device(np.zeros((0, 2), np.int32), np.int32))
+    torch.cuda.synchronize()
+    assert np.array_equal(gu.bits(gu.from_device(kv, dtype)), gu.bits(want))
+
+
+def test_copy_on_write_parallel_sampling():
+    """Parallel sampling: n samples share a prompt whose last block is partly
+    filled.  Each sample forks the shared block with pa_copy_blocks, writes
+    its own next token into its copy, and decodes; every sample matches the
+    oracle, and the shared blocks keep their bits."""
+    import dataclasses
+    n, prompt = 6, 16 * 20 + 9
+    base = build_workload("cow", dtype="bf16", num_q_heads=32, num_kv_heads=8, head_dim=128,
+                          num_blocks=2000, requests=[(prompt, 1)], seed=77, table_width=32)
+    nbp = -(-prompt // 16)
+    shared = base.block_table[0, :nbp].copy()
+    rng = np.random.default_rng(78)
+    spare = np.setdiff1d(np.arange(base.num_blocks), shared)
+    fork_dst = rng.choice(spare, n, replace=False).astype(np.int32)
+    tables = np.full((n, 32), -1, np.int32)
+    for smp in range(n):
+        tables[smp, :nbp] = shared
+        tables[smp, nbp - 1] = fork_dst[smp]
+    pairs = np.stack([np.full(n, shared[-1], np.int32), fork_dst], 1)
+    rs = np.random.default_rng(79)
+    def bf16(shape):
+        x = rs.standard_normal(shape).astype(np.float32)
+        return (x.view(np.uint32) >> 16).astype(np.uint16)
+    w = dataclasses.replace(
+        base, block_table=tables, seq_lens=np.full(n, prompt + 1, np.int32),
+        num_computed=np.full(n, prompt, np.int32),
+        query_start_loc=np.arange(n + 1, dtype=np.int32),
+        q=bf16((n, 32, 128)), k_new=bf16((n, 8, 128)), v_new=bf16((n, 8, 128)))
+    dev = gu.Device(w, base.pool)
+    pa.pa_copy_blocks(dev.kv, gu.ints_to_device(pairs, np.int32))
+    slots = dev.slot_mapping()
+    dev.scatter(slots)
+    out = gu.from_device(dev.attend(), "bf16")
+    g_pool = gu.from_device(dev.kv, "bf16")
+    r_pool = oracle.copy_blocks(base.pool, pairs)
+    r_slots = oracle.slot_mapping(tables, w.query_start_loc, w.num_computed, 16)
+    assert np.array_equal(slots.cpu().numpy(), r_slots)
+    r_pool = oracle.reshape_and_cache(r_pool, w.k_new, w.v_new, r_slots)
+    assert np.array_equal(gu.bits(g_pool), gu.bits(r_pool))
+    assert np.array_equal(gu.bits(g_pool[shared]), gu.bits(base.pool[shared]))
+    ref = oracle.paged_attention(w.q, r_pool, tables, w.seq_lens, w.query_start_loc,
+                                 w.num_computed, w.scale, "bf16")
+    gu.check_close(w, out, ref, what="cow samples")
