@@ -190,11 +190,13 @@ class Scheduler:
         """[P1] §4.3.2: a new sample of a running request shares all of its
         blocks (one more reference each) and continues from the same tokens.
         Only a request past its prefill (every token but the last sampled one
-        computed) can fork; otherwise nothing happens and False is returned."""
+        computed) can fork, and only while fewer than max_num_seqs requests
+        run; otherwise nothing happens and False is returned."""
         p = self.requests.get(parent_id)
         assert child_id not in self.requests
         if (p is None or p.status != RUNNING or p.num_computed != len(p.tokens) - 1
-                or p.num_generated >= max_new_tokens):
+                or p.num_generated >= max_new_tokens
+                or len(self.running) >= self.max_num_seqs):
             return False
         assert p.prompt_len + max_new_tokens - 1 <= self.max_model_len
         c = Request(child_id, list(p.tokens), p.prompt_len, max_new_tokens,

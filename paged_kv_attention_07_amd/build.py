@@ -48,6 +48,15 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
+def host_sources():
+    """Plain C++ (host-only) sources, compiled with the host compiler."""
+    return sorted(glob.glob(os.path.join(CSRC, "*.cpp")))
+
+
+def host_flags():
+    return ["-O2", "-std=c++17", "-fPIC", "-Wall", f"-I{INCLUDE}", f"-I{CSRC}"]
+
+
 def build(verbose: bool = False, out: str = LIB_PATH, extra_flags=()) -> str:
     """Compile every source into one shared library; returns its path."""
     objs = []
@@ -58,6 +67,14 @@ def build(verbose: bool = False, out: str = LIB_PATH, extra_flags=()) -> str:
     for src in sources():
         obj = os.path.join(build_dir, os.path.basename(src) + ".o")
         cmd = [cc, *compile_flags(), *extra_flags, "-c", src, "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT), src))
+        objs.append(obj)
+    cxx = shutil.which("g++") or "c++"
+    for src in host_sources():
+        obj = os.path.join(build_dir, os.path.basename(src) + ".o")
+        cmd = [cxx, *host_flags(), "-c", src, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT), src))
@@ -73,7 +90,7 @@ def build(verbose: bool = False, out: str = LIB_PATH, extra_flags=()) -> str:
         if p.returncode:
             failed.append(src)
     if failed:
-        raise RuntimeError("hipcc failed for: " + ", ".join(os.path.basename(f) for f in failed))
+        raise RuntimeError("compilation failed for: " + ", ".join(os.path.basename(f) for f in failed))
     tmp = out + ".tmp"
     cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:

@@ -3,6 +3,7 @@ declares, and its host-side argument checks return the documented status
 codes before anything is launched (no GPU is touched by these tests)."""
 
 import ctypes
+import glob
 import os
 import re
 import subprocess
@@ -11,6 +12,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "pa.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 pa = pytest.importorskip("paged_kv_attention_07_amd")
 lib = pa.lib
@@ -21,16 +23,20 @@ FAKE_WS = ctypes.c_void_p(0x100000)  # 256-byte aligned
 
 
 def declared_functions():
-    text = open(HEADER, encoding="utf-8").read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(pa_[a-z_]+)\s*\(", text)))
+    names = set()
+    for path in HEADERS:
+        text = open(path, encoding="utf-8").read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"\b(pa_[a-z_0-9]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_declares_the_boundary():
     names = declared_functions()
     for want in ("pa_reshape_and_cache", "pa_attention_decode", "pa_attention_mixed",
                  "pa_compute_slot_mapping", "pa_attention_workspace_size", "pa_status_string",
-                 "pa_copy_blocks"):
+                 "pa_copy_blocks", "pa_sched_create", "pa_sched_schedule", "pa_sched_update",
+                 "pa_xxh64"):
         assert want in names
 
 
@@ -44,9 +50,10 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_no_torch_types_in_header():
-    text = open(HEADER, encoding="utf-8").read()
-    assert "torch" not in text.lower().replace("pytorch", "") or "at::" not in text
-    assert "extern \"C\"" in text
+    for path in HEADERS:
+        text = open(path, encoding="utf-8").read()
+        assert "at::" not in text and "torch::" not in text and "c10::" not in text
+        assert "extern \"C\"" in text
 
 
 def test_status_strings():
