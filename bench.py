@@ -330,6 +330,77 @@ def measure_copy(args, pairs_n: int, num_blocks: int = 20000):
             "pct_peak_hbm": round(100 * moved / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
 
 
+def measure_serve(name: str = "serve_llama3_2k"):
+    """The multi-step driver over a synthetic serving trace: the C++
+    scheduler plans every step (prefix hits, chunked prefill, forks), one
+    metadata copy, block copies, slot mapping, K/V scatter and attention on
+    the GPU.  One attention layer per step (no model): tokens/s here is the
+    rate at which the engine turns scheduled tokens into attention output."""
+    import torch
+    from paged_kv_attention_07_amd.engine import Engine
+    from workloads.trace import step_inputs, trace
+    t = trace(name)
+    Hq, Hkv, D = 32, 8, 128
+    q, k, v = step_inputs(t.seed, 0, t.max_num_batched_tokens, Hq, Hkv, D, "bf16")
+    dev = [torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda() for x in (q, k, v)]
+    # sampled tokens, looked up per (request, step): the stand-in for a model
+    max_id = max([r for a in t.arrivals.values() for r, _, _ in a] +
+                 [c for f in t.forks.values() for _, c, _ in f]) + 1
+    table = np.array([[t.sampled(r, st) for st in range(t.num_steps)] for r in range(max_id)],
+                     dtype=np.int32)
+
+    def run():
+        eng = Engine(num_blocks=t.num_blocks, max_num_batched_tokens=t.max_num_batched_tokens,
+                     max_num_seqs=t.max_num_seqs, max_model_len=t.max_model_len, num_q_heads=Hq,
+                     num_kv_heads=Hkv, head_dim=D, dtype="bf16")
+        host_s, tokens, steps, gpu_ms = 0.0, 0, 0, []
+        events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(64)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for step in range(t.num_steps):
+            for rid, prompt, n in t.arrivals.get(step, []):
+                eng.add_request(rid, prompt, n)
+            for parent, child, n in t.forks.get(step, []):
+                eng.fork(parent, child, n)
+            h0 = time.perf_counter()
+            e0, e1 = events[steps % len(events)]
+            e0.record()
+            st = eng.step(*dev)
+            e1.record()
+            if st.num_seqs == 0:
+                eng.update([])
+                if not eng.stats()["num_waiting"] and step > max(t.arrivals):
+                    break
+                continue
+            eng.update(table[st.request_ids, step])
+            host_s += time.perf_counter() - h0
+            tokens += st.num_tokens
+            steps += 1
+            if steps % len(events) == 0:
+                gpu_ms.extend(a.elapsed_time(b) for a, b in events)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        gpu_ms.extend(a.elapsed_time(b) for a, b in events[:steps % len(events)])
+        stats = eng.stats()
+        eng.close()
+        del eng
+        torch.cuda.empty_cache()
+        return wall, host_s, tokens, steps, stats, float(np.sum(gpu_ms))
+
+    run()                                   # warm-up pass over the same trace
+    wall, host_s, tokens, steps, stats, gpu_total_ms = run()
+    print(f"[bench] serve {name}: {steps} steps, {tokens} tokens in {wall * 1e3:.1f} ms",
+          file=sys.stderr, flush=True)
+    return {"trace": name, "steps": steps, "tokens": tokens,
+            "tokens_per_s": round(tokens / wall, 1), "ms_per_step": round(wall * 1e3 / steps, 4),
+            "host_us_per_step": round(host_s * 1e6 / steps, 1),
+            "gpu_us_per_step": round(gpu_total_ms * 1e3 / steps, 1),
+            "prefix_hit_tokens": stats["total_prefix_hit_tokens"],
+            "preemptions": stats["total_preemptions"],
+            "layer": "Llama-3-8B attention layer (Hq 32, Hkv 8, D 128, bf16)"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -339,7 +410,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--extra", action="store_true", help="also time the prefix-shared and "
                     "long-context decode batches")
-    ap.add_argument("--only", choices=sorted(WORKLOADS) + ["copy"], default=None)
+    ap.add_argument("--only", choices=sorted(WORKLOADS) + ["copy", "serve"], default=None)
     ap.add_argument("--copy-probe", action="store_true",
                     help="after timing, copy 1 GiB device-to-device 3 times (a kernel of "
                          "known traffic, to calibrate the profiler's FETCH_SIZE/WRITE_SIZE)")
@@ -354,11 +425,13 @@ def main():
     rot = 4
     names = [args.only] if args.only else ["decode", "mixed", "chunk"] + (
         ["prefix", "long", "prefill2k", "prefill8k", "prefillbatch"] if args.extra else [])
-    copy_lines = []
+    copy_lines, serve_line = [], None
     if args.only == "copy" or (args.extra and not args.only):
         copy_lines = [measure_copy(args, n) for n in (16, 256, 4096)]
-        if args.only == "copy":
-            names = ["decode"]
+    if args.only == "serve" or (args.extra and not args.only):
+        serve_line = measure_serve()
+    if args.only in ("copy", "serve"):
+        names = ["decode"]
     results = {k: measure(WORKLOADS[k], args, rot if k != "long" else 2) for k in names}
 
     head = results.get("decode") or next(iter(results.values()))
@@ -444,6 +517,8 @@ def main():
             }
     if copy_lines:
         line["copy_blocks"] = copy_lines
+    if serve_line:
+        line["serve"] = serve_line
     if args.copy_probe:
         # an elementwise kernel that reads 1 GiB and writes 1 GiB
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")

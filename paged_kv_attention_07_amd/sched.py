@@ -92,7 +92,8 @@ def block_hash(parent: Optional[int], tokens) -> int:
 
 @dataclasses.dataclass
 class Step:
-    """Views of one step's metadata (valid until the next schedule())."""
+    """Views of one step's metadata (valid until the same buffer set is
+    reused, two schedule() calls later)."""
     request_ids: np.ndarray
     query_start_loc: np.ndarray
     num_computed: np.ndarray
@@ -103,6 +104,8 @@ class Step:
     preempted: np.ndarray
     max_query_len: int
     max_seq_len: int
+    buffer: int                      # which buffer set holds it
+    arena_len: int                   # int32 elements of the arena in use
 
     @property
     def num_seqs(self) -> int:
@@ -117,11 +120,31 @@ class Step:
         return np.diff(self.query_start_loc)
 
 
+class ArenaLayout:
+    """One int32 arena per buffer set holding everything the GPU needs, so a
+    step's metadata goes to the device in one copy of its used prefix:
+    [query_start_loc S+1 | num_computed S | seq_lens S | copy_pairs 2S |
+     block_table S x stride]."""
+
+    def __init__(self, max_num_seqs: int, stride: int):
+        S = max_num_seqs
+        self.S, self.stride = S, stride
+        self.qsl = 0
+        self.nc = S + 1
+        self.sl = 2 * S + 1
+        self.cp = 3 * S + 1
+        self.bt = 5 * S + 1
+        self.size = self.bt + S * stride
+
+    def used(self, num_seqs: int) -> int:
+        return self.bt + num_seqs * self.stride
+
+
 class Scheduler:
     def __init__(self, num_blocks: int, block_size: int, max_num_batched_tokens: int,
                  max_num_seqs: int, max_model_len: int, enable_chunked_prefill: bool = True,
                  enable_prefix_caching: bool = True, long_prefill_token_threshold: int = 0,
-                 pin: bool = False):
+                 pin: bool = False, num_buffers: int = 2):
         cfg = _Config(num_blocks, block_size, max_num_batched_tokens, max_num_seqs,
                       max_model_len, long_prefill_token_threshold, int(enable_chunked_prefill),
                       int(enable_prefix_caching))
@@ -131,29 +154,42 @@ class Scheduler:
         self.num_blocks, self.block_size = num_blocks, block_size
         self.max_num_seqs = max_num_seqs
         self.stride = -(-max_model_len // block_size)
+        self.layout = L = ArenaLayout(max_num_seqs, self.stride)
         S, T = max_num_seqs, max_num_batched_tokens
-
-        def buf(shape, dt):
+        # arenas: torch pinned tensors when pin=True (kept so copies from
+        # them are asynchronous), numpy views either way
+        self.arenas_torch, self.arenas = [], []
+        for _ in range(num_buffers):
             if pin:
                 import torch
-                tdt = {np.int32: torch.int32, np.int64: torch.int64}[dt]
-                return torch.empty(shape, dtype=tdt, pin_memory=True).numpy()
-            return np.empty(shape, dt)
-
-        self._bufs = dict(request_ids=buf(S, np.int64), query_start_loc=buf(S + 1, np.int32),
-                          num_computed=buf(S, np.int32), seq_lens=buf(S, np.int32),
-                          block_table=buf((S, self.stride), np.int32),
-                          token_ids=buf(T, np.int32), copy_pairs=buf((S, 2), np.int32),
-                          preempted_ids=buf(S, np.int64))
-        b = self._bufs
-        self._step = _Step(*(b[k].ctypes.data for k in (
-            "request_ids", "query_start_loc", "num_computed", "seq_lens", "block_table",
-            "token_ids", "copy_pairs", "preempted_ids")), self.stride, 0, 0, 0, 0, 0, 0)
+                t = torch.empty(L.size, dtype=torch.int32, pin_memory=True)
+                self.arenas_torch.append(t)
+                self.arenas.append(t.numpy())
+            else:
+                self.arenas.append(np.empty(L.size, np.int32))
+        self._ids = [np.empty(S, np.int64) for _ in range(num_buffers)]
+        self._pre = [np.empty(S, np.int64) for _ in range(num_buffers)]
+        self._tok = [np.empty(T, np.int32) for _ in range(num_buffers)]
+        self._steps = []
+        for i, a in enumerate(self.arenas):
+            base = a.ctypes.data
+            self._steps.append(_Step(
+                self._ids[i].ctypes.data, base + 4 * L.qsl, base + 4 * L.nc, base + 4 * L.sl,
+                base + 4 * L.bt, self._tok[i].ctypes.data, base + 4 * L.cp,
+                self._pre[i].ctypes.data, self.stride, 0, 0, 0, 0, 0, 0))
+        self._next = 0
         self._finished = np.empty(S, np.int64)
-        self._last_n = 0
+
+    @classmethod
+    def view(cls, handle) -> "Scheduler":
+        """A non-owning handle on a scheduler created elsewhere (an engine's):
+        requests, forks and inspection only."""
+        self = cls.__new__(cls)
+        self._h, self._owned, self._steps = handle, False, []
+        return self
 
     def close(self) -> None:
-        if self._h:
+        if self._h and getattr(self, "_owned", True):
             lib.pa_sched_destroy(self._h)
             self._h = None
 
@@ -176,16 +212,19 @@ class Scheduler:
 
     # ---- steps
     def schedule(self) -> Step:
-        st = self._step
+        i = self._next
+        self._next = (i + 1) % len(self._steps)
+        st = self._steps[i]
         _check("pa_sched_schedule", lib.pa_sched_schedule(self._h, ctypes.byref(st)))
-        b, n = self._bufs, st.num_seqs
-        self._last_n = n
-        return Step(request_ids=b["request_ids"][:n], query_start_loc=b["query_start_loc"][:n + 1],
-                    num_computed=b["num_computed"][:n], seq_lens=b["seq_lens"][:n],
-                    block_table=b["block_table"][:n], token_ids=b["token_ids"][:st.num_tokens],
-                    copy_pairs=b["copy_pairs"][:st.num_copies],
-                    preempted=b["preempted_ids"][:st.num_preempted],
-                    max_query_len=st.max_query_len, max_seq_len=st.max_seq_len)
+        a, L, n = self.arenas[i], self.layout, st.num_seqs
+        return Step(request_ids=self._ids[i][:n], query_start_loc=a[L.qsl:L.qsl + n + 1],
+                    num_computed=a[L.nc:L.nc + n], seq_lens=a[L.sl:L.sl + n],
+                    block_table=a[L.bt:L.bt + n * self.stride].reshape(n, self.stride),
+                    token_ids=self._tok[i][:st.num_tokens],
+                    copy_pairs=a[L.cp:L.cp + 2 * st.num_copies].reshape(-1, 2),
+                    preempted=self._pre[i][:st.num_preempted],
+                    max_query_len=st.max_query_len, max_seq_len=st.max_seq_len,
+                    buffer=i, arena_len=L.used(n))
 
     def update(self, sampled) -> List[int]:
         s = np.ascontiguousarray(sampled, dtype=np.int32)
@@ -203,7 +242,9 @@ class Scheduler:
 
     def request(self, request_id: int) -> dict:
         info = _ReqInfo()
-        blocks = np.empty(self.stride + 1, np.int32)
+        _check("pa_sched_get_request", lib.pa_sched_get_request(
+            self._h, request_id, ctypes.byref(info), None, 0))
+        blocks = np.empty(max(info.num_blocks, 1), np.int32)
         _check("pa_sched_get_request", lib.pa_sched_get_request(
             self._h, request_id, ctypes.byref(info), blocks.ctypes.data, blocks.size))
         d = {k: getattr(info, k) for k, _ in _ReqInfo._fields_}
@@ -212,8 +253,10 @@ class Scheduler:
         return d
 
     def free_queue(self) -> List[int]:
-        out = np.empty(self.num_blocks, np.int32)
         n = _i32()
+        _check("pa_sched_get_free_queue", lib.pa_sched_get_free_queue(
+            self._h, None, 0, ctypes.byref(n)))
+        out = np.empty(max(n.value, 1), np.int32)
         _check("pa_sched_get_free_queue", lib.pa_sched_get_free_queue(
             self._h, out.ctypes.data, out.size, ctypes.byref(n)))
         return out[:n.value].tolist()

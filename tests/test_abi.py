@@ -192,3 +192,24 @@ def test_single_hip_runtime_in_process():
     out = subprocess.run(["python", "-c", code], capture_output=True, text=True, cwd=ROOT,
                          check=True).stdout.strip()
     assert out == "1"
+
+
+def test_engine_checks():
+    """pa_engine_* validate their arguments before touching the GPU."""
+    from paged_kv_attention_07_amd.engine import _Geometry
+    from paged_kv_attention_07_amd.sched import _Config
+    cfg = _Config(64, 16, 256, 8, 1024, 0, 1, 1)
+    geo = _Geometry(32, 8, 128, 1, 0.088, 0)
+    size = lib.pa_engine_device_bytes(ctypes.byref(cfg), ctypes.byref(geo))
+    assert size > 0 and size % 256 == 0
+    bad_cfg = _Config(64, 8, 256, 8, 1024, 0, 1, 1)            # block size 8
+    assert lib.pa_engine_device_bytes(ctypes.byref(bad_cfg), ctypes.byref(geo)) == 0
+    bad_geo = _Geometry(32, 8, 96, 1, 0.088, 0)                # head_dim 96
+    assert lib.pa_engine_device_bytes(ctypes.byref(cfg), ctypes.byref(bad_geo)) == 0
+    h = ctypes.c_void_p()
+    assert lib.pa_engine_create(ctypes.byref(cfg), ctypes.byref(geo), None, FAKE_WS, size,
+                                ctypes.byref(h)) == INVALID
+    assert lib.pa_engine_create(ctypes.byref(cfg), ctypes.byref(geo), FAKE, FAKE_WS, 16,
+                                ctypes.byref(h)) == WORKSPACE
+    assert lib.pa_engine_create(ctypes.byref(cfg), ctypes.byref(geo), FAKE,
+                                ctypes.c_void_p(0x100010), size, ctypes.byref(h)) == INVALID

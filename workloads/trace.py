@@ -108,7 +108,7 @@ TRACES = {
                            prompt_len=(5, 90), max_new=(1, 50), arrival_steps=50,
                            enable_prefix_caching=False, long_prefill_token_threshold=20),
     # serving-shaped: Llama-3-8B layer, 2048-token budget, system prompts
-    "serve_llama3_2k": dict(seed=3101, num_requests=256, num_steps=200, num_blocks=20000,
+    "serve_llama3_2k": dict(seed=3101, num_requests=256, num_steps=600, num_blocks=20000,
                             max_num_batched_tokens=2048, max_num_seqs=128, max_model_len=4096,
                             prompt_len=(64, 1536), max_new=(16, 256), num_prefixes=8,
                             prefix_len=(256, 1024), prefix_share=0.5, arrival_steps=60,
@@ -116,5 +116,19 @@ TRACES = {
 }
 
 
+TRACES["engine_small"] = dict(TRACES["sched_small"], seed=3201, num_requests=36)
+
+
 def trace(name: str) -> Trace:
     return make_trace(name, **TRACES[name])
+
+
+def step_inputs(seed: int, step: int, num_tokens: int, num_q_heads: int, num_kv_heads: int,
+                head_dim: int, dtype: str):
+    """q [T, Hq, D], k / v [T, Hkv, D] storage bits for one engine step (the
+    stand-ins for a model's projections), seeded by (seed, step)."""
+    from .gen import _normal
+    rng = np.random.default_rng(np.random.SeedSequence([seed, 0x57E9, step]))
+    return (_normal(rng, (num_tokens, num_q_heads, head_dim), dtype),
+            _normal(rng, (num_tokens, num_kv_heads, head_dim), dtype),
+            _normal(rng, (num_tokens, num_kv_heads, head_dim), dtype))
