@@ -355,7 +355,7 @@ def measure_serve(name: str = "serve_llama3_2k"):
                      num_kv_heads=Hkv, head_dim=D, dtype="bf16")
         host_s, tokens, steps, gpu_ms = 0.0, 0, 0, []
         events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                  for _ in range(64)]
+                  for _ in range(t.num_steps)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for step in range(t.num_steps):
@@ -364,7 +364,7 @@ def measure_serve(name: str = "serve_llama3_2k"):
             for parent, child, n in t.forks.get(step, []):
                 eng.fork(parent, child, n)
             h0 = time.perf_counter()
-            e0, e1 = events[steps % len(events)]
+            e0, e1 = events[steps]
             e0.record()
             st = eng.step(*dev)
             e1.record()
@@ -377,11 +377,10 @@ def measure_serve(name: str = "serve_llama3_2k"):
             host_s += time.perf_counter() - h0
             tokens += st.num_tokens
             steps += 1
-            if steps % len(events) == 0:
-                gpu_ms.extend(a.elapsed_time(b) for a, b in events)
+
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        gpu_ms.extend(a.elapsed_time(b) for a, b in events[:steps % len(events)])
+        gpu_ms.extend(a.elapsed_time(b) for a, b in events[:steps])
         stats = eng.stats()
         eng.close()
         del eng
@@ -423,7 +422,9 @@ def main():
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     rot = 4
-    names = [args.only] if args.only else ["decode", "mixed", "chunk"] + (
+    # the headline is always the decode batch; --only adds one more leg
+    names = ["decode"] + ([args.only] if args.only not in (None, "decode") else []) if args.only \
+        else ["decode", "mixed", "chunk"] + (
         ["prefix", "long", "prefill2k", "prefill8k", "prefillbatch"] if args.extra else [])
     copy_lines, serve_line = [], None
     if args.only == "copy" or (args.extra and not args.only):
@@ -432,6 +433,7 @@ def main():
         serve_line = measure_serve()
     if args.only in ("copy", "serve"):
         names = ["decode"]
+    names = [n for n in names if n in WORKLOADS]
     results = {k: measure(WORKLOADS[k], args, rot if k != "long" else 2) for k in names}
 
     head = results.get("decode") or next(iter(results.values()))

@@ -8,7 +8,9 @@
  *
  * Conventions shared by every entry point
  *   - Pointers are DEVICE pointers owned by the caller unless marked (host).
- *     The library keeps no pointer after a call returns and never allocates.
+ *     The library keeps no pointer after a call returns and never allocates
+ *     memory; pa_attention_mixed keeps one side stream and two events per
+ *     device, created on its first use there.
  *   - Every call is asynchronous on `stream` (a hipStream_t passed as void*;
  *     NULL = the default stream) and never synchronises.
  *   - Tensors are dense, row-major, with the shapes given below.
@@ -120,7 +122,8 @@ int pa_copy_blocks(void* kv_cache, const int32_t* block_pairs, int32_t num_pairs
  * need for their split-KV partial results (max, sum, unnormalised output per
  * query head and partition).  Pure function of its arguments; returns 0 for
  * arguments the attention calls would reject.  `num_splits` = 0 selects the
- * library's own partition count (the same value the attention call uses).
+ * library's own partition count; the size covers every plan the attention
+ * calls may choose for these arguments.
  */
 size_t pa_attention_workspace_size(int32_t num_seqs, int32_t num_tokens,
                                    int32_t num_q_heads, int32_t num_kv_heads,
@@ -168,7 +171,12 @@ int pa_attention_decode(void* out, const void* q, const void* kv_cache,
  *   position pos = num_computed_tokens[r] + i; it attends keys 0..pos:
  *     out[t][h] = sum_{j<=pos} softmax_j(scale * <q[t][h], K_j>) * V_j.
  *   Requests with one query take the decode path; longer ones the MFMA
- *   tile path with a causal mask.
+ *   tile path with a causal mask.  When the batch has a chunk and at least
+ *   one other request, the tiles run on a library-owned side stream,
+ *   concurrently with the decode rows (one decode wave and one tile wave per
+ *   SIMD), forked from and joined back into `stream` with events, so stream
+ *   order is kept for the caller.  PA_MIXED_OVERLAP=0 in the environment
+ *   runs both on `stream` instead.
  *
  *   out, q              [num_tokens, num_q_heads, head_dim], cache dtype.
  *   seq_lens            [num_seqs]: keys of the request's last query,

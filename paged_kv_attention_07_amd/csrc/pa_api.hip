@@ -2,6 +2,9 @@
 // The public contract of every function is documented in include/pa.h.
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
+
+#include <mutex>
 
 #include "pa.h"
 #include "pa_kernels.h"
@@ -12,7 +15,11 @@ constexpr int kVersion = 100;  // 0.1.0
 
 // Partition plan for the balanced split: enough wavefronts to fill the chip
 // (256 CUs, ~8 resident waves each), but no range shorter than a few blocks.
+// Beside concurrent prefill tiles the decode rows take one wave per SIMD, so
+// each SIMD holds one bandwidth-bound decode wave and one compute-bound tile
+// wave.
 constexpr int kTargetWaves = 256 * 8;
+constexpr int kTargetWavesBesidePrefill = 256 * 4;
 constexpr int kMinBlocksPerRange = 4;
 
 int heads_per_wave(int group) { return group < 4 ? group : 4; }
@@ -27,11 +34,21 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-int plan_chunks(int num_seqs, int num_kv_heads, int group, int max_seq_len, int num_splits) {
+bool overlap_enabled();
+
+// Prefill tiles run beside the decode rows when the batch can hold both: a
+// chunk (max_query_len > 1) and at least one other request.
+bool tiles_beside_decode(int num_seqs, int max_query_len) {
+  return max_query_len > 1 && num_seqs >= 2 && overlap_enabled();
+}
+
+int plan_chunks(int num_seqs, int num_kv_heads, int group, int max_seq_len, int num_splits,
+                bool beside_prefill) {
   if (num_splits > 0) return num_splits;
   const int hg = group / heads_per_wave(group);
   const int64_t blocks_upper = (int64_t)num_seqs * ceil_div(max_seq_len, pa::kBlockSize);
-  int64_t n = ceil_div(kTargetWaves, (int64_t)num_kv_heads * hg);
+  const int waves = beside_prefill ? kTargetWavesBesidePrefill : kTargetWaves;
+  int64_t n = ceil_div(waves, (int64_t)num_kv_heads * hg);
   const int64_t cap = ceil_div(blocks_upper, kMinBlocksPerRange);
   if (n > cap) n = cap;
   if (n < 1) n = 1;
@@ -73,6 +90,40 @@ int check_heads(int32_t num_q_heads, int32_t num_kv_heads) {
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
+
+// Side stream for the prefill tiles of a mixed batch, one per device,
+// created on first use: the compute-bound tiles run concurrently with the
+// bandwidth-bound decode rows, forked from and joined back into the caller's
+// stream with two events.  The mutex makes the fork/join enqueue atomic when
+// several host threads call at once.
+struct SideStream {
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int kMaxDevices = 64;
+std::mutex g_side_mu;
+SideStream g_side[kMaxDevices];
+
+// caller holds g_side_mu
+hipError_t side_stream(SideStream** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  SideStream& s = g_side[dev];
+  if (!s.stream) {
+    if ((e = hipStreamCreateWithFlags(&s.stream, hipStreamNonBlocking)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&s.fork, hipEventDisableTiming)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&s.join, hipEventDisableTiming)) != hipSuccess) return e;
+  }
+  *out = &s;
+  return hipSuccess;
+}
+
+bool overlap_enabled() {
+  const char* v = getenv("PA_MIXED_OVERLAP");
+  return !(v && v[0] == '0');
+}
 
 }  // namespace
 
@@ -139,12 +190,14 @@ size_t pa_attention_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t
                                    int32_t num_kv_heads, int32_t head_dim, int32_t max_seq_len,
                                    int32_t max_query_len, int32_t num_splits) {
   (void)num_tokens;
-  (void)max_query_len;
   if (num_seqs <= 0 || num_kv_heads <= 0 || max_seq_len <= 0 || num_splits < 0) return 0;
   if (head_dim != 64 && head_dim != 128) return 0;
   if (check_heads(num_q_heads, num_kv_heads) != PA_OK) return 0;
   const int group = num_q_heads / num_kv_heads;
-  const int chunks = plan_chunks(num_seqs, num_kv_heads, group, max_seq_len, num_splits);
+  (void)max_query_len;
+  // the plan without concurrent tiles has the most ranges: size for it, so the
+  // buffer covers either plan
+  const int chunks = plan_chunks(num_seqs, num_kv_heads, group, max_seq_len, num_splits, false);
   return workspace_layout(num_seqs, num_q_heads, head_dim, chunks).total;
 }
 
@@ -153,7 +206,8 @@ static int attention_common(void* out, const void* q, const void* kv_cache, int6
                             int32_t dtype, const int32_t* block_table, int32_t bt_stride,
                             const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len,
                             int32_t num_q_heads, float scale, void* workspace,
-                            size_t workspace_bytes, int32_t num_splits, pa::DecodeArgs* a) {
+                            size_t workspace_bytes, int32_t num_splits, int32_t max_query_len,
+                            pa::DecodeArgs* a) {
   int st = check_cache(kv_cache, num_blocks, block_size, num_kv_heads, head_dim, dtype);
   if (st != PA_OK) return st;
   st = check_heads(num_q_heads, num_kv_heads);
@@ -166,7 +220,8 @@ static int attention_common(void* out, const void* q, const void* kv_cache, int6
   if (max_seq_len == 0) return PA_OK;
   if (bt_stride < ceil_div(max_seq_len, pa::kBlockSize)) return PA_ERR_INVALID_ARG;
   const int group = num_q_heads / num_kv_heads;
-  const int chunks = plan_chunks(num_seqs, num_kv_heads, group, max_seq_len, num_splits);
+  const int chunks = plan_chunks(num_seqs, num_kv_heads, group, max_seq_len, num_splits,
+                                 tiles_beside_decode(num_seqs, max_query_len));
   const WsLayout lay = workspace_layout(num_seqs, num_q_heads, head_dim, chunks);
   if (!workspace || workspace_bytes < lay.total) return PA_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return PA_ERR_WORKSPACE;
@@ -201,7 +256,7 @@ int pa_attention_decode(void* out, const void* q, const void* kv_cache, int64_t 
   const int st = attention_common(out, q, kv_cache, num_blocks, block_size, num_kv_heads, head_dim,
                                   dtype, block_table, block_table_stride, seq_lens, num_seqs,
                                   max_seq_len, num_q_heads, scale, workspace, workspace_bytes,
-                                  num_splits, &a);
+                                  num_splits, 1, &a);
   if (st <= 0) return st;
   return hip_status(pa::launch_decode(a, dtype, head_dim, num_q_heads / num_kv_heads,
                                       static_cast<hipStream_t>(stream)));
@@ -220,7 +275,7 @@ int pa_attention_mixed(void* out, const void* q, const void* kv_cache, int64_t n
   const int st = attention_common(out, q, kv_cache, num_blocks, block_size, num_kv_heads, head_dim,
                                   dtype, block_table, block_table_stride, seq_lens, num_seqs,
                                   max_seq_len, num_q_heads, scale, workspace, workspace_bytes,
-                                  num_splits, &a);
+                                  num_splits, max_query_len, &a);
   if (st <= 0) return st;
   if (num_tokens == 0) return PA_OK;
   if (!query_start_loc || !num_computed_tokens) return PA_ERR_INVALID_ARG;
@@ -228,6 +283,7 @@ int pa_attention_mixed(void* out, const void* q, const void* kv_cache, int64_t n
   if (max_query_len > 1 && !pa::prefill_supported(dtype, head_dim, group))
     return PA_ERR_UNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  a.qsl = query_start_loc;
   if (max_query_len > 1) {
     pa::PrefillArgs p{};
     p.out = out;
@@ -244,10 +300,24 @@ int pa_attention_mixed(void* out, const void* q, const void* kv_cache, int64_t n
     p.max_tiles = (int)(ceil_div(num_tokens, pa::kQueriesPerTile) + num_seqs);
     p.max_query_len = max_query_len;
     p.scale_log2 = a.scale_log2;
+    if (tiles_beside_decode(num_seqs, max_query_len)) {
+      p.beside_decode = 1;
+      // fork: tiles on the side stream, decode rows on the caller's; join
+      std::lock_guard<std::mutex> lock(g_side_mu);
+      SideStream* side = nullptr;
+      hipError_t e = side_stream(&side);
+      if (e == hipSuccess) e = hipEventRecord(side->fork, s);
+      if (e == hipSuccess) e = hipStreamWaitEvent(side->stream, side->fork, 0);
+      if (e == hipSuccess) e = pa::launch_prefill(p, dtype, head_dim, group, side->stream);
+      if (e == hipSuccess) e = hipEventRecord(side->join, side->stream);
+      if (e != hipSuccess) return PA_ERR_HIP;
+      const hipError_t ed = pa::launch_decode(a, dtype, head_dim, group, s);
+      e = hipStreamWaitEvent(s, side->join, 0);  // joined whatever the decode launch did
+      return hip_status(ed != hipSuccess ? ed : e);
+    }
     const hipError_t e = pa::launch_prefill(p, dtype, head_dim, group, s);
     if (e != hipSuccess) return PA_ERR_HIP;
   }
-  a.qsl = query_start_loc;
   return hip_status(pa::launch_decode(a, dtype, head_dim, group, s));
 }
 

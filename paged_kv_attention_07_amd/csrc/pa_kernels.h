@@ -44,6 +44,7 @@ struct PrefillArgs {
   int32_t num_q_heads;
   int32_t max_tiles;          // upper bound on the tile count (grid size)
   int32_t max_query_len;      // (host) longest chunk: picks the tile shape
+  int32_t beside_decode;      // (host) 1: runs concurrently with decode rows
   float scale_log2;
 };
 

@@ -431,16 +431,18 @@ __global__ __launch_bounds__(256 * KSPLIT) __attribute__((amdgpu_waves_per_eu(2,
 }
 
 // Tile shape of a launch: NT = 2 (32 tokens per wave, one key part) for long
-// chunks, NT = 1 with two key parts for short ones, which would leave most of
-// the chip idle otherwise.  PA_PREFILL_TOKENS_PER_WAVE=16|32 overrides the
-// choice (a tuning and testing knob).
+// chunks and when the tiles share the chip with concurrent decode rows (a
+// 4-wave work-group of 254 VGPRs per wave fits beside one decode wave per
+// SIMD); NT = 1 with two key parts for short chunks alone, which would leave
+// most of the chip idle otherwise.  PA_PREFILL_TOKENS_PER_WAVE=16|32
+// overrides the choice (a tuning and testing knob).
 int choose_nt(const PrefillArgs& a) {
   if (const char* env = getenv("PA_PREFILL_TOKENS_PER_WAVE")) {
     const int v = atoi(env);
     if (v == 16) return 1;
     if (v == 32) return 2;
   }
-  return a.max_query_len >= 1024 ? 2 : 1;
+  return (a.max_query_len >= 1024 || a.beside_decode) ? 2 : 1;
 }
 
 template <typename E, int D, int WPW, int NT, int KSPLIT>

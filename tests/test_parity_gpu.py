@@ -419,3 +419,16 @@ def test_copy_on_write_parallel_sampling():
     ref = oracle.paged_attention(w.q, r_pool, tables, w.seq_lens, w.query_start_loc,
                                  w.num_computed, w.scale, "bf16")
     gu.check_close(w, out, ref, what="cow samples")
+
+
+@pytest.mark.parametrize("overlap", ["0", "1"])
+def test_mixed_with_and_without_concurrent_tiles(overlap, monkeypatch):
+    """The mixed entry runs prefill tiles on a side stream beside the decode
+    rows by default; both schedules give the oracle's rows, including the
+    one-request batch (no side stream) and a repeat on the same buffers."""
+    monkeypatch.setenv("PA_MIXED_OVERLAP", overlap)
+    full_check(workload("mixed_bf16_small"))
+    lens = [300, 40, 129, 2000, 17]
+    q_lens = [100, 1, 64, 1, 1]
+    full_check(_variant("bf16", 32, 8, 128, lens, seed=91, q_lens=q_lens))
+    full_check(_variant("f16", 8, 2, 64, [77], seed=92, q_lens=[60]))
