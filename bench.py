@@ -422,9 +422,7 @@ def main():
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     rot = 4
-    # the headline is always the decode batch; --only adds one more leg
-    names = ["decode"] + ([args.only] if args.only not in (None, "decode") else []) if args.only \
-        else ["decode", "mixed", "chunk"] + (
+    names = [args.only] if args.only else ["decode", "mixed", "chunk"] + (
         ["prefix", "long", "prefill2k", "prefill8k", "prefillbatch"] if args.extra else [])
     copy_lines, serve_line = [], None
     if args.only == "copy" or (args.extra and not args.only):
@@ -436,11 +434,33 @@ def main():
     names = [n for n in names if n in WORKLOADS]
     results = {k: measure(WORKLOADS[k], args, rot if k != "long" else 2) for k in names}
 
-    head = results.get("decode") or next(iter(results.values()))
+    # the headline is the decode batch; with --only <leg> it is that leg, with
+    # the roofline of the kernel that dominates it
+    head_key = "decode" if "decode" in results else next(iter(results))
+    head = results[head_key]
     w, c = head["w"], head["counts"]
     step_bytes = c["attn_logical"] + c["scatter"] + c["slots"]
     value = step_bytes / (head["ms_step"] * 1e-3) / 1e9
     achieved = c["attn_logical"] / (head["attn_ms_avg"] * 1e-3) / 1e9
+    launch = {"avg_launch_us": round(head["attn_ms_avg"] * 1e3, 2),
+              "p10_us": round(head["attn_ms_p10"] * 1e3, 2),
+              "p90_us": round(head["attn_ms_p90"] * 1e3, 2)}
+    if head_key in ("chunk", "prefill2k", "prefill8k", "prefillbatch"):
+        tflops = c["chunk_flops"] / (head["attn_ms_avg"] * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(tflops, 1),
+                    "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                    "kernel": "pa_attention_mixed (prefill_tile_kernel)",
+                    "alg_flops_per_launch": int(c["chunk_flops"]), **launch}
+    else:
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "traffic": recorded_traffic("decode_split_kernel")
+                    if head_key == "decode" else None,
+                    "traffic_kernel": "decode_split_kernel (profiles/traffic.json)",
+                    "kernel": "pa_attention_decode (decode_split_kernel + decode_merge_kernel)"
+                    if head_key == "decode" else "pa_attention_mixed",
+                    "alg_bytes_per_launch": int(c["attn_logical"]), **launch}
     line = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -460,17 +480,7 @@ def main():
                    "step": "slot_mapping + reshape_and_cache + attention",
                    "pool_rotation": rot, "num_splits": args.splits or "auto"},
         "pct_peak_hbm": round(100 * value / HBM_PEAK_GBS, 2),
-        "roofline": {
-            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": recorded_traffic("decode_split_kernel"),
-            "traffic_kernel": "decode_split_kernel (profiles/traffic.json)",
-            "kernel": "pa_attention_decode (decode_split_kernel + decode_merge_kernel)",
-            "alg_bytes_per_launch": int(c["attn_logical"]),
-            "avg_launch_us": round(head["attn_ms_avg"] * 1e3, 2),
-            "p10_us": round(head["attn_ms_p10"] * 1e3, 2),
-            "p90_us": round(head["attn_ms_p90"] * 1e3, 2),
-        },
+        "roofline": roofline,
         "gpu": gpu_info(),
     }
     if "mixed" in results:
