@@ -13,10 +13,11 @@
 // of the KV head over the same tokens, so each K/V tile staged in LDS feeds 4
 // heads.  A wave covers NT sub-tiles of 16 tokens: with NT = 2 every K and V
 // fragment read from LDS feeds two matrix-core products.  Keys are processed
-// 64 at a time (four 16-token blocks looked up in the block table), staged in
-// double-buffered LDS with global loads two iterations ahead.  With KSPLIT = 2
-// the parts split the tile's key range and are merged through LDS at the end
-// (more waves for chunks too short to fill the chip).
+// 64 at a time (four 16-token blocks looked up in the block table), copied
+// from HBM straight into double-buffered LDS by the load unit (16 bytes per
+// lane, no registers), one iteration ahead.  With KSPLIT = 2 the parts split
+// the tile's key range and are merged through LDS at the end (more waves for
+// chunks too short to fill the chip).
 //
 // Matrix-core mapping (v_mfma_f32_16x16x32_{bf16,f16}).  Scores are formed
 // transposed, S^T = K Q^T (keys x tokens), because the accumulator layout of
@@ -24,9 +25,12 @@
 // operand layout the second product O^T = V^T P^T needs for P^T, so the
 // probabilities go from the softmax to the matrix core without moving across
 // lanes.  Each lane then holds the output of one token, so the online-softmax
-// rescale is a per-lane scalar.  V is written transposed into LDS (pairs of
-// keys per 32-bit word) while it is staged.  The contraction order inside an
-// MFMA is a permutation of the keys; A and B use the same permutation.
+// rescale is a per-lane scalar.  K and V keep their cache layout in LDS
+// (a 16-byte column swizzle per row keeps the reads free of bank
+// conflicts); V^T fragments are read with the transposing LDS read
+// (ds_read_b64_tr_b16: each lane gets 4 keys of one head dimension).  The
+// contraction order inside an MFMA is a permutation of the keys; A and B
+// use the same permutation.
 #include <math.h>
 #include <stdlib.h>
 
@@ -58,14 +62,25 @@ constexpr int kKeysPerIter = 64;  // keys staged per iteration (4 paged blocks)
 template <int D>
 struct TileShape {
   static constexpr int ROWB = D * 2;                 // bytes of one token's head row
-  static constexpr int KROW = ROWB + 16;             // padded LDS row of K
-  static constexpr int VROW = kKeysPerIter * 2 + 8;  // padded LDS row of V^T
+  static constexpr int CPR = ROWB / 16;              // 16-byte columns per row
+  static constexpr int RPG = 256 / ROWB;             // rows per 256 bytes (64 banks)
+  static constexpr int RPI = 1024 / ROWB;            // rows per 1 KiB wave copy
   static constexpr int NKS = D / 32;                 // MFMA k-steps of Q K^T
   static constexpr int NMT = D / 16;                 // 16-dim tiles of the output
-  static constexpr int KBUF = kKeysPerIter * KROW;
-  static constexpr int VBUF = D * VROW;
-  static constexpr int STAGE = KBUF + VBUF;          // one LDS stage: K then V^T
+  static constexpr int KBUF = kKeysPerIter * ROWB;
+  static constexpr int STAGE = 2 * KBUF;             // one LDS stage: K rows then V rows
+  // Physical 16-byte column of logical column c in LDS row `row`.  K is read
+  // 16 rows x one column at a time (16 bytes per lane): fk spreads those 16
+  // reads over all 64 banks.  V is read 8 rows x two adjacent columns at a
+  // time (8 bytes per lane): fv spreads those 16 pieces over all banks.
+  static __device__ __forceinline__ int fk(int row) { return (row / RPG) % CPR; }
+  static __device__ __forceinline__ int fv(int row) { return 2 * ((row / RPG) % (CPR / 2)); }
 };
+
+// Zero row: the copy source for key rows past the tile's last key, so that
+// those rows hold zeros (V must not carry a stale NaN into a product with a
+// zero probability).
+__device__ __attribute__((aligned(256))) uint8_t g_zero_row[256];
 
 // Tokens per tile for a launch configuration.
 template <int WPW, int NT>
@@ -77,9 +92,13 @@ template <typename E, int D, int WPW, int NT, int KSPLIT>
 __global__ __launch_bounds__(256 * KSPLIT) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_tile_kernel(PrefillArgs a) {
   using S = TileShape<D>;
   constexpr int QT = tile_tokens<WPW, NT>();   // tokens per tile
-  // [part][stage]: the next 64 keys of each part are staged while the
-  // current ones are used
-  __shared__ __attribute__((aligned(16))) uint8_t lds[KSPLIT][2][S::STAGE];
+  // [part][stage]: each part's next 64 keys are copied in while the current
+  // ones are used.  Two stages keep a 4-wave work-group at 64 KiB of LDS, so
+  // two work-groups share a CU and their barriers do not couple (a third
+  // stage, or 8-wave groups sharing the stages, left one group per CU and
+  // measured slower).
+  constexpr int NSTAGE = 2;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[KSPLIT][NSTAGE][S::STAGE];
   __shared__ int s_tile[2];
 
   const int tid = threadIdx.x;
@@ -175,84 +194,37 @@ __global__ __launch_bounds__(256 * KSPLIT) __attribute__((amdgpu_waves_per_eu(2,
     return lb < nb_need ? load_scalar(bt + lb) : 0;
   };
 
-  // Staging: wavefront w4 of a part moves paged block w4 of the part's
+  // Staging: wavefront w4 of a part copies paged block w4 of the part's
   // iteration (keys 16 w4 .. 16 w4 + 15), so its block id is wave-uniform.
-  // K rows go to LDS unchanged (lane l, step i: key (64 i + l) / CPR, 16-byte
-  // column l % CPR).  V goes in transposed, two keys per 32-bit word: lane l,
-  // step i handles key pair l % 8 and 8-dim column 8 i + l / 8, so the lanes
-  // of one store write consecutive words.
-  constexpr int CPR = S::ROWB / 16;            // 16-byte columns per row
-  constexpr int KPT = 16 * CPR / kWave;        // K pieces per lane per block
-  constexpr int VPT = (D / 8) / 8;             // V column groups per lane per block
-  struct Regs {
-    u32x4_t k[KPT], v[VPT][2];
-  };
-  // Per-lane byte offsets inside a block (32-bit): with the block base
-  // wave-uniform, every load is scalar base + vector offset.
-  uint32_t koff[KPT], voff[VPT][2];
+  // Each 1 KiB copy moves RPI rows: lane l lands at LDS byte 16 l of the
+  // copy, so it fetches row l / CPR at the global column that the row's
+  // swizzle puts in slot l % CPR.
+  constexpr int CPB = 16 * S::ROWB / 1024;     // copies per block half
+  uint32_t goff[2][CPB];                       // per-lane byte offset inside a block
+  uint32_t zoff[2][CPB];                       // the same column in the zero row
 #pragma unroll
-  for (int i = 0; i < KPT; ++i) {
-    const int c = i * kWave + lane;
-    koff[i] = (uint32_t)((c / CPR) * tok_stride + (c % CPR) * 16);
-  }
+  for (int hv = 0; hv < 2; ++hv)
 #pragma unroll
-  for (int i = 0; i < VPT; ++i)
-#pragma unroll
-    for (int e = 0; e < 2; ++e)
-      voff[i][e] = (uint32_t)(half_stride + (2 * (lane & 7) + e) * tok_stride +
-                              (8 * i + (lane >> 3)) * 16);
-  // Loads are issued unconditionally (every address stays inside a real
-  // block: ids past the table's end read block 0, rows past kend read their
-  // own block) and keys past kend are zeroed when staged, so the compiler can
-  // wait for exactly the loads a stage needs.
-  auto fetch = [&](Regs& R, int phys) {
+    for (int i = 0; i < CPB; ++i) {
+      const int rib = S::RPI * i + lane / S::CPR;       // row in block
+      const int row = 16 * w4 + rib;                    // row in stage
+      const int col = (lane % S::CPR) ^ (hv ? S::fv(row) : S::fk(row));
+      goff[hv][i] = (uint32_t)(hv * half_stride + rib * tok_stride + col * 16);
+      zoff[hv][i] = (uint32_t)(col * 16);
+    }
+  auto dma = [&](int it, int phys, int buf) {
     const uint8_t* blk = kvh + (int64_t)phys * blk_stride;
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) R.k[i] = load16(blk + koff[i]);
-#pragma unroll
-    for (int i = 0; i < VPT; ++i)
-#pragma unroll
-      for (int e = 0; e < 2; ++e) R.v[i][e] = load16(blk + voff[i][e]);
-  };
-  // LDS offsets of this lane's staged pieces
-  uint32_t kdst[KPT], vdst[VPT];
-#pragma unroll
-  for (int i = 0; i < KPT; ++i) {
-    const int c = i * kWave + lane;
-    kdst[i] = (uint32_t)((16 * w4 + c / CPR) * S::KROW + (c % CPR) * 16);
-  }
-#pragma unroll
-  for (int i = 0; i < VPT; ++i)
-    vdst[i] = (uint32_t)(S::KBUF + (8 * (8 * i + (lane >> 3))) * S::VROW +
-                         4 * (8 * w4 + (lane & 7)));
-  auto stage = [&](Regs& R, int it, int buf) {
-    uint8_t* st = lds[part][buf];
     const int key0 = it * kKeysPerIter + 16 * w4;
-    if (key0 + 16 > kend) {
-      // the block crosses the tile's last visible key: zero what lies past it
-      const u32x4_t z = {0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int i = 0; i < KPT; ++i)
-        R.k[i] = key0 + (i * kWave + lane) / CPR < kend ? R.k[i] : z;
-      const bool ok0 = key0 + 2 * (lane & 7) < kend, ok1 = key0 + 2 * (lane & 7) + 1 < kend;
+    for (int hv = 0; hv < 2; ++hv) {
 #pragma unroll
-      for (int i = 0; i < VPT; ++i) {
-        R.v[i][0] = ok0 ? R.v[i][0] : z;
-        R.v[i][1] = ok1 ? R.v[i][1] : z;
+      for (int i = 0; i < CPB; ++i) {
+        const int rib = S::RPI * i + lane / S::CPR;
+        const uint8_t* src = key0 + rib < kend ? blk + goff[hv][i] : g_zero_row + zoff[hv][i];
+        uint8_t* dst = &lds[part][buf][hv * S::KBUF + (16 * w4 + S::RPI * i) * S::ROWB];
+        __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
       }
     }
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) *reinterpret_cast<u32x4_t*>(st + kdst[i]) = R.k[i];
-#pragma unroll
-    for (int i = 0; i < VPT; ++i)
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        // dims 8dc + 2w (lo) and 8dc + 2w + 1 (hi), keys 2kp and 2kp + 1
-        *reinterpret_cast<uint32_t*>(st + vdst[i] + (2 * w) * S::VROW) =
-            pair_lo(R.v[i][0][w], R.v[i][1][w]);
-        *reinterpret_cast<uint32_t*>(st + vdst[i] + (2 * w + 1) * S::VROW) =
-            pair_hi(R.v[i][0][w], R.v[i][1][w]);
-      }
   };
 
   f32x4_t acc[NT][S::NMT];
@@ -277,8 +249,9 @@ __global__ __launch_bounds__(256 * KSPLIT) __attribute__((amdgpu_waves_per_eu(2,
       for (int j = 0; j < NT; ++j) st[j][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < S::NKS; ++s) {
+        const int row = 16 * tt + n;
         const u32x4_t ka = *reinterpret_cast<const u32x4_t*>(
-            lds_kc + (16 * tt + n) * S::KROW + s * 64 + g * 16);
+            lds_kc + row * S::ROWB + (((4 * s + g) ^ S::fk(row)) << 4));
 #pragma unroll
         for (int j = 0; j < NT; ++j) st[j][tt] = mfma16x16x32<E>(ka, qf[j][s], st[j][tt]);
       }
@@ -340,39 +313,46 @@ __global__ __launch_bounds__(256 * KSPLIT) __attribute__((amdgpu_waves_per_eu(2,
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
       for (int mt = 0; mt < S::NMT; ++mt) {
-        const uint8_t* vp = lds_vc + (16 * mt + n) * S::VROW + (32 * s2 + 4 * g) * 2;
-        const uint2 lo = *reinterpret_cast<const uint2*>(vp);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vp + 32);
-        const u32x4_t va = {lo.x, lo.y, hi.x, hi.y};
+        // lane (n, g): dim 16 mt + n, keys 32 s2 + 4 g + (0..3) and
+        // 32 s2 + 16 + 4 g + (0..3); the transposing read hands lane
+        // 4 q + c of each 16-lane group element c of the 8 bytes that lane
+        // 4 i + q points at, for i = 0..3 (i = key, q = dim quad)
+        const int e = 4 * mt + (n & 3);                  // 8-byte piece (4 dims)
+        u32x4_t va;
+#pragma unroll
+        for (int hv = 0; hv < 2; ++hv) {
+          const int row = 32 * s2 + 16 * hv + 4 * g + (n >> 2);
+          const uint8_t* vp = lds_vc + row * S::ROWB + ((((e >> 1) ^ S::fv(row)) << 4) | ((e & 1) << 3));
+          typedef short v4s_t __attribute__((ext_vector_type(4)));
+          const v4s_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4s_t*)(vp));
+          const uint2 w = __builtin_bit_cast(uint2, t);
+          va[2 * hv] = w.x;
+          va[2 * hv + 1] = w.y;
+        }
 #pragma unroll
         for (int j = 0; j < NT; ++j) acc[j][mt] = mfma16x16x32<E>(va, pb[j][s2], acc[j][mt]);
       }
   };
 
-  // Every part runs n0 loop trips in lockstep (one barrier per trip); a part
-  // with fewer iterations idles on its last trip.  Trip t computes iteration
-  // it_begin + t from LDS stage t & 1, issues the loads of iteration
-  // it_begin + t + 2 into register set t & 1, and stages iteration
-  // it_begin + t + 1 from the other set (loaded one trip earlier).
-  Regs R0, R1;
-  fetch(R0, block_id(it_begin));
-  if (my_iters > 0) stage(R0, it_begin, 0);
-  fetch(R1, block_id(it_begin + 1));
-  int id_ahead = block_id(it_begin + 2);
-  __syncthreads();
-  auto trip = [&](int t, Regs& Rload, Regs& Rstage) {
+  // Every part runs n0 loop trips in lockstep, one barrier per trip; a part
+  // with fewer iterations idles on its last trips.  Trip t waits for its own
+  // copies of iteration it_begin + t (the only loads in flight), meets the
+  // other waves at the barrier (after which every copy of that iteration has
+  // landed and every wave is done with the other stage), starts the copies
+  // of the next iteration into the other stage, and computes.
+  if (my_iters > 0) dma(it_begin, block_id(it_begin), 0);
+  int id_next = block_id(it_begin + 1);
+  for (int t = 0; t < n0; ++t) {
     const int buf = t & 1;
-    const int it = it_begin + t;
-    fetch(Rload, id_ahead);  // unconditional: past the range it reads block 0, never staged
-    id_ahead = block_id(it + 3);
-    if (t < my_iters) compute(it, buf);
-    if (t + 1 < my_iters) stage(Rstage, it + 1, buf ^ 1);
+    const int phys = id_next;
+    id_next = block_id(it_begin + t + 2);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-  };
-  for (int t = 0; t < n0; t += 2) {
-    trip(t, R0, R1);
-    if (t + 1 < n0) trip(t + 1, R1, R0);
+    if (t + 1 < my_iters) dma(it_begin + t + 1, phys, buf ^ 1);
+    if (t < my_iters) compute(it_begin + t, buf);
   }
+  if constexpr (KSPLIT == 2) __syncthreads();  // stages are reused for the merge
 
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
@@ -382,7 +362,7 @@ __global__ __launch_bounds__(256 * KSPLIT) __attribute__((amdgpu_waves_per_eu(2,
   if constexpr (KSPLIT == 2) {
     // ---- merge the parts: part 1 leaves (max, row sum, O^T) in its LDS stages
     constexpr int NF = NT * (S::NMT * 4 + 2);  // floats per lane
-    static_assert(4 * kWave * NF * 4 <= 2 * S::STAGE, "merge buffer must fit in part 1's stages");
+    static_assert(4 * kWave * NF * 4 <= NSTAGE * S::STAGE, "merge buffer must fit in part 1's stages");
     float* xch = reinterpret_cast<float*>(&lds[1][0][0]) + (w4 * kWave + lane) * NF;
     if (part == 1) {
 #pragma unroll
@@ -430,19 +410,20 @@ __global__ __launch_bounds__(256 * KSPLIT) __attribute__((amdgpu_waves_per_eu(2,
   }
 }
 
-// Tile shape of a launch: NT = 2 (32 tokens per wave, one key part) for long
-// chunks and when the tiles share the chip with concurrent decode rows (a
-// 4-wave work-group of 254 VGPRs per wave fits beside one decode wave per
-// SIMD); NT = 1 with two key parts for short chunks alone, which would leave
-// most of the chip idle otherwise.  PA_PREFILL_TOKENS_PER_WAVE=16|32
-// overrides the choice (a tuning and testing knob).
-int choose_nt(const PrefillArgs& a) {
-  if (const char* env = getenv("PA_PREFILL_TOKENS_PER_WAVE")) {
+// Tile shape of a launch.
+//   0: 16 tokens per wave, two key parts of 4 waves: short chunks alone, which
+//      would leave most of the chip idle with fewer, larger tiles;
+//   1: 32 tokens per wave, one part of 4 waves: long chunks (each K and V
+//      fragment read from LDS feeds two products), and tiles running beside
+//      concurrent decode rows (a 4-wave work-group fits next to one decode
+//      wave per SIMD).
+// PA_PREFILL_SHAPE=0|1 overrides the choice (a tuning and testing knob).
+int choose_shape(const PrefillArgs& a) {
+  if (const char* env = getenv("PA_PREFILL_SHAPE")) {
     const int v = atoi(env);
-    if (v == 16) return 1;
-    if (v == 32) return 2;
+    if (v == 0 || v == 1) return v;
   }
-  return (a.max_query_len >= 1024 || a.beside_decode) ? 2 : 1;
+  return (a.beside_decode || a.max_query_len >= 1024) ? 1 : 0;
 }
 
 template <typename E, int D, int WPW, int NT, int KSPLIT>
@@ -459,8 +440,8 @@ hipError_t launch_shape(const PrefillArgs& a, hipStream_t stream) {
 
 template <typename E, int D, int WPW>
 hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream) {
-  return choose_nt(a) == 2 ? launch_shape<E, D, WPW, 2, 1>(a, stream)
-                           : launch_shape<E, D, WPW, 1, 2>(a, stream);
+  return choose_shape(a) == 1 ? launch_shape<E, D, WPW, 2, 1>(a, stream)
+                              : launch_shape<E, D, WPW, 1, 2>(a, stream);
 }
 
 template <typename E, int D>

@@ -299,9 +299,9 @@ def sampled_rows_check(w, dev_out_bits, rows):
     return sub
 
 
-def _large_prefill_check(name, tokens_per_wave, monkeypatch):
+def _large_prefill_check(name, shape, monkeypatch):
     import dataclasses
-    monkeypatch.setenv("PA_PREFILL_TOKENS_PER_WAVE", str(tokens_per_wave))
+    monkeypatch.setenv("PA_PREFILL_SHAPE", str(shape))
     w = workload(name)
     pool = gu.poisoned_pool(w)
     dev = gu.Device(w, pool)
@@ -320,23 +320,23 @@ def _large_prefill_check(name, tokens_per_wave, monkeypatch):
     sub = sampled_rows_check(w, out, rows)
     ref = oracle.paged_attention(sub.q, r_pool, sub.block_table, sub.seq_lens,
                                  sub.query_start_loc, sub.num_computed, w.scale, w.dtype)
-    gu.check_close(w, out[rows], ref, what=f"{name}/{tokens_per_wave}")
+    gu.check_close(w, out[rows], ref, what=f"{name}/shape{shape}")
 
 
-@pytest.mark.parametrize("tokens_per_wave", [16, 32])
+@pytest.mark.parametrize("shape", [0, 1])
 @pytest.mark.parametrize("name", ["prefill_chunk_2048_bf16", "prefill_batch_4x1024_bf16"])
-def test_large_prefill_sampled(name, tokens_per_wave, monkeypatch):
-    _large_prefill_check(name, tokens_per_wave, monkeypatch)
+def test_large_prefill_sampled(name, shape, monkeypatch):
+    _large_prefill_check(name, shape, monkeypatch)
 
 
 def test_prefill_8k_sampled(monkeypatch):
-    _large_prefill_check("prefill_8192_bf16", 32, monkeypatch)
+    _large_prefill_check("prefill_8192_bf16", 1, monkeypatch)
 
 
-@pytest.mark.parametrize("tokens_per_wave", [16, 32])
-def test_mixed_both_tile_shapes(tokens_per_wave, monkeypatch):
-    """Both prefill tile shapes on the small mixed batch and on odd groupings."""
-    monkeypatch.setenv("PA_PREFILL_TOKENS_PER_WAVE", str(tokens_per_wave))
+@pytest.mark.parametrize("shape", [0, 1])
+def test_mixed_all_tile_shapes(shape, monkeypatch):
+    """Every prefill tile shape on the small mixed batch and on odd groupings."""
+    monkeypatch.setenv("PA_PREFILL_SHAPE", str(shape))
     full_check(workload("mixed_bf16_small"))
     lens = [40, 17, 300, 5, 64, 129, 1, 700]
     q_lens = [40, 2, 33, 1, 16, 100, 1, 64]
