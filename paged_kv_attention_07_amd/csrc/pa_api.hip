@@ -317,6 +317,7 @@ int pa_attention_mixed(void* out, const void* q, const void* kv_cache, int64_t n
     }
     const hipError_t e = pa::launch_prefill(p, dtype, head_dim, group, s);
     if (e != hipSuccess) return PA_ERR_HIP;
+    if (num_seqs == 1) return PA_OK;  // the one request is the chunk: no decode rows
   }
   return hip_status(pa::launch_decode(a, dtype, head_dim, group, s));
 }
