@@ -39,6 +39,7 @@ WORKLOADS = {
     "prefix": "prefix_shared_decode_bf16",
     "long": "long_context_decode_bf16",
     "chunk": "prefill_chunk_bf16",
+    "prefixplain": "prefix_shared_decode_bf16",
     "prefill2k": "prefill_chunk_2048_bf16",
     "prefill8k": "prefill_8192_bf16",
     "prefillbatch": "prefill_batch_4x1024_bf16",
@@ -114,7 +115,7 @@ def alg_counts(w):
 class Stepper:
     """Device copies of one workload and the step of the hot path over them."""
 
-    def __init__(self, w, rotations: int, splits: int):
+    def __init__(self, w, rotations: int, splits: int, shared_prefix: int = 0):
         import torch
         import paged_kv_attention_07_amd as pa
         self.pa, self.torch, self.w, self.splits = pa, torch, w, splits
@@ -138,12 +139,21 @@ class Stepper:
         nbytes = pa.pa_attention_workspace_size(w.num_seqs, w.num_tokens, w.num_q_heads,
                                                 w.num_kv_heads, w.head_dim, w.max_seq_len,
                                                 w.max_query_len, splits)
+        self.shared_prefix = shared_prefix
+        if shared_prefix:
+            nbytes = max(nbytes, pa.pa_attention_decode_shared_prefix_workspace_size(
+                w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.max_seq_len,
+                shared_prefix, splits))
         self.ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device="cuda")
         self.decode = w.is_decode_only
 
     def attention(self, kv):
         w, pa = self.w, self.pa
-        if self.decode:
+        if self.decode and self.shared_prefix:
+            pa.pa_attention_decode_shared_prefix(
+                self.q, kv, self.bt, self.sl, w.scale, w.max_seq_len, self.shared_prefix,
+                out=self.out, workspace=self.ws, num_splits=self.splits)
+        elif self.decode:
             pa.pa_attention_decode(self.q, kv, self.bt, self.sl, w.scale, w.max_seq_len,
                                    out=self.out, workspace=self.ws, num_splits=self.splits)
         else:
@@ -276,13 +286,14 @@ def cpu_baseline(w, budget_s: float = 12.0):
 # --------------------------------------------------------------------------
 
 
-def measure(name, args, rotations):
+def measure(name, args, rotations, shared_prefix=False):
     from workloads import make_workload
     t0 = time.perf_counter()
     w = make_workload(name)
     print(f"[bench] {name}: generated in {time.perf_counter() - t0:.1f}s", file=sys.stderr,
           flush=True)
-    st = Stepper(w, rotations, args.splits)
+    st = Stepper(w, rotations, args.splits,
+                 w.meta.get("shared_prefix_blocks", 0) if shared_prefix else 0)
     ms_step, attn_ms = st.run(args.steps, args.warmup)
     c = alg_counts(w)
     attn_avg = float(np.mean(attn_ms))
@@ -423,7 +434,8 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     rot = 4
     names = [args.only] if args.only else ["decode", "mixed", "chunk"] + (
-        ["prefix", "long", "prefill2k", "prefill8k", "prefillbatch"] if args.extra else [])
+        ["prefix", "prefixplain", "long", "prefill2k", "prefill8k", "prefillbatch"]
+        if args.extra else [])
     copy_lines, serve_line = [], None
     if args.only == "copy" or (args.extra and not args.only):
         copy_lines = [measure_copy(args, n) for n in (16, 256, 4096)]
@@ -432,7 +444,10 @@ def main():
     if args.only in ("copy", "serve"):
         names = ["decode"]
     names = [n for n in names if n in WORKLOADS]
-    results = {k: measure(WORKLOADS[k], args, rot if k != "long" else 2) for k in names}
+    # the prefix-shared batch runs the shared-prefix decode ("prefix") and the
+    # plain decode ("prefixplain") on the same inputs
+    results = {k: measure(WORKLOADS[k], args, rot if k != "long" else 2,
+                          shared_prefix=(k == "prefix")) for k in names}
 
     # the headline is the decode batch; with --only <leg> it is that leg, with
     # the roofline of the kernel that dominates it
@@ -453,14 +468,19 @@ def main():
                     "kernel": "pa_attention_mixed (prefill_tile_kernel)",
                     "alg_flops_per_launch": int(c["chunk_flops"]), **launch}
     else:
+        # shared-prefix batches are priced on unique bytes (the prefix once)
+        alg = c["attn_unique"] if head_key in ("prefix", "prefixplain") else c["attn_logical"]
+        achieved = alg / (head["attn_ms_avg"] * 1e-3) / 1e9
+        kernel = {"decode": "pa_attention_decode (decode_split_kernel + decode_merge_kernel)",
+                  "prefix": "pa_attention_decode_shared_prefix",
+                  "prefixplain": "pa_attention_decode", "long": "pa_attention_decode",
+                  "mixed": "pa_attention_mixed"}.get(head_key, head_key)
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                     "traffic": recorded_traffic("decode_split_kernel")
                     if head_key == "decode" else None,
                     "traffic_kernel": "decode_split_kernel (profiles/traffic.json)",
-                    "kernel": "pa_attention_decode (decode_split_kernel + decode_merge_kernel)"
-                    if head_key == "decode" else "pa_attention_mixed",
-                    "alg_bytes_per_launch": int(c["attn_logical"]), **launch}
+                    "kernel": kernel, "alg_bytes_per_launch": int(alg), **launch}
     line = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -516,11 +536,13 @@ def main():
                 "mfma_util": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
                 "tokens_per_s": round(rw.num_tokens / (r["ms_step"] * 1e-3), 1),
             }
-    for key in ("prefix", "long"):
+    for key in ("prefix", "prefixplain", "long"):
         if key in results:
             r = results[key]
             rw, rc = r["w"], r["counts"]
             line[f"{key}_decode"] = {
+                "entry": ("pa_attention_decode_shared_prefix" if key == "prefix"
+                          else "pa_attention_decode"),
                 "workload": rw.name,
                 "attention_avg_us": round(r["attn_ms_avg"] * 1e3, 2),
                 "hbm_gbs_unique": round(rc["attn_unique"] / (r["attn_ms_avg"] * 1e-3) / 1e9, 1),

@@ -8,9 +8,7 @@
  *
  * Conventions shared by every entry point
  *   - Pointers are DEVICE pointers owned by the caller unless marked (host).
- *     The library keeps no pointer after a call returns and never allocates
- *     memory; pa_attention_mixed keeps one side stream and two events per
- *     device, created on its first use there.
+ *     The library keeps no pointer after a call returns and never allocates.
  *   - Every call is asynchronous on `stream` (a hipStream_t passed as void*;
  *     NULL = the default stream) and never synchronises.
  *   - Tensors are dense, row-major, with the shapes given below.
@@ -162,6 +160,42 @@ int pa_attention_decode(void* out, const void* q, const void* kv_cache,
                         int32_t num_splits, void* stream);
 
 /*
+ * pa_attention_decode_shared_prefix -- decode for a batch whose requests all
+ * start with the same physical blocks (a common prompt prefix shared through
+ * prefix caching: [P4] §3.5, [P1] §4.3.1).  Same result as
+ * pa_attention_decode; the prefix's keys are read once for the whole batch:
+ *   - a matrix-core pass attends every request's query to the prefix keys
+ *     (one virtual request whose queries are all the rows), producing a
+ *     partial (max, sum, output) per row and query head;
+ *   - the split decode attends each request's keys after the prefix, in the
+ *     same launch as the pass (work-groups of both kinds);
+ *   - a merge combines both with the online-softmax identity.
+ *
+ *   shared_prefix_blocks  (host) P: block_table[r][0 .. P-1] are the same
+ *                         physical blocks for every r (precondition, not
+ *                         checked on the device), and 16 P <= seq_lens[r]
+ *                         <= max_seq_len.  P = 0, fp32, or a head shape
+ *                         without a matrix-core path runs pa_attention_decode.
+ *   workspace             >= pa_attention_decode_shared_prefix_workspace_size
+ *                         (same arguments) bytes, 256-byte aligned.
+ *   Other arguments as pa_attention_decode.
+ */
+size_t pa_attention_decode_shared_prefix_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                                        int32_t num_kv_heads, int32_t head_dim,
+                                                        int32_t max_seq_len,
+                                                        int32_t shared_prefix_blocks,
+                                                        int32_t num_splits);
+
+int pa_attention_decode_shared_prefix(void* out, const void* q, const void* kv_cache,
+                                      int64_t num_blocks, int32_t block_size,
+                                      int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                                      const int32_t* block_table, int32_t block_table_stride,
+                                      const int32_t* seq_lens, int32_t num_seqs,
+                                      int32_t max_seq_len, int32_t num_q_heads, float scale,
+                                      int32_t shared_prefix_blocks, void* workspace,
+                                      size_t workspace_bytes, int32_t num_splits, void* stream);
+
+/*
  * pa_attention_mixed -- attention for a chunked-prefill mixed batch.
  *   [P4] §4.2 (prefill chunks and decodes packed in one 1-D varlen batch;
  *   each sequence handled by its own bounds; a chunk attends its cached
@@ -172,11 +206,11 @@ int pa_attention_decode(void* out, const void* q, const void* kv_cache,
  *     out[t][h] = sum_{j<=pos} softmax_j(scale * <q[t][h], K_j>) * V_j.
  *   Requests with one query take the decode path; longer ones the MFMA
  *   tile path with a causal mask.  When the batch has a chunk and at least
- *   one other request, the tiles run on a library-owned side stream,
- *   concurrently with the decode rows (one decode wave and one tile wave per
- *   SIMD), forked from and joined back into `stream` with events, so stream
- *   order is kept for the caller.  PA_MIXED_OVERLAP=0 in the environment
- *   runs both on `stream` instead.
+ *   one other request, the tiles and the decode ranges are work-groups of
+ *   one launch (one tile wave and one decode wave per SIMD), so the
+ *   compute-bound and the bandwidth-bound halves overlap; the decode merge
+ *   follows.  PA_MIXED_OVERLAP=0 in the environment launches them one after
+ *   the other instead.
  *
  *   out, q              [num_tokens, num_q_heads, head_dim], cache dtype.
  *   seq_lens            [num_seqs]: keys of the request's last query,

@@ -17,6 +17,7 @@ __all__ = [
     "PAError", "lib", "library_path", "DTYPE_CODES",
     "pa_compute_slot_mapping", "pa_reshape_and_cache", "pa_copy_blocks",
     "pa_attention_workspace_size", "pa_attention_decode", "pa_attention_mixed",
+    "pa_attention_decode_shared_prefix", "pa_attention_decode_shared_prefix_workspace_size",
     "pa_status_string", "pa_version",
 ]
 
@@ -64,6 +65,13 @@ lib.pa_attention_mixed.argtypes = [
     _i32, _i32, _i32, _f32,                          # max_q max_L Hq scale
     _vp, _sz, _i32, _vp]                             # ws ws_bytes splits stream
 lib.pa_attention_mixed.restype = ctypes.c_int
+lib.pa_attention_decode_shared_prefix_workspace_size.argtypes = [_i32] * 7
+lib.pa_attention_decode_shared_prefix_workspace_size.restype = _sz
+lib.pa_attention_decode_shared_prefix.argtypes = [
+    _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32,   # out q kv NB B Hkv D dtype
+    _vp, _i32, _vp, _i32, _i32, _i32, _f32,          # bt stride seq_lens R max_L Hq scale
+    _i32, _vp, _sz, _i32, _vp]                       # prefix ws ws_bytes splits stream
+lib.pa_attention_decode_shared_prefix.restype = ctypes.c_int
 
 PA_F32, PA_BF16, PA_F16 = 0, 1, 2
 DTYPE_CODES = {"f32": PA_F32, "bf16": PA_BF16, "f16": PA_F16}
@@ -208,6 +216,42 @@ def pa_attention_decode(q, kv_cache, block_table, seq_lens, scale: float, max_se
         int(max_seq_len), hq, float(scale), _dev(ws, "workspace"),
         ws.numel() * ws.element_size(), int(num_splits), _stream())
     _check("pa_attention_decode", st)
+    return out
+
+
+def pa_attention_decode_shared_prefix_workspace_size(num_seqs: int, num_q_heads: int,
+                                                     num_kv_heads: int, head_dim: int,
+                                                     max_seq_len: int, shared_prefix_blocks: int,
+                                                     num_splits: int = 0) -> int:
+    return lib.pa_attention_decode_shared_prefix_workspace_size(
+        num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, shared_prefix_blocks,
+        num_splits)
+
+
+def pa_attention_decode_shared_prefix(q, kv_cache, block_table, seq_lens, scale: float,
+                                      max_seq_len: int, shared_prefix_blocks: int, out=None,
+                                      workspace=None, num_splits: int = 0):
+    """Decode where every request's first `shared_prefix_blocks` table entries
+    are the same physical blocks: the prefix is read once; see pa.h."""
+    torch = _torch()
+    nb, bs, hkv, d = _cache_dims(kv_cache)
+    R, hq = int(q.shape[0]), int(q.shape[1])
+    if q.dim() != 3 or int(q.shape[2]) != d or q.dtype != kv_cache.dtype:
+        raise ValueError("q must be [num_seqs, num_q_heads, head_dim] in the cache dtype")
+    if out is None:
+        out = torch.empty_like(q)
+    need = pa_attention_decode_shared_prefix_workspace_size(R, hq, hkv, d, max_seq_len,
+                                                            shared_prefix_blocks, num_splits)
+    if need == 0:
+        raise ValueError("unsupported shared-prefix decode arguments")
+    ws = _workspace(need, q.device, workspace)
+    st = lib.pa_attention_decode_shared_prefix(
+        _dev(out, "out"), _dev(q, "q"), _dev(kv_cache, "kv_cache"), nb, bs, hkv, d,
+        _dtype_code(kv_cache), _dev(block_table, "block_table", torch.int32, 2),
+        int(block_table.shape[1]), _dev(seq_lens, "seq_lens", torch.int32, 1), R,
+        int(max_seq_len), hq, float(scale), int(shared_prefix_blocks), _dev(ws, "workspace"),
+        ws.numel() * ws.element_size(), int(num_splits), _stream())
+    _check("pa_attention_decode_shared_prefix", st)
     return out
 
 

@@ -4,7 +4,6 @@
 #include <stdint.h>
 #include <stdlib.h>
 
-#include <mutex>
 
 #include "pa.h"
 #include "pa_kernels.h"
@@ -90,35 +89,6 @@ int check_heads(int32_t num_q_heads, int32_t num_kv_heads) {
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
-
-// Side stream for the prefill tiles of a mixed batch, one per device,
-// created on first use: the compute-bound tiles run concurrently with the
-// bandwidth-bound decode rows, forked from and joined back into the caller's
-// stream with two events.  The mutex makes the fork/join enqueue atomic when
-// several host threads call at once.
-struct SideStream {
-  hipStream_t stream = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-};
-constexpr int kMaxDevices = 64;
-std::mutex g_side_mu;
-SideStream g_side[kMaxDevices];
-
-// caller holds g_side_mu
-hipError_t side_stream(SideStream** out) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-  SideStream& s = g_side[dev];
-  if (!s.stream) {
-    if ((e = hipStreamCreateWithFlags(&s.stream, hipStreamNonBlocking)) != hipSuccess) return e;
-    if ((e = hipEventCreateWithFlags(&s.fork, hipEventDisableTiming)) != hipSuccess) return e;
-    if ((e = hipEventCreateWithFlags(&s.join, hipEventDisableTiming)) != hipSuccess) return e;
-  }
-  *out = &s;
-  return hipSuccess;
-}
 
 bool overlap_enabled() {
   const char* v = getenv("PA_MIXED_OVERLAP");
@@ -207,7 +177,7 @@ static int attention_common(void* out, const void* q, const void* kv_cache, int6
                             const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len,
                             int32_t num_q_heads, float scale, void* workspace,
                             size_t workspace_bytes, int32_t num_splits, int32_t max_query_len,
-                            pa::DecodeArgs* a) {
+                            int32_t shared_prefix_blocks, pa::DecodeArgs* a) {
   int st = check_cache(kv_cache, num_blocks, block_size, num_kv_heads, head_dim, dtype);
   if (st != PA_OK) return st;
   st = check_heads(num_q_heads, num_kv_heads);
@@ -220,9 +190,14 @@ static int attention_common(void* out, const void* q, const void* kv_cache, int6
   if (max_seq_len == 0) return PA_OK;
   if (bt_stride < ceil_div(max_seq_len, pa::kBlockSize)) return PA_ERR_INVALID_ARG;
   const int group = num_q_heads / num_kv_heads;
-  const int chunks = plan_chunks(num_seqs, num_kv_heads, group, max_seq_len, num_splits,
-                                 tiles_beside_decode(num_seqs, max_query_len));
-  const WsLayout lay = workspace_layout(num_seqs, num_q_heads, head_dim, chunks);
+  // with a shared prefix the split covers the keys after it, beside the
+  // prefix pass, and R more slots hold the prefix partials
+  const int P = shared_prefix_blocks;
+  const int chunks = plan_chunks(num_seqs, num_kv_heads, group,
+                                 P > 0 ? max(max_seq_len - P * pa::kBlockSize, 1) : max_seq_len,
+                                 num_splits, P > 0 || tiles_beside_decode(num_seqs, max_query_len));
+  const WsLayout lay = workspace_layout(num_seqs, num_q_heads, head_dim,
+                                        chunks + (P > 0 ? num_seqs : 0));
   if (!workspace || workspace_bytes < lay.total) return PA_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return PA_ERR_WORKSPACE;
 
@@ -243,6 +218,8 @@ static int attention_common(void* out, const void* q, const void* kv_cache, int6
   a->ws_meta = reinterpret_cast<int32_t*>(ws + lay.meta);
   a->ws_ml = reinterpret_cast<float*>(ws + lay.ml);
   a->ws_o = reinterpret_cast<float*>(ws + lay.o);
+  a->skip_blocks = P;
+  a->prefix_slot0 = P > 0 ? num_seqs + chunks : -1;
   return 1;  // proceed
 }
 
@@ -256,7 +233,7 @@ int pa_attention_decode(void* out, const void* q, const void* kv_cache, int64_t 
   const int st = attention_common(out, q, kv_cache, num_blocks, block_size, num_kv_heads, head_dim,
                                   dtype, block_table, block_table_stride, seq_lens, num_seqs,
                                   max_seq_len, num_q_heads, scale, workspace, workspace_bytes,
-                                  num_splits, 1, &a);
+                                  num_splits, 1, 0, &a);
   if (st <= 0) return st;
   return hip_status(pa::launch_decode(a, dtype, head_dim, num_q_heads / num_kv_heads,
                                       static_cast<hipStream_t>(stream)));
@@ -275,7 +252,7 @@ int pa_attention_mixed(void* out, const void* q, const void* kv_cache, int64_t n
   const int st = attention_common(out, q, kv_cache, num_blocks, block_size, num_kv_heads, head_dim,
                                   dtype, block_table, block_table_stride, seq_lens, num_seqs,
                                   max_seq_len, num_q_heads, scale, workspace, workspace_bytes,
-                                  num_splits, max_query_len, &a);
+                                  num_splits, max_query_len, 0, &a);
   if (st <= 0) return st;
   if (num_tokens == 0) return PA_OK;
   if (!query_start_loc || !num_computed_tokens) return PA_ERR_INVALID_ARG;
@@ -301,25 +278,84 @@ int pa_attention_mixed(void* out, const void* q, const void* kv_cache, int64_t n
     p.max_query_len = max_query_len;
     p.scale_log2 = a.scale_log2;
     if (tiles_beside_decode(num_seqs, max_query_len)) {
+      // tiles and decode ranges in one launch, then the merge
       p.beside_decode = 1;
-      // fork: tiles on the side stream, decode rows on the caller's; join
-      std::lock_guard<std::mutex> lock(g_side_mu);
-      SideStream* side = nullptr;
-      hipError_t e = side_stream(&side);
-      if (e == hipSuccess) e = hipEventRecord(side->fork, s);
-      if (e == hipSuccess) e = hipStreamWaitEvent(side->stream, side->fork, 0);
-      if (e == hipSuccess) e = pa::launch_prefill(p, dtype, head_dim, group, side->stream);
-      if (e == hipSuccess) e = hipEventRecord(side->join, side->stream);
+      const hipError_t e = pa::launch_fused(a, p, dtype, head_dim, group, s);
       if (e != hipSuccess) return PA_ERR_HIP;
-      const hipError_t ed = pa::launch_decode(a, dtype, head_dim, group, s);
-      e = hipStreamWaitEvent(s, side->join, 0);  // joined whatever the decode launch did
-      return hip_status(ed != hipSuccess ? ed : e);
+      return hip_status(pa::launch_decode_merge(a, dtype, head_dim, group, s));
     }
     const hipError_t e = pa::launch_prefill(p, dtype, head_dim, group, s);
     if (e != hipSuccess) return PA_ERR_HIP;
     if (num_seqs == 1) return PA_OK;  // the one request is the chunk: no decode rows
   }
   return hip_status(pa::launch_decode(a, dtype, head_dim, group, s));
+}
+
+size_t pa_attention_decode_shared_prefix_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                                        int32_t num_kv_heads, int32_t head_dim,
+                                                        int32_t max_seq_len,
+                                                        int32_t shared_prefix_blocks,
+                                                        int32_t num_splits) {
+  const size_t plain = pa_attention_workspace_size(num_seqs, num_seqs, num_q_heads, num_kv_heads,
+                                                   head_dim, max_seq_len, 1, num_splits);
+  if (plain == 0 || shared_prefix_blocks < 0 ||
+      (int64_t)shared_prefix_blocks * pa::kBlockSize > max_seq_len)
+    return 0;
+  if (shared_prefix_blocks == 0) return plain;
+  const int group = num_q_heads / num_kv_heads;
+  const int rest = max(max_seq_len - shared_prefix_blocks * pa::kBlockSize, 1);
+  const int chunks = plan_chunks(num_seqs, num_kv_heads, group, rest, num_splits, true);
+  const size_t casc = workspace_layout(num_seqs, num_q_heads, head_dim, chunks + num_seqs).total;
+  return casc > plain ? casc : plain;
+}
+
+int pa_attention_decode_shared_prefix(void* out, const void* q, const void* kv_cache,
+                                      int64_t num_blocks, int32_t block_size,
+                                      int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                                      const int32_t* block_table, int32_t block_table_stride,
+                                      const int32_t* seq_lens, int32_t num_seqs,
+                                      int32_t max_seq_len, int32_t num_q_heads, float scale,
+                                      int32_t shared_prefix_blocks, void* workspace,
+                                      size_t workspace_bytes, int32_t num_splits, void* stream) {
+  const int P = shared_prefix_blocks;
+  if (P < 0 || (int64_t)P * pa::kBlockSize > max_seq_len) return PA_ERR_INVALID_ARG;
+  const int group = num_kv_heads > 0 && num_q_heads % num_kv_heads == 0
+                        ? num_q_heads / num_kv_heads : 0;
+  // no prefix, or no matrix-core path for this configuration: plain decode
+  if (P == 0 || !pa::prefill_supported(dtype, head_dim, group))
+    return pa_attention_decode(out, q, kv_cache, num_blocks, block_size, num_kv_heads, head_dim,
+                               dtype, block_table, block_table_stride, seq_lens, num_seqs,
+                               max_seq_len, num_q_heads, scale, workspace, workspace_bytes,
+                               num_splits, stream);
+  pa::DecodeArgs a{};
+  const int st = attention_common(out, q, kv_cache, num_blocks, block_size, num_kv_heads, head_dim,
+                                  dtype, block_table, block_table_stride, seq_lens, num_seqs,
+                                  max_seq_len, num_q_heads, scale, workspace, workspace_bytes,
+                                  num_splits, 1, P, &a);
+  if (st <= 0) return st;
+  pa::PrefillArgs p{};
+  p.q = q;
+  p.kv = kv_cache;
+  p.block_table = block_table;  // row 0 holds the shared prefix like every row
+  p.bt_stride = block_table_stride;
+  p.num_seqs = 1;
+  p.num_kv_heads = num_kv_heads;
+  p.num_q_heads = num_q_heads;
+  p.max_tiles = (int)ceil_div(num_seqs, pa::kQueriesPerTile) + 1;
+  p.max_query_len = num_seqs;
+  p.beside_decode = 1;
+  p.scale_log2 = a.scale_log2;
+  p.cascade_rows = num_seqs;
+  p.cascade_keys = P * pa::kBlockSize;
+  p.prefix_slot0 = a.prefix_slot0;
+  p.ws_ml = a.ws_ml;
+  p.ws_o = a.ws_o;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // the prefix pass and the split over the suffixes in one launch, then the
+  // merge of prefix and suffix partials
+  const hipError_t e = pa::launch_fused(a, p, dtype, head_dim, group, s);
+  if (e != hipSuccess) return PA_ERR_HIP;
+  return hip_status(pa::launch_decode_merge(a, dtype, head_dim, group, s));
 }
 
 }  // extern "C"

@@ -1,603 +1,77 @@
-// Decode attention over a paged KV cache on gfx950, with a balanced
-// split-KV partition-and-reduce.
-//
-// What it computes ("vLLM 架构源码解析（一）" §3.3.3 and §4.2;
-// "Inside vLLM" §3.3): for each request with one new query token, softmax
-// attention of that token over its seq_len cached keys, read through the
-// request's block table.  Partial results over key ranges are merged with
-// the online-softmax identity (max, sum, unnormalised output), the
-// "Online Softmax" the first page names in §6.4.
-//
-// Work decomposition.  The blocks of all decode requests are laid end to end
-// (request 0's blocks, then request 1's, ...) and the list is cut into
-// `num_chunks` equal ranges.  One wavefront takes one range for one KV head
-// (and up to four query heads of its group), so every wavefront streams the
-// same number of bytes whatever the length mix; a range that covers a whole
-// request finishes it in place, a request cut by range boundaries leaves one
-// partial per range, and a small merge kernel combines them.  Partials of
-// (request r, range c) go to workspace slot r + c, which is unique because
-// both indices only grow along the list.
-//
-// Inside a wavefront (64 lanes).  Lane = (token group tg = lane / 8, column
-// ds = lane % 8).  For each 16-token block the lane loads tokens tg and tg+8;
-// the 8 lanes of a group read 128 contiguous bytes of a token's head row per
-// instruction (16 bytes each), so every load instruction touches 8 full
-// 128-byte lines.  Scores are 8-lane DPP sums of per-lane dot products
-// (bf16/f16: v_dot2 pairs, no conversion); each token group keeps its own
-// running max / sum / accumulator (no cross-group traffic in the loop), with
-// the accumulator rescaled only when the max grows by more than 2^8.  P*V
-// pairs the group's two tokens in one v_dot2 per output element.  At the end
-// of a range the 8 groups are merged and reduce-scattered so each lane owns
-// a few contiguous output elements.
-#include <math.h>
-
-#include "pa_common.h"
-#include "pa_kernels.h"
+// Launchers of the decode split and merge kernels (device code in
+// pa_decode_impl.h).
+#include "pa_decode_impl.h"
 
 namespace pa {
 namespace {
 
 template <typename E, int D, int HPW>
-struct Shape {
-  static constexpr int ESZ = E::bytes;
-  static constexpr int EPV = 16 / ESZ;    // elements per 16-byte vector
-  static constexpr int ROWB = D * ESZ;    // bytes of one token's row for one kv head
-  static constexpr int NCH = ROWB / 128;  // 16-byte vectors per lane per token
-  static constexpr int DPL = NCH * EPV;   // head dims owned by a lane
-  static constexpr int NV = HPW * DPL;    // accumulator floats per lane
-  static constexpr int NOUT = NV / 8;     // outputs per lane after the group merge
-  static constexpr int RUN = NOUT < EPV ? NOUT : EPV;  // contiguous dims per store
-  static_assert(NCH >= 1 && NOUT >= 1, "unsupported decode shape");
-};
-
-// head dim of lane-local element e for column ds
-template <class S>
-__device__ __forceinline__ int dim_of(int e, int ds) {
-  return (e / S::EPV) * (8 * S::EPV) + ds * S::EPV + (e % S::EPV);
-}
-
-struct ReqInfo {
-  int nb;   // blocks this request contributes to the decode list (0 = not a decode row)
-  int row;  // query/output row
-  int len;  // keys
-};
-
-__device__ __forceinline__ ReqInfo req_info(const DecodeArgs& a, int r) {
-  ReqInfo ri{0, 0, 0};
-  if (r < a.num_seqs) {
-    const int L = a.seq_lens[r];
-    bool active = L > 0;
-    int row = r;
-    if (a.qsl) {
-      const int q0 = a.qsl[r], q1 = a.qsl[r + 1];
-      active = active && (q1 - q0 == 1);
-      row = q0;
-    }
-    ri.nb = active ? (L + kBlockSize - 1) / kBlockSize : 0;
-    ri.row = row;
-    ri.len = L;
-  }
-  return ri;
-}
-
-__device__ __forceinline__ int total_blocks(const DecodeArgs& a) {
-  int W = 0;
-  for (int base = 0; base < a.num_seqs; base += kWave)
-    W += uniform(wave_sum(req_info(a, base + lane_id()).nb));
-  return W;
-}
-
-__device__ __forceinline__ int64_t chunk_begin(int c, int W, int N) {
-  return (int64_t)c * W / N;
-}
-
-// the range holding flat block x (ranges may be empty when W < N)
-__device__ __forceinline__ int chunk_of(int64_t x, int W, int N) {
-  return (int)(((x + 1) * N + W - 1) / W) - 1;
-}
-
-template <typename E>
-__device__ __forceinline__ float to_f(uint32_t w, int half);
-
-template <>
-__device__ __forceinline__ float to_f<BF16>(uint32_t w, int half) {
-  return half ? bf16_hi(w) : bf16_lo(w);
-}
-template <>
-__device__ __forceinline__ float to_f<F16>(uint32_t w, int half) {
-  return half ? f16_hi(w) : f16_lo(w);
-}
-
-// Store RUN consecutive values (times `mul`) as element type E.
-template <typename E, int RUN>
-__device__ __forceinline__ void store_run(void* dst, const float* v, float mul) {
-  if constexpr (E::kind == F32::kind) {
-    float* p = static_cast<float*>(dst);
-    if constexpr (RUN % 4 == 0) {
-#pragma unroll
-      for (int i = 0; i < RUN; i += 4) {
-        f32x4_t x = {v[i] * mul, v[i + 1] * mul, v[i + 2] * mul, v[i + 3] * mul};
-        *reinterpret_cast<f32x4_t*>(p + i) = x;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < RUN; ++i) p[i] = v[i] * mul;
-    }
-  } else {
-    if constexpr (RUN % 2 == 0) {
-      uint32_t w[RUN / 2];
-#pragma unroll
-      for (int i = 0; i < RUN / 2; ++i) {
-        w[i] = (E::kind == BF16::kind) ? pack_bf16(v[2 * i] * mul, v[2 * i + 1] * mul)
-                                       : pack_f16(v[2 * i] * mul, v[2 * i + 1] * mul);
-      }
-      uint32_t* p = static_cast<uint32_t*>(dst);
-      if constexpr (RUN == 8) {
-        u32x4_t x = {w[0], w[1], w[2], w[3]};
-        store16(p, x);
-      } else {
-#pragma unroll
-        for (int i = 0; i < RUN / 2; ++i) p[i] = w[i];
-      }
-    } else {
-      const uint32_t w = (E::kind == BF16::kind) ? pack_bf16(v[0] * mul, 0.f)
-                                                 : pack_f16(v[0] * mul, 0.f);
-      *static_cast<uint16_t*>(dst) = (uint16_t)(w & 0xffffu);
-    }
-  }
-}
-
-template <int RUN>
-__device__ __forceinline__ void store_f32_run(float* p, const float* v) {
-  if constexpr (RUN % 4 == 0) {
-#pragma unroll
-    for (int i = 0; i < RUN; i += 4) {
-      f32x4_t x = {v[i], v[i + 1], v[i + 2], v[i + 3]};
-      *reinterpret_cast<f32x4_t*>(p + i) = x;
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < RUN; ++i) p[i] = v[i];
-  }
-}
-
-template <typename E, int D, int HPW>
-struct BlockRegs {
-  using S = Shape<E, D, HPW>;
-  u32x4_t k0[S::NCH], k1[S::NCH], v0[S::NCH], v1[S::NCH];
-};
-
-template <typename E, int D, int HPW>
-__device__ __forceinline__ void load_block(BlockRegs<E, D, HPW>& b, const uint8_t* p,
-                                           int64_t tok8, int64_t half) {
-  using S = Shape<E, D, HPW>;
-#pragma unroll
-  for (int c = 0; c < S::NCH; ++c) {
-    b.k0[c] = load16(p + c * 128);
-    b.k1[c] = load16(p + tok8 + c * 128);
-  }
-#pragma unroll
-  for (int c = 0; c < S::NCH; ++c) {
-    b.v0[c] = load16(p + half + c * 128);
-    b.v1[c] = load16(p + half + tok8 + c * 128);
-  }
-}
-
-// One 16-token block of one request: scores of tokens tg and tg+8 of the
-// block for the wave's query heads, running-max update, and P*V.
-template <typename E, int D, int HPW>
-__device__ __forceinline__ void attend_block(BlockRegs<E, D, HPW>& b, int j, int nb, int L,
-                                             int tg, float scale_log2,
-                                             const u32x4_t (&qv)[HPW][Shape<E, D, HPW>::NCH],
-                                             float (&m)[HPW], float (&l)[HPW],
-                                             float (&acc)[HPW][Shape<E, D, HPW>::DPL]) {
-  using S = Shape<E, D, HPW>;
-  // ---- scores of tokens tg and tg+8 for each head (log2 units)
-  float s0[HPW], s1[HPW];
-#pragma unroll
-  for (int hh = 0; hh < HPW; ++hh) {
-    float a0 = 0.f, a1 = 0.f;
-#pragma unroll
-    for (int c = 0; c < S::NCH; ++c)
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        if constexpr (E::kind == F32::kind) {
-          const float qf = __uint_as_float(qv[hh][c][w]);
-          a0 = fmaf(__uint_as_float(b.k0[c][w]), qf, a0);
-          a1 = fmaf(__uint_as_float(b.k1[c][w]), qf, a1);
-        } else if constexpr (E::kind == BF16::kind) {
-          a0 = dot2_bf16(b.k0[c][w], qv[hh][c][w], a0);
-          a1 = dot2_bf16(b.k1[c][w], qv[hh][c][w], a1);
-        } else {
-          a0 = dot2_f16(b.k0[c][w], qv[hh][c][w], a0);
-          a1 = dot2_f16(b.k1[c][w], qv[hh][c][w], a1);
-        }
-      }
-    s0[hh] = sum8(a0) * scale_log2;
-    s1[hh] = sum8(a1) * scale_log2;
-  }
-  // ---- partial last block: drop scores and values past the sequence end
-  if (j == nb - 1 && (L & (kBlockSize - 1))) {
-    const int nvalid = L - j * kBlockSize;
-    const bool ok0 = tg < nvalid, ok1 = tg + 8 < nvalid;
-#pragma unroll
-    for (int hh = 0; hh < HPW; ++hh) {
-      s0[hh] = ok0 ? s0[hh] : -INFINITY;
-      s1[hh] = ok1 ? s1[hh] : -INFINITY;
-    }
-#pragma unroll
-    for (int c = 0; c < S::NCH; ++c)
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        b.v0[c][w] = ok0 ? b.v0[c][w] : 0u;
-        b.v1[c][w] = ok1 ? b.v1[c][w] : 0u;
-      }
-  }
-  // ---- running max; rescale only when it grows by more than 8 (log2 units)
-  bool grow = false;
-  float mn[HPW];
-#pragma unroll
-  for (int hh = 0; hh < HPW; ++hh) {
-    mn[hh] = fmaxf(m[hh], fmaxf(s0[hh], s1[hh]));
-    grow |= mn[hh] > m[hh] + 8.f;
-  }
-  if (__any(grow)) {
-#pragma unroll
-    for (int hh = 0; hh < HPW; ++hh) {
-      const float mu = (mn[hh] > m[hh] + 8.f) ? mn[hh] : m[hh];
-      const float alpha = (mu == m[hh]) ? 1.f : __builtin_amdgcn_exp2f(m[hh] - mu);
-      l[hh] *= alpha;
-#pragma unroll
-      for (int e = 0; e < S::DPL; ++e) acc[hh][e] *= alpha;
-      m[hh] = mu;
-    }
-  }
-  float p0[HPW], p1[HPW];
-#pragma unroll
-  for (int hh = 0; hh < HPW; ++hh) {
-    const float ms = (m[hh] == -INFINITY) ? 0.f : m[hh];
-    p0[hh] = __builtin_amdgcn_exp2f(s0[hh] - ms);
-    p1[hh] = __builtin_amdgcn_exp2f(s1[hh] - ms);
-    l[hh] += p0[hh] + p1[hh];
-  }
-  // ---- P * V
-  if constexpr (E::kind == F32::kind) {
-#pragma unroll
-    for (int c = 0; c < S::NCH; ++c)
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float x0 = __uint_as_float(b.v0[c][w]);
-        const float x1 = __uint_as_float(b.v1[c][w]);
-#pragma unroll
-        for (int hh = 0; hh < HPW; ++hh)
-          acc[hh][c * 4 + w] = fmaf(p1[hh], x1, fmaf(p0[hh], x0, acc[hh][c * 4 + w]));
-      }
-  } else {
-    uint32_t pp[HPW];
-#pragma unroll
-    for (int hh = 0; hh < HPW; ++hh)
-      pp[hh] = (E::kind == BF16::kind) ? pack_bf16(p0[hh], p1[hh]) : pack_f16(p0[hh], p1[hh]);
-#pragma unroll
-    for (int c = 0; c < S::NCH; ++c)
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t lo = pair_lo(b.v0[c][w], b.v1[c][w]);
-        const uint32_t hi = pair_hi(b.v0[c][w], b.v1[c][w]);
-        const int e = c * S::EPV + 2 * w;
-#pragma unroll
-        for (int hh = 0; hh < HPW; ++hh) {
-          if constexpr (E::kind == BF16::kind) {
-            acc[hh][e] = dot2_bf16(lo, pp[hh], acc[hh][e]);
-            acc[hh][e + 1] = dot2_bf16(hi, pp[hh], acc[hh][e + 1]);
-          } else {
-            acc[hh][e] = dot2_f16(lo, pp[hh], acc[hh][e]);
-            acc[hh][e + 1] = dot2_f16(hi, pp[hh], acc[hh][e + 1]);
-          }
-        }
-      }
-  }
-}
-
-// Attention of one query row over keys [16*j0, min(16*j1, L)) of request r.
-template <typename E, int D, int HPW>
-__device__ __forceinline__ void process_range(const DecodeArgs& a, int r, int row, int L, int j0,
-                                              int j1, int h, int hq0, bool whole, int slot) {
-  using S = Shape<E, D, HPW>;
-  const int lane = lane_id();
-  const int tg = lane >> 3;
-  const int ds = lane & 7;
-
-  // this lane's slice of the HPW query vectors
-  u32x4_t qv[HPW][S::NCH];
-  {
-    const uint8_t* qb = static_cast<const uint8_t*>(a.q) +
-                        ((int64_t)row * a.num_q_heads + hq0) * S::ROWB + ds * 16;
-#pragma unroll
-    for (int hh = 0; hh < HPW; ++hh)
-#pragma unroll
-      for (int c = 0; c < S::NCH; ++c) qv[hh][c] = load16(qb + hh * S::ROWB + c * 128);
-  }
-
-  const int64_t tok_stride = (int64_t)a.num_kv_heads * S::ROWB;
-  const int64_t half_stride = kBlockSize * tok_stride;
-  const int64_t blk_stride = 2 * half_stride;
-  const int64_t tok8 = 8 * tok_stride;
-  const uint8_t* kvh = static_cast<const uint8_t*>(a.kv) + (int64_t)h * S::ROWB +
-                       tg * tok_stride + ds * 16;
-  const int32_t* bt = a.block_table + (int64_t)r * a.bt_stride;
-  const int nb = (L + kBlockSize - 1) / kBlockSize;
-
-  float m[HPW], l[HPW], acc[HPW][S::DPL];
-#pragma unroll
-  for (int hh = 0; hh < HPW; ++hh) {
-    m[hh] = -INFINITY;
-    l[hh] = 0.f;
-#pragma unroll
-    for (int e = 0; e < S::DPL; ++e) acc[hh][e] = 0.f;
-  }
-
-  // three register buffers: blocks j+1 and j+2 are in flight while block j
-  // is processed; block ids are read one step before their loads are issued
-  BlockRegs<E, D, HPW> b0, b1, b2;
-  int id_next = (j0 + 2 < j1) ? load_scalar(bt + j0 + 2) : 0;
-  load_block<E, D, HPW>(b0, kvh + (int64_t)load_scalar(bt + j0) * blk_stride, tok8, half_stride);
-  if (j0 + 1 < j1)
-    load_block<E, D, HPW>(b1, kvh + (int64_t)load_scalar(bt + j0 + 1) * blk_stride, tok8,
-                          half_stride);
-  int j = j0;
-  auto issue = [&](BlockRegs<E, D, HPW>& b) {
-    // load block j + 2 into b, then fetch the id of block j + 3
-    if (j + 2 < j1) {
-      load_block<E, D, HPW>(b, kvh + (int64_t)id_next * blk_stride, tok8, half_stride);
-      id_next = (j + 3 < j1) ? load_scalar(bt + j + 3) : 0;
-    }
-  };
-  while (true) {
-    issue(b2);
-    attend_block<E, D, HPW>(b0, j, nb, L, tg, a.scale_log2, qv, m, l, acc);
-    if (++j >= j1) break;
-    issue(b0);
-    attend_block<E, D, HPW>(b1, j, nb, L, tg, a.scale_log2, qv, m, l, acc);
-    if (++j >= j1) break;
-    issue(b1);
-    attend_block<E, D, HPW>(b2, j, nb, L, tg, a.scale_log2, qv, m, l, acc);
-    if (++j >= j1) break;
-  }
-
-  // ---- merge the 8 token groups: common max, rescaled sums and accumulators
-  float Mh[HPW], Lh[HPW];
-#pragma unroll
-  for (int hh = 0; hh < HPW; ++hh) {
-    float M = m[hh];
-    M = fmaxf(M, shfl_xor(M, 8));
-    M = fmaxf(M, shfl_xor(M, 16));
-    M = fmaxf(M, shfl_xor(M, 32));
-    const float sc = (m[hh] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m[hh] - M);
-    float lt = l[hh] * sc;
-    lt += shfl_xor(lt, 8);
-    lt += shfl_xor(lt, 16);
-    lt += shfl_xor(lt, 32);
-#pragma unroll
-    for (int e = 0; e < S::DPL; ++e) acc[hh][e] *= sc;
-    Mh[hh] = M;
-    Lh[hh] = lt;
-  }
-  // reduce-scatter over the groups: lane keeps NOUT consecutive values of
-  // the flattened [HPW][DPL] accumulator, starting at `base`
-  float* v = &acc[0][0];
-  int base = 0;
-#pragma unroll
-  for (int st = 0; st < 3; ++st) {
-    const int n = S::NV >> st;
-    const int bit = (tg >> st) & 1;
-#pragma unroll
-    for (int i = 0; i < n / 2; ++i) {
-      const float lo = v[i], hi = v[i + n / 2];
-      const float send = bit ? lo : hi;
-      const float keep = bit ? hi : lo;
-      v[i] = keep + shfl_xor(send, 8 << st);
-    }
-    base += bit * (n / 2);
-  }
-  const int hsel = base / S::DPL;
-  const int e0 = base % S::DPL;
-  float lsel = Lh[0], msel = Mh[0];
-#pragma unroll
-  for (int hh = 1; hh < HPW; ++hh) {
-    lsel = (hsel == hh) ? Lh[hh] : lsel;
-    msel = (hsel == hh) ? Mh[hh] : msel;
-  }
-  const int hq = hq0 + hsel;
-  if (whole) {
-    uint8_t* ob = static_cast<uint8_t*>(a.out) + ((int64_t)row * a.num_q_heads + hq) * S::ROWB;
-    const float inv = 1.f / lsel;
-#pragma unroll
-    for (int r0 = 0; r0 < S::NOUT; r0 += S::RUN)
-      store_run<E, S::RUN>(ob + (int64_t)dim_of<S>(e0 + r0, ds) * S::ESZ, v + r0, inv);
-  } else {
-    const int64_t ps = (int64_t)slot * a.num_q_heads + hq;
-    float* ob = a.ws_o + ps * D;
-#pragma unroll
-    for (int r0 = 0; r0 < S::NOUT; r0 += S::RUN)
-      store_f32_run<S::RUN>(ob + dim_of<S>(e0 + r0, ds), v + r0);
-    // one lane per head writes (max, sum): the lane whose run starts the head
-    if (e0 == 0 && ds == 0) {
-      f32x2_t ml = {msel, lsel};
-      *reinterpret_cast<f32x2_t*>(a.ws_ml + ps * 2) = ml;
-    }
-  }
-}
-
-template <typename E, int D, int HPW>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_split_kernel(DecodeArgs a) {
-  const int lane = lane_id();
-  const int item = uniform(blockIdx.x * 4 + (threadIdx.x >> 6));
-  const int per_chunk = a.num_kv_heads * a.head_groups;
-  if (item >= a.num_chunks * per_chunk) return;
-  const int c = item / per_chunk;
-  const int rem = item - c * per_chunk;
-  const int h = rem / a.head_groups;
-  const int hs = rem - h * a.head_groups;
-  const int group = a.num_q_heads / a.num_kv_heads;
-  const int hq0 = h * group + hs * HPW;
-
-  const int W = total_blocks(a);
-  if (W == 0) return;
-  const int64_t b0 = chunk_begin(c, W, a.num_chunks);
-  const int64_t b1 = chunk_begin(c + 1, W, a.num_chunks);
-  if (b0 >= b1) return;
-
-  int running = 0;
-  for (int base = 0; base < a.num_seqs && running < b1; base += kWave) {
-    const ReqInfo ri = req_info(a, base + lane);
-    const int incl = wave_incl_scan(ri.nb) + running;
-    const int excl = incl - ri.nb;
-    uint64_t mask = __ballot(ri.nb > 0 && excl < b1 && incl > b0);
-    while (mask) {
-      const int src = __builtin_ctzll(mask);
-      mask &= mask - 1;
-      const int s = readlane(excl, src), e = readlane(incl, src);
-      const int L = readlane(ri.len, src), row = readlane(ri.row, src);
-      const int j0 = (int)((b0 > s ? b0 : s) - s);
-      const int j1 = (int)((b1 < e ? b1 : e) - s);
-      const bool whole = (j0 == 0) && (j1 == e - s);
-      if (j0 == 0 && h == 0 && hs == 0 && lane == 0) {
-        // the range holding the request's first block records how it was cut
-        const int cl = whole ? -1 : chunk_of(e - 1, W, a.num_chunks);
-        int4 meta = {whole ? -1 : c, cl, W, 0};
-        *reinterpret_cast<int4*>(a.ws_meta + 4 * (int64_t)(base + src)) = meta;
-      }
-      process_range<E, D, HPW>(a, base + src, row, L, j0, j1, h, hq0, whole, base + src + c);
-    }
-    running = readlane(incl, kWave - 1);
-  }
-}
-
-// Merge the partials of requests cut by range boundaries.  One wavefront per
-// (request, query head); lane owns D/64 consecutive dims.  The split kernel
-// recorded, for each decode request, its first and last range and W.  The
-// (max, sum) pairs of all ranges are read at once, one range per lane, and the
-// partial outputs in batches of 8 ranges, so the merge costs a few memory
-// round trips whatever the number of ranges.
-template <typename E, int D>
-__global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
-  const int lane = lane_id();
-  const int r = blockIdx.x / a.num_q_heads;
-  const int hq = blockIdx.x - r * a.num_q_heads;
-  bool active = a.seq_lens[r] > 0;
-  int row = r;
-  if (a.qsl) {
-    const int q0 = a.qsl[r], q1 = a.qsl[r + 1];
-    active = active && (q1 - q0 == 1);
-    row = q0;
-  }
-  const int4 meta = *reinterpret_cast<const int4*>(a.ws_meta + 4 * (int64_t)r);
-  if (!active || meta.x < 0) return;  // finished in place by its range
-  const int cf = uniform(meta.x), cl = uniform(meta.y), W = uniform(meta.z);
-  const int N = a.num_chunks;
-  const int64_t base = (int64_t)r * a.num_q_heads + hq;  // slot (r + c) -> + c * Hq
-
-  // pass 1: global max and weighted sum over ranges, lanes in parallel
-  float M = -INFINITY;
-  for (int c0 = cf; c0 <= cl; c0 += kWave) {
-    const int c = c0 + lane;
-    float mc = -INFINITY;
-    if (c <= cl && chunk_begin(c, W, N) < chunk_begin(c + 1, W, N))
-      mc = a.ws_ml[(base + (int64_t)c * a.num_q_heads) * 2];
-    M = fmaxf(M, mc);
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, shfl_xor(M, o));
-
-  constexpr int DPT = D / kWave;
-  float lsum = 0.f, acc[DPT];
-#pragma unroll
-  for (int i = 0; i < DPT; ++i) acc[i] = 0.f;
-  for (int c0 = cf; c0 <= cl; c0 += kWave) {
-    const int c = c0 + lane;
-    float w = 0.f;
-    if (c <= cl && chunk_begin(c, W, N) < chunk_begin(c + 1, W, N)) {
-      const f32x2_t ml = *reinterpret_cast<const f32x2_t*>(
-          a.ws_ml + (base + (int64_t)c * a.num_q_heads) * 2);
-      w = __builtin_amdgcn_exp2f(ml[0] - M);
-      lsum += w * ml[1];
-    }
-    // pass 2: this group of up to 64 ranges, 8 loads in flight at a time
-    const int n = min(kWave, cl - c0 + 1);
-    for (int k0 = 0; k0 < n; k0 += 8) {
-      float v[8][DPT], wk[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        wk[k] = __shfl(w, k0 + k < n ? k0 + k : 0, kWave);
-        wk[k] = k0 + k < n ? wk[k] : 0.f;
-#pragma unroll
-        for (int i = 0; i < DPT; ++i) v[k][i] = 0.f;
-        if (wk[k] != 0.f) {
-          const float* po = a.ws_o + (base + (int64_t)(c0 + k0 + k) * a.num_q_heads) * D +
-                            lane * DPT;
-#pragma unroll
-          for (int i = 0; i < DPT; ++i) v[k][i] = po[i];
-        }
-      }
-#pragma unroll
-      for (int k = 0; k < 8; ++k)
-#pragma unroll
-        for (int i = 0; i < DPT; ++i) acc[i] = fmaf(wk[k], v[k][i], acc[i]);
-    }
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) lsum += shfl_xor(lsum, o);
-  uint8_t* ob = static_cast<uint8_t*>(a.out) +
-                (((int64_t)row * a.num_q_heads + hq) * D + lane * DPT) * E::bytes;
-  store_run<E, DPT>(ob, acc, 1.f / lsum);
-}
-
-template <typename E, int D, int HPW>
-hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
+hipError_t launch_split_typed(const DecodeArgs& a, hipStream_t stream) {
   const int64_t items = (int64_t)a.num_chunks * a.num_kv_heads * a.head_groups;
   const unsigned wgs = (unsigned)((items + 3) / 4);
   hipLaunchKernelGGL((decode_split_kernel<E, D, HPW>), dim3(wgs), dim3(256), 0, stream, a);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  const unsigned merges = (unsigned)a.num_seqs * (unsigned)a.num_q_heads;
-  if (a.num_chunks > 1 && merges > 0) {
-    hipLaunchKernelGGL((decode_merge_kernel<E, D>), dim3(merges), dim3(64), 0, stream, a);
-    err = hipGetLastError();
-  }
-  return err;
+  return hipGetLastError();
 }
 
 template <typename E, int D>
-hipError_t launch_hpw(const DecodeArgs& a, int group, hipStream_t stream) {
+hipError_t launch_merge_typed(const DecodeArgs& a, hipStream_t stream) {
+  const unsigned merges = (unsigned)a.num_seqs * (unsigned)a.num_q_heads;
+  if ((a.num_chunks > 1 || a.prefix_slot0 >= 0) && merges > 0) {
+    hipLaunchKernelGGL((decode_merge_kernel<E, D>), dim3(merges), dim3(64), 0, stream, a);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
+template <typename E, int D>
+hipError_t launch_hpw(const DecodeArgs& a, int group, bool split, hipStream_t stream) {
+  if (!split) return launch_merge_typed<E, D>(a, stream);
   switch (group) {
-    case 1: return launch_typed<E, D, 1>(a, stream);
-    case 2: return launch_typed<E, D, 2>(a, stream);
+    case 1: return launch_split_typed<E, D, 1>(a, stream);
+    case 2: return launch_split_typed<E, D, 2>(a, stream);
     case 4:
-    case 8: return launch_typed<E, D, 4>(a, stream);
+    case 8: return launch_split_typed<E, D, 4>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <typename E>
-hipError_t launch_dim(const DecodeArgs& a, int head_dim, int group, hipStream_t stream) {
+hipError_t launch_dim(const DecodeArgs& a, int head_dim, int group, bool split,
+                      hipStream_t stream) {
   switch (head_dim) {
-    case 64: return launch_hpw<E, 64>(a, group, stream);
-    case 128: return launch_hpw<E, 128>(a, group, stream);
+    case 64: return launch_hpw<E, 64>(a, group, split, stream);
+    case 128: return launch_hpw<E, 128>(a, group, split, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_part(const DecodeArgs& a, int dtype, int head_dim, int group, bool split,
+                       hipStream_t stream) {
+  if (a.num_chunks <= 0 || a.num_seqs <= 0) return hipSuccess;
+  switch (dtype) {
+    case F32::kind: return launch_dim<F32>(a, head_dim, group, split, stream);
+    case BF16::kind: return launch_dim<BF16>(a, head_dim, group, split, stream);
+    case F16::kind: return launch_dim<F16>(a, head_dim, group, split, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
+hipError_t launch_decode_split(const DecodeArgs& a, int dtype, int head_dim, int group,
+                               hipStream_t stream) {
+  return launch_part(a, dtype, head_dim, group, true, stream);
+}
+
+hipError_t launch_decode_merge(const DecodeArgs& a, int dtype, int head_dim, int group,
+                               hipStream_t stream) {
+  return launch_part(a, dtype, head_dim, group, false, stream);
+}
+
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int head_dim, int group,
                          hipStream_t stream) {
-  if (a.num_chunks <= 0 || a.num_seqs <= 0) return hipSuccess;
-  switch (dtype) {
-    case F32::kind: return launch_dim<F32>(a, head_dim, group, stream);
-    case BF16::kind: return launch_dim<BF16>(a, head_dim, group, stream);
-    case F16::kind: return launch_dim<F16>(a, head_dim, group, stream);
-    default: return hipErrorInvalidValue;
-  }
+  const hipError_t e = launch_decode_split(a, dtype, head_dim, group, stream);
+  return e != hipSuccess ? e : launch_decode_merge(a, dtype, head_dim, group, stream);
 }
 
 }  // namespace pa

@@ -27,6 +27,11 @@ struct DecodeArgs {
   float* ws_ml;               // [(R + num_chunks), Hq, 2]  (max, sum) per partial
   float* ws_o;                // [(R + num_chunks), Hq, D]  unnormalised partial outputs
   int32_t* ws_meta;           // [R, 4]: first range, last range (-1: no merge), W, 0
+  // Shared prefix (0 / -1 when absent): the first skip_blocks table entries
+  // of every row are one common prefix, attended separately; request r's
+  // prefix partial (max, sum, output) is in workspace slot prefix_slot0 + r.
+  int32_t skip_blocks;
+  int32_t prefix_slot0;
 };
 
 // Arguments of the MFMA prefill-tile kernel.
@@ -46,6 +51,16 @@ struct PrefillArgs {
   int32_t max_query_len;      // (host) longest chunk: picks the tile shape
   int32_t beside_decode;      // (host) 1: runs concurrently with decode rows
   float scale_log2;
+  // Shared-prefix pass (cascade_rows > 0): one virtual request whose queries
+  // are rows 0 .. cascade_rows - 1 of q and whose keys are the first
+  // cascade_keys positions of block_table row 0, all visible; each row's
+  // partial (max, sum, unnormalised output) goes to workspace slot
+  // prefix_slot0 + row instead of `out`.
+  int32_t cascade_rows;
+  int32_t cascade_keys;
+  int32_t prefix_slot0;
+  float* ws_ml;
+  float* ws_o;
 };
 
 constexpr int kQueriesPerTile = 16;  // fewest query tokens per prefill tile (grid bound)
@@ -63,12 +78,22 @@ hipError_t launch_copy_blocks(void* kv_cache, const int32_t* pairs, int32_t num_
                               int64_t block_bytes, hipStream_t stream);
 
 // dtype: pa_dtype value; head_dim 64 | 128; group = Hq / Hkv in {1,2,4,8}.
+// launch_decode = launch_decode_split then launch_decode_merge.
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int head_dim, int group,
                          hipStream_t stream);
+hipError_t launch_decode_split(const DecodeArgs& a, int dtype, int head_dim, int group,
+                               hipStream_t stream);
+hipError_t launch_decode_merge(const DecodeArgs& a, int dtype, int head_dim, int group,
+                               hipStream_t stream);
 
 hipError_t launch_prefill(const PrefillArgs& a, int dtype, int head_dim, int group,
                           hipStream_t stream);
 
 bool prefill_supported(int dtype, int head_dim, int group);
+
+// Prefill tiles (32 tokens per wave) and the decode split in one launch; the
+// caller launches the decode merge afterwards on the same stream.
+hipError_t launch_fused(const DecodeArgs& da, const PrefillArgs& p, int dtype, int head_dim,
+                        int group, hipStream_t stream);
 
 }  // namespace pa

@@ -1,414 +1,11 @@
-// Prefill-chunk attention over a paged KV cache on gfx950 (MFMA tiles).
-//
-// What it computes ("vllm v1 源码精读（三）" §4.2; "Inside vLLM" §3.4): for a
-// request with q_len > 1 new tokens on top of num_computed cached ones, token
-// i (absolute position pos = num_computed + i) attends keys 0..pos of its own
-// request -- the cached history plus the earlier tokens of the chunk (causal
-// inside the chunk).  Keys are read through the request's block table; the
-// new tokens' K/V were scattered into the cache beforehand.
-//
-// Tiling.  A work-group owns one tile of query tokens of one request and one
-// group of query heads sharing a KV head.  Its waves form KSPLIT key parts of
-// 4 waves; within a part, for GQA group 4, the 4 waves are the 4 query heads
-// of the KV head over the same tokens, so each K/V tile staged in LDS feeds 4
-// heads.  A wave covers NT sub-tiles of 16 tokens: with NT = 2 every K and V
-// fragment read from LDS feeds two matrix-core products.  Keys are processed
-// 64 at a time (four 16-token blocks looked up in the block table), copied
-// from HBM straight into double-buffered LDS by the load unit (16 bytes per
-// lane, no registers), one iteration ahead.  With KSPLIT = 2 the parts split
-// the tile's key range and are merged through LDS at the end (more waves for
-// chunks too short to fill the chip).
-//
-// Matrix-core mapping (v_mfma_f32_16x16x32_{bf16,f16}).  Scores are formed
-// transposed, S^T = K Q^T (keys x tokens), because the accumulator layout of
-// a 16x16 tile gives each lane 4 consecutive keys of ONE token: exactly the
-// operand layout the second product O^T = V^T P^T needs for P^T, so the
-// probabilities go from the softmax to the matrix core without moving across
-// lanes.  Each lane then holds the output of one token, so the online-softmax
-// rescale is a per-lane scalar.  K and V keep their cache layout in LDS
-// (a 16-byte column swizzle per row keeps the reads free of bank
-// conflicts); V^T fragments are read with the transposing LDS read
-// (ds_read_b64_tr_b16: each lane gets 4 keys of one head dimension).  The
-// contraction order inside an MFMA is a permutation of the keys; A and B
-// use the same permutation.
-#include <math.h>
+// Tile-shape choice and launchers of the prefill tile kernel (device code
+// in pa_prefill_impl.h).
 #include <stdlib.h>
 
-#include "pa_common.h"
-#include "pa_kernels.h"
+#include "pa_prefill_impl.h"
 
 namespace pa {
 namespace {
-
-template <typename E>
-__device__ __forceinline__ f32x4_t mfma16x16x32(u32x4_t a, u32x4_t b, f32x4_t c) {
-  if constexpr (E::kind == BF16::kind) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-  } else {
-    typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
-                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
-  }
-}
-
-template <typename E>
-__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-  return E::kind == BF16::kind ? pack_bf16(lo, hi) : pack_f16(lo, hi);
-}
-
-constexpr int kKeysPerIter = 64;  // keys staged per iteration (4 paged blocks)
-
-template <int D>
-struct TileShape {
-  static constexpr int ROWB = D * 2;                 // bytes of one token's head row
-  static constexpr int CPR = ROWB / 16;              // 16-byte columns per row
-  static constexpr int RPG = 256 / ROWB;             // rows per 256 bytes (64 banks)
-  static constexpr int RPI = 1024 / ROWB;            // rows per 1 KiB wave copy
-  static constexpr int NKS = D / 32;                 // MFMA k-steps of Q K^T
-  static constexpr int NMT = D / 16;                 // 16-dim tiles of the output
-  static constexpr int KBUF = kKeysPerIter * ROWB;
-  static constexpr int STAGE = 2 * KBUF;             // one LDS stage: K rows then V rows
-  // Physical 16-byte column of logical column c in LDS row `row`.  K is read
-  // 16 rows x one column at a time (16 bytes per lane): fk spreads those 16
-  // reads over all 64 banks.  V is read 8 rows x two adjacent columns at a
-  // time (8 bytes per lane): fv spreads those 16 pieces over all banks.
-  static __device__ __forceinline__ int fk(int row) { return (row / RPG) % CPR; }
-  static __device__ __forceinline__ int fv(int row) { return 2 * ((row / RPG) % (CPR / 2)); }
-};
-
-// Zero row: the copy source for key rows past the tile's last key, so that
-// those rows hold zeros (V must not carry a stale NaN into a product with a
-// zero probability).
-__device__ __attribute__((aligned(256))) uint8_t g_zero_row[256];
-
-// Tokens per tile for a launch configuration.
-template <int WPW, int NT>
-constexpr int tile_tokens() {
-  return 16 * NT * (4 / WPW);
-}
-
-template <typename E, int D, int WPW, int NT, int KSPLIT>
-__global__ __launch_bounds__(256 * KSPLIT) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_tile_kernel(PrefillArgs a) {
-  using S = TileShape<D>;
-  constexpr int QT = tile_tokens<WPW, NT>();   // tokens per tile
-  // [part][stage]: each part's next 64 keys are copied in while the current
-  // ones are used.  Two stages keep a 4-wave work-group at 64 KiB of LDS, so
-  // two work-groups share a CU and their barriers do not couple (a third
-  // stage, or 8-wave groups sharing the stages, left one group per CU and
-  // measured slower).
-  constexpr int NSTAGE = 2;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[KSPLIT][NSTAGE][S::STAGE];
-  __shared__ int s_tile[2];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = uniform(tid >> 6);
-  const int part = wave >> 2;                  // key part
-  const int w4 = wave & 3;                     // wave within the part
-  const int group = a.num_q_heads / a.num_kv_heads;
-  const int hg = group / WPW;
-  const int h = blockIdx.y / hg;
-  const int hs = blockIdx.y - h * hg;
-
-  // ---- which request / tile this work-group owns
-  if (wave == 0) {
-    int found_r = -1, found_t = 0, running = 0;
-    const int want = blockIdx.x;
-    for (int base = 0; base < a.num_seqs && found_r < 0; base += kWave) {
-      const int r = base + lane;
-      int nt = 0;
-      if (r < a.num_seqs) {
-        const int ql = a.qsl[r + 1] - a.qsl[r];
-        nt = ql > 1 ? (ql + QT - 1) / QT : 0;
-      }
-      const int incl = wave_incl_scan(nt) + running;
-      const int excl = incl - nt;
-      const uint64_t hit = __ballot(nt > 0 && want >= excl && want < incl);
-      if (hit) {
-        const int src = __builtin_ctzll(hit);
-        found_r = base + src;
-        // a request's tiles are handed out last-first: the tiles with the
-        // most keys start early and the short ones fill in behind them
-        found_t = readlane(incl, src) - 1 - want;
-      }
-      running = readlane(incl, kWave - 1);
-    }
-    if (lane == 0) {
-      s_tile[0] = found_r;
-      s_tile[1] = found_t;
-    }
-  }
-  __syncthreads();
-  const int r = uniform(s_tile[0]);
-  if (r < 0) return;
-  const int tile = uniform(s_tile[1]);
-
-  const int q0 = a.qsl[r];
-  const int qlen = a.qsl[r + 1] - q0;
-  const int nc = a.num_computed[r];
-  const int L = a.seq_lens[r];
-  const int tile_start = tile * QT;
-  const int tile_valid = min(QT, qlen - tile_start);
-  const int kend = min(L, nc + tile_start + tile_valid);  // keys this tile needs
-  const int niter = (kend + kKeysPerIter - 1) / kKeysPerIter;
-  const int n0 = (niter + KSPLIT - 1) / KSPLIT;           // trips of every part
-  const int it_begin = part * n0;
-  const int my_iters = max(0, min(n0, niter - it_begin));
-
-  const int hw = w4 % WPW;                     // head within the group
-  const int sub = w4 / WPW;                    // token group of this wave
-  const int hq = h * group + hs * WPW + hw;
-  const int n = lane & 15;                     // token column of this lane
-  const int g = lane >> 4;                     // lane group
-
-  // NT sub-tiles of 16 tokens: sub-tile j starts at token sub_start[j]
-  int sub_start[NT], sub_valid[NT], pos[NT];
-  u32x4_t qf[NT][S::NKS];                      // Q^T fragments: token n, dims 32s + 8g .. +8
-#pragma unroll
-  for (int j = 0; j < NT; ++j) {
-    sub_start[j] = tile_start + (sub * NT + j) * 16;
-    sub_valid[j] = max(0, min(16, qlen - sub_start[j]));
-    pos[j] = nc + sub_start[j] + min(n, max(sub_valid[j] - 1, 0));  // last visible key
-    const bool ok = n < sub_valid[j];
-    const uint8_t* qp = static_cast<const uint8_t*>(a.q) +
-                        ((int64_t)(q0 + sub_start[j] + n) * a.num_q_heads + hq) * S::ROWB +
-                        g * 16;
-#pragma unroll
-    for (int s = 0; s < S::NKS; ++s) {
-      const u32x4_t z = {0u, 0u, 0u, 0u};
-      qf[j][s] = ok ? load16(qp + s * 64) : z;
-    }
-  }
-
-  const int64_t tok_stride = (int64_t)a.num_kv_heads * S::ROWB;
-  const int64_t half_stride = kBlockSize * tok_stride;
-  const int64_t blk_stride = 2 * half_stride;
-  const uint8_t* kvh = static_cast<const uint8_t*>(a.kv) + (int64_t)h * S::ROWB;
-  const int32_t* bt = a.block_table + (int64_t)r * a.bt_stride;
-
-  // id of the paged block this wavefront stages in (global) iteration it
-  const int nb_need = (kend + kBlockSize - 1) / kBlockSize;
-  auto block_id = [&](int it) {
-    const int lb = it * 4 + w4;
-    return lb < nb_need ? load_scalar(bt + lb) : 0;
-  };
-
-  // Staging: wavefront w4 of a part copies paged block w4 of the part's
-  // iteration (keys 16 w4 .. 16 w4 + 15), so its block id is wave-uniform.
-  // Each 1 KiB copy moves RPI rows: lane l lands at LDS byte 16 l of the
-  // copy, so it fetches row l / CPR at the global column that the row's
-  // swizzle puts in slot l % CPR.
-  constexpr int CPB = 16 * S::ROWB / 1024;     // copies per block half
-  uint32_t goff[2][CPB];                       // per-lane byte offset inside a block
-  uint32_t zoff[2][CPB];                       // the same column in the zero row
-#pragma unroll
-  for (int hv = 0; hv < 2; ++hv)
-#pragma unroll
-    for (int i = 0; i < CPB; ++i) {
-      const int rib = S::RPI * i + lane / S::CPR;       // row in block
-      const int row = 16 * w4 + rib;                    // row in stage
-      const int col = (lane % S::CPR) ^ (hv ? S::fv(row) : S::fk(row));
-      goff[hv][i] = (uint32_t)(hv * half_stride + rib * tok_stride + col * 16);
-      zoff[hv][i] = (uint32_t)(col * 16);
-    }
-  auto dma = [&](int it, int phys, int buf) {
-    const uint8_t* blk = kvh + (int64_t)phys * blk_stride;
-    const int key0 = it * kKeysPerIter + 16 * w4;
-#pragma unroll
-    for (int hv = 0; hv < 2; ++hv) {
-#pragma unroll
-      for (int i = 0; i < CPB; ++i) {
-        const int rib = S::RPI * i + lane / S::CPR;
-        const uint8_t* src = key0 + rib < kend ? blk + goff[hv][i] : g_zero_row + zoff[hv][i];
-        uint8_t* dst = &lds[part][buf][hv * S::KBUF + (16 * w4 + S::RPI * i) * S::ROWB];
-        __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
-      }
-    }
-  };
-
-  f32x4_t acc[NT][S::NMT];
-  float m[NT], lsum[NT];
-#pragma unroll
-  for (int j = 0; j < NT; ++j) {
-    m[j] = -INFINITY;
-    lsum[j] = 0.f;
-#pragma unroll
-    for (int mt = 0; mt < S::NMT; ++mt) acc[j][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  }
-
-  // One 64-key iteration from LDS stage `buf`: S^T, online softmax, O^T.
-  auto compute = [&](int it, int buf) {
-    const uint8_t* lds_kc = lds[part][buf];
-    const uint8_t* lds_vc = lds[part][buf] + S::KBUF;
-    // ---- S^T for 64 keys x 16 tokens per sub-tile: 4 tiles of 16 keys
-    f32x4_t st[NT][4];
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-#pragma unroll
-      for (int j = 0; j < NT; ++j) st[j][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < S::NKS; ++s) {
-        const int row = 16 * tt + n;
-        const u32x4_t ka = *reinterpret_cast<const u32x4_t*>(
-            lds_kc + row * S::ROWB + (((4 * s + g) ^ S::fk(row)) << 4));
-#pragma unroll
-        for (int j = 0; j < NT; ++j) st[j][tt] = mfma16x16x32<E>(ka, qf[j][s], st[j][tt]);
-      }
-    }
-    const int key0 = it * kKeysPerIter;
-    u32x4_t pb[NT][2];
-#pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      // ---- causal mask on diagonal tiles; scores stay unscaled (the scale,
-      // with log2(e) folded in, is applied inside the exponent below)
-      float (&x)[4][4] = *reinterpret_cast<float (*)[4][4]>(&st[j][0]);
-      if (key0 + kKeysPerIter - 1 > nc + sub_start[j]) {
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = key0 + 16 * tt + 4 * g + i;
-            x[tt][i] = key <= pos[j] ? x[tt][i] : -INFINITY;
-          }
-      }
-      float mx = x[0][0];
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, x[tt][i]);
-      mx = fmaxf(mx, shfl_xor(mx, 16));
-      mx = fmaxf(mx, shfl_xor(mx, 32));
-      mx *= a.scale_log2;  // scale > 0: max of scaled = scaled max
-      const float mn = fmaxf(m[j], mx);
-      const bool grow = mn > m[j] + 8.f;
-      if (__any(grow)) {
-        const float mu = grow ? mn : m[j];
-        const float alpha = (mu == m[j]) ? 1.f : __builtin_amdgcn_exp2f(m[j] - mu);
-        lsum[j] *= alpha;
-#pragma unroll
-        for (int mt = 0; mt < S::NMT; ++mt) acc[j][mt] *= alpha;
-        m[j] = mu;
-      }
-      const float ms = (m[j] == -INFINITY) ? 0.f : m[j];
-      float p[4][4];
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[tt][i] = __builtin_amdgcn_exp2f(fmaf(x[tt][i], a.scale_log2, -ms));
-          lsum[j] += p[tt][i];
-        }
-      // lane group g holds keys 32s2 + 4g + (0..3) and 32s2 + 16 + 4g + (0..3)
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        pb[j][s2][0] = pack2<E>(p[2 * s2][0], p[2 * s2][1]);
-        pb[j][s2][1] = pack2<E>(p[2 * s2][2], p[2 * s2][3]);
-        pb[j][s2][2] = pack2<E>(p[2 * s2 + 1][0], p[2 * s2 + 1][1]);
-        pb[j][s2][3] = pack2<E>(p[2 * s2 + 1][2], p[2 * s2 + 1][3]);
-      }
-    }
-    // ---- O^T += V^T P^T, 32 keys per MFMA
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-      for (int mt = 0; mt < S::NMT; ++mt) {
-        // lane (n, g): dim 16 mt + n, keys 32 s2 + 4 g + (0..3) and
-        // 32 s2 + 16 + 4 g + (0..3); the transposing read hands lane
-        // 4 q + c of each 16-lane group element c of the 8 bytes that lane
-        // 4 i + q points at, for i = 0..3 (i = key, q = dim quad)
-        const int e = 4 * mt + (n & 3);                  // 8-byte piece (4 dims)
-        u32x4_t va;
-#pragma unroll
-        for (int hv = 0; hv < 2; ++hv) {
-          const int row = 32 * s2 + 16 * hv + 4 * g + (n >> 2);
-          const uint8_t* vp = lds_vc + row * S::ROWB + ((((e >> 1) ^ S::fv(row)) << 4) | ((e & 1) << 3));
-          typedef short v4s_t __attribute__((ext_vector_type(4)));
-          const v4s_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) v4s_t*)(vp));
-          const uint2 w = __builtin_bit_cast(uint2, t);
-          va[2 * hv] = w.x;
-          va[2 * hv + 1] = w.y;
-        }
-#pragma unroll
-        for (int j = 0; j < NT; ++j) acc[j][mt] = mfma16x16x32<E>(va, pb[j][s2], acc[j][mt]);
-      }
-  };
-
-  // Every part runs n0 loop trips in lockstep, one barrier per trip; a part
-  // with fewer iterations idles on its last trips.  Trip t waits for its own
-  // copies of iteration it_begin + t (the only loads in flight), meets the
-  // other waves at the barrier (after which every copy of that iteration has
-  // landed and every wave is done with the other stage), starts the copies
-  // of the next iteration into the other stage, and computes.
-  if (my_iters > 0) dma(it_begin, block_id(it_begin), 0);
-  int id_next = block_id(it_begin + 1);
-  for (int t = 0; t < n0; ++t) {
-    const int buf = t & 1;
-    const int phys = id_next;
-    id_next = block_id(it_begin + t + 2);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (t + 1 < my_iters) dma(it_begin + t + 1, phys, buf ^ 1);
-    if (t < my_iters) compute(it_begin + t, buf);
-  }
-  if constexpr (KSPLIT == 2) __syncthreads();  // stages are reused for the merge
-
-#pragma unroll
-  for (int j = 0; j < NT; ++j) {
-    lsum[j] += shfl_xor(lsum[j], 16);
-    lsum[j] += shfl_xor(lsum[j], 32);
-  }
-  if constexpr (KSPLIT == 2) {
-    // ---- merge the parts: part 1 leaves (max, row sum, O^T) in its LDS stages
-    constexpr int NF = NT * (S::NMT * 4 + 2);  // floats per lane
-    static_assert(4 * kWave * NF * 4 <= NSTAGE * S::STAGE, "merge buffer must fit in part 1's stages");
-    float* xch = reinterpret_cast<float*>(&lds[1][0][0]) + (w4 * kWave + lane) * NF;
-    if (part == 1) {
-#pragma unroll
-      for (int j = 0; j < NT; ++j) {
-#pragma unroll
-        for (int mt = 0; mt < S::NMT; ++mt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) xch[j * (S::NMT * 4 + 2) + 4 * mt + i] = acc[j][mt][i];
-        xch[j * (S::NMT * 4 + 2) + S::NMT * 4] = m[j];
-        xch[j * (S::NMT * 4 + 2) + S::NMT * 4 + 1] = lsum[j];
-      }
-    }
-    __syncthreads();
-    if (part == 1) return;
-#pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      const float* src = xch + j * (S::NMT * 4 + 2);
-      const float m1 = src[S::NMT * 4], l1 = src[S::NMT * 4 + 1];
-      const float M = fmaxf(m[j], m1);         // m is finite: key 0 is visible
-      const float a0 = __builtin_amdgcn_exp2f(m[j] - M);
-      const float a1 = (m1 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m1 - M);
-      lsum[j] = lsum[j] * a0 + l1 * a1;
-#pragma unroll
-      for (int mt = 0; mt < S::NMT; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[j][mt][i] = acc[j][mt][i] * a0 + src[4 * mt + i] * a1;
-    }
-  }
-
-  // ---- normalise and store: lane holds dims 16mt + 4g + (0..3) of token n
-#pragma unroll
-  for (int j = 0; j < NT; ++j) {
-    if (n < sub_valid[j]) {
-      const float inv = 1.f / lsum[j];
-      uint8_t* op = static_cast<uint8_t*>(a.out) +
-                    ((int64_t)(q0 + sub_start[j] + n) * a.num_q_heads + hq) * S::ROWB + g * 8;
-#pragma unroll
-      for (int mt = 0; mt < S::NMT; ++mt) {
-        uint2 w;
-        w.x = pack2<E>(acc[j][mt][0] * inv, acc[j][mt][1] * inv);
-        w.y = pack2<E>(acc[j][mt][2] * inv, acc[j][mt][3] * inv);
-        *reinterpret_cast<uint2*>(op + mt * 32) = w;
-      }
-    }
-  }
-}
 
 // Tile shape of a launch.
 //   0: 16 tokens per wave, two key parts of 4 waves: short chunks alone, which

@@ -85,9 +85,13 @@ class Device:
         import paged_kv_attention_07_amd as pa
         pa.pa_reshape_and_cache(self.k_new, self.v_new, self.kv, slots)
 
-    def attend(self, num_splits=0, force_mixed=False):
+    def attend(self, num_splits=0, force_mixed=False, shared_prefix=None):
         import paged_kv_attention_07_amd as pa
         w = self.w
+        if shared_prefix is not None:
+            return pa.pa_attention_decode_shared_prefix(
+                self.q, self.kv, self.block_table, self.seq_lens, w.scale, w.max_seq_len,
+                shared_prefix, num_splits=num_splits)
         if w.is_decode_only and not force_mixed:
             return pa.pa_attention_decode(self.q, self.kv, self.block_table, self.seq_lens,
                                           w.scale, w.max_seq_len, num_splits=num_splits)
@@ -96,7 +100,7 @@ class Device:
                                      num_splits=num_splits)
 
 
-def run_step(w, *, poison=True, num_splits=0, force_mixed=False):
+def run_step(w, *, poison=True, num_splits=0, force_mixed=False, shared_prefix=None):
     """Slot mapping, scatter and attention on the GPU for one step of `w`.
     Returns (pool_before, gpu_slots, gpu_pool, gpu_out) as host arrays."""
     import torch
@@ -104,7 +108,7 @@ def run_step(w, *, poison=True, num_splits=0, force_mixed=False):
     dev = Device(w, pool)
     slots = dev.slot_mapping()
     dev.scatter(slots)
-    out = dev.attend(num_splits=num_splits, force_mixed=force_mixed)
+    out = dev.attend(num_splits=num_splits, force_mixed=force_mixed, shared_prefix=shared_prefix)
     torch.cuda.synchronize()
     return pool, slots.cpu().numpy(), from_device(dev.kv, w.dtype), from_device(out, w.dtype)
 

@@ -335,8 +335,10 @@ def test_prefill_8k_sampled(monkeypatch):
 
 @pytest.mark.parametrize("shape", [0, 1])
 def test_mixed_all_tile_shapes(shape, monkeypatch):
-    """Every prefill tile shape on the small mixed batch and on odd groupings."""
+    """Every prefill tile shape on the small mixed batch and on odd groupings
+    (tiles launched on their own, so the shape knob applies)."""
     monkeypatch.setenv("PA_PREFILL_SHAPE", str(shape))
+    monkeypatch.setenv("PA_MIXED_OVERLAP", "0")
     full_check(workload("mixed_bf16_small"))
     lens = [40, 17, 300, 5, 64, 129, 1, 700]
     q_lens = [40, 2, 33, 1, 16, 100, 1, 64]
@@ -423,12 +425,73 @@ def test_copy_on_write_parallel_sampling():
 
 @pytest.mark.parametrize("overlap", ["0", "1"])
 def test_mixed_with_and_without_concurrent_tiles(overlap, monkeypatch):
-    """The mixed entry runs prefill tiles on a side stream beside the decode
-    rows by default; both schedules give the oracle's rows, including the
-    one-request batch (no side stream) and a repeat on the same buffers."""
+    """The mixed entry runs prefill tiles and decode ranges in one launch by
+    default; both schedules give the oracle's rows, including the one-request
+    batch (tiles alone)."""
     monkeypatch.setenv("PA_MIXED_OVERLAP", overlap)
     full_check(workload("mixed_bf16_small"))
     lens = [300, 40, 129, 2000, 17]
     q_lens = [100, 1, 64, 1, 1]
     full_check(_variant("bf16", 32, 8, 128, lens, seed=91, q_lens=q_lens))
     full_check(_variant("f16", 8, 2, 64, [77], seed=92, q_lens=[60]))
+
+
+# --------------------------------------------------------------------------
+# decode with a shared prompt prefix read once (cascade)
+# --------------------------------------------------------------------------
+
+
+def test_shared_prefix_small_config():
+    w = workload("prefix_shared_small")
+    full_check(w, shared_prefix=w.meta["shared_prefix_blocks"])
+
+
+@pytest.mark.parametrize("splits", [0, 1, 3, 40])
+def test_shared_prefix_full_config_sampled(splits):
+    """The 256-request batch with a 64-block shared prefix, 32 requests
+    compared with the oracle (all 256 checked for finite output)."""
+    w = workload("prefix_shared_decode_bf16")
+    pool, _, _, out = gu.run_step(w, shared_prefix=w.meta["shared_prefix_blocks"],
+                                  num_splits=splits)
+    rows = np.arange(0, 256, 8)
+    r_slots, r_pool, ref = gu.oracle_step(w, pool, requests=rows)
+    assert np.all(np.isfinite(oracle.decode_bits(out, w.dtype)))
+    gu.check_close(w, out, ref, rows=gu.rows_of(w, rows), what="shared prefix")
+
+
+@pytest.mark.parametrize("dtype,Hq,Hkv,D", [("bf16", 32, 8, 128), ("bf16", 8, 8, 128),
+                                            ("f16", 16, 2, 64), ("bf16", 8, 2, 64)])
+def test_shared_prefix_edges(dtype, Hq, Hkv, D):
+    """Suffixes of every kind after a 5-block prefix: empty (the context is
+    exactly the prefix), one key, a partial last block, long; plus the
+    prefix-free fallback (P = 0), all against the oracle."""
+    P = 5
+    lens = [P * 16, P * 16 + 1, P * 16 + 7, P * 16 + 16, P * 16 + 300, P * 16 + 33, 2000]
+    w = build_workload(f"sp_{dtype}_{Hq}x{Hkv}x{D}", dtype=dtype, num_q_heads=Hq,
+                       num_kv_heads=Hkv, head_dim=D, num_blocks=600,
+                       requests=[(L - 1, 1) for L in lens], seed=61 + Hq + D,
+                       shared_prefix_blocks=P)
+    full_check(w, shared_prefix=P)
+    full_check(w, shared_prefix=0)
+    full_check(w, shared_prefix=P, num_splits=2)
+
+
+@pytest.mark.parametrize("name,P", [("prefix_shared_small", 4), ("sp_edges", 5)])
+def test_shared_prefix_matches_plain_decode(name, P):
+    """Both decode entries on the same batch agree to a few bf16 ulps of the
+    output (each is a bf16-rounded evaluation of the same softmax).  This
+    catches keys past the prefix leaking into the prefix pass (rows there
+    sit after the keys they may see), which stays near the oracle tolerance
+    but is several times the rounding."""
+    if name == "sp_edges":
+        lens = [P * 16, P * 16 + 1, P * 16 + 7, P * 16 + 16, P * 16 + 300, P * 16 + 33, 2000]
+        w = build_workload("sp_edges", dtype="bf16", num_q_heads=8, num_kv_heads=8, head_dim=128,
+                           num_blocks=600, requests=[(L - 1, 1) for L in lens], seed=197,
+                           shared_prefix_blocks=P)
+    else:
+        w = workload(name)
+    dev = gu.Device(w, gu.poisoned_pool(w))
+    dev.scatter(dev.slot_mapping())
+    a = oracle.decode_bits(gu.from_device(dev.attend(), w.dtype), w.dtype)
+    b = oracle.decode_bits(gu.from_device(dev.attend(shared_prefix=P), w.dtype), w.dtype)
+    assert np.max(np.abs(a - b)) <= 6e-3

@@ -230,6 +230,7 @@ def build_workload(
 
     meta = dict(meta or {})
     meta["blocks_used"] = int(need)
+    meta["shared_prefix_blocks"] = int(S)
     if not values:
         return Workload(
             name=name, dtype=dtype, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
