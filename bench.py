@@ -454,7 +454,8 @@ def main():
     head_key = "decode" if "decode" in results else next(iter(results))
     head = results[head_key]
     w, c = head["w"], head["counts"]
-    step_bytes = c["attn_logical"] + c["scatter"] + c["slots"]
+    attn_bytes = c["attn_unique"] if head_key in ("prefix", "prefixplain") else c["attn_logical"]
+    step_bytes = attn_bytes + c["scatter"] + c["slots"]
     value = step_bytes / (head["ms_step"] * 1e-3) / 1e9
     achieved = c["attn_logical"] / (head["attn_ms_avg"] * 1e-3) / 1e9
     launch = {"avg_launch_us": round(head["attn_ms_avg"] * 1e3, 2),
