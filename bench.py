@@ -2,10 +2,15 @@
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
                     [--extra] [--only decode|mixed|prefix|long] [--splits S]
+                    [--separate]
 
 A step is one pass of the whole path over one batch: slot mapping of the new
 tokens, reshape_and_cache of their K/V, then attention (decode for the decode
-batch, mixed for the chunked-prefill batch).  Inputs are resident in HBM
+batch, mixed for the chunked-prefill batch).  By default the three run as one
+attention launch (pa_cache_and_attend_*: the launch stores the new tokens and
+reads them from the input rows) plus the split merge; --separate times the
+three calls one after the other.  The shared-prefix leg always runs them
+apart (its entry takes the cache as written).  Inputs are resident in HBM
 before timing starts; several copies of the KV pool are rotated so that
 successive steps do not hit in the 256 MB Infinity Cache.
 
@@ -115,10 +120,12 @@ def alg_counts(w):
 class Stepper:
     """Device copies of one workload and the step of the hot path over them."""
 
-    def __init__(self, w, rotations: int, splits: int, shared_prefix: int = 0):
+    def __init__(self, w, rotations: int, splits: int, shared_prefix: int = 0,
+                 fused: bool = True):
         import torch
         import paged_kv_attention_07_amd as pa
         self.pa, self.torch, self.w, self.splits = pa, torch, w, splits
+        self.fused = fused and not shared_prefix
         tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[w.dtype]
 
         def dev(a):
@@ -164,6 +171,23 @@ class Stepper:
     def step(self, i, ev=None):
         pa, w = self.pa, self.w
         kv = self.pools[i % len(self.pools)]
+        if self.fused:
+            if ev is not None:
+                ev[0].record()
+            if self.decode:
+                pa.pa_cache_and_attend_decode(self.q, self.kn, self.vn, kv, self.bt, self.sl,
+                                              w.scale, w.max_seq_len, out=self.out,
+                                              slot_mapping=self.slots, workspace=self.ws,
+                                              num_splits=self.splits)
+            else:
+                pa.pa_cache_and_attend_mixed(self.q, self.kn, self.vn, kv, self.bt, self.sl,
+                                             self.qsl, self.nc, w.scale, w.max_query_len,
+                                             w.max_seq_len, out=self.out,
+                                             slot_mapping=self.slots, workspace=self.ws,
+                                             num_splits=self.splits)
+            if ev is not None:
+                ev[1].record()
+            return
         pa.pa_compute_slot_mapping(self.bt, self.qsl, self.nc, w.num_tokens, w.block_size,
                                    out=self.slots)
         pa.pa_reshape_and_cache(self.kn, self.vn, kv, self.slots)
@@ -293,11 +317,12 @@ def measure(name, args, rotations, shared_prefix=False):
     print(f"[bench] {name}: generated in {time.perf_counter() - t0:.1f}s", file=sys.stderr,
           flush=True)
     st = Stepper(w, rotations, args.splits,
-                 w.meta.get("shared_prefix_blocks", 0) if shared_prefix else 0)
+                 w.meta.get("shared_prefix_blocks", 0) if shared_prefix else 0,
+                 fused=not args.separate)
     ms_step, attn_ms = st.run(args.steps, args.warmup)
     c = alg_counts(w)
     attn_avg = float(np.mean(attn_ms))
-    res = dict(w=w, counts=c, ms_step=ms_step, attn_ms_avg=attn_avg,
+    res = dict(w=w, counts=c, ms_step=ms_step, attn_ms_avg=attn_avg, fused=st.fused,
                attn_ms_p10=float(np.percentile(attn_ms, 10)),
                attn_ms_p90=float(np.percentile(attn_ms, 90)))
     print(f"[bench] {name}: {ms_step * 1e3:.1f} us/step, attention {attn_avg * 1e3:.1f} us",
@@ -418,6 +443,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--separate", action="store_true",
+                    help="slot mapping, reshape_and_cache and attention as three calls "
+                         "(default: one cache-and-attend launch)")
     ap.add_argument("--extra", action="store_true", help="also time the prefix-shared and "
                     "long-context decode batches")
     ap.add_argument("--only", choices=sorted(WORKLOADS) + ["copy", "serve"], default=None)
@@ -466,16 +494,22 @@ def main():
         roofline = {"bound": "mfma", "achieved": round(tflops, 1),
                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
-                    "kernel": "pa_attention_mixed (prefill_tile_kernel)",
+                    "kernel": ("pa_cache_and_attend_mixed" if head["fused"]
+                               else "pa_attention_mixed") + " (prefill_tile_kernel)",
                     "alg_flops_per_launch": int(c["chunk_flops"]), **launch}
     else:
         # shared-prefix batches are priced on unique bytes (the prefix once)
         alg = c["attn_unique"] if head_key in ("prefix", "prefixplain") else c["attn_logical"]
+        if head["fused"]:
+            # the launch also reads the new K/V rows, stores them and the slots
+            alg += c["scatter"] + 8 * w.num_tokens
         achieved = alg / (head["attn_ms_avg"] * 1e-3) / 1e9
-        kernel = {"decode": "pa_attention_decode (decode_split_kernel + decode_merge_kernel)",
+        dec = "pa_cache_and_attend_decode" if head["fused"] else "pa_attention_decode"
+        kernel = {"decode": dec + " (decode_split_kernel + decode_merge_kernel)",
                   "prefix": "pa_attention_decode_shared_prefix",
-                  "prefixplain": "pa_attention_decode", "long": "pa_attention_decode",
-                  "mixed": "pa_attention_mixed"}.get(head_key, head_key)
+                  "prefixplain": dec, "long": dec,
+                  "mixed": "pa_cache_and_attend_mixed" if head["fused"]
+                  else "pa_attention_mixed"}.get(head_key, head_key)
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                     "traffic": recorded_traffic("decode_split_kernel")
@@ -498,7 +532,9 @@ def main():
         "config": {"workload": w.name, "description": DESCR.get(w.name, ""),
                    "num_seqs": w.num_seqs, "query_tokens": w.num_tokens,
                    "keys": int(w.seq_lens.sum()), "pool_blocks": w.num_blocks,
-                   "step": "slot_mapping + reshape_and_cache + attention",
+                   "step": ("slot_mapping + reshape_and_cache + attention in one launch "
+                            "(pa_cache_and_attend_*) + split merge" if head["fused"] else
+                            "slot_mapping + reshape_and_cache + attention (three calls)"),
                    "pool_rotation": rot, "num_splits": args.splits or "auto"},
         "pct_peak_hbm": round(100 * value / HBM_PEAK_GBS, 2),
         "roofline": roofline,
@@ -543,6 +579,7 @@ def main():
             rw, rc = r["w"], r["counts"]
             line[f"{key}_decode"] = {
                 "entry": ("pa_attention_decode_shared_prefix" if key == "prefix"
+                          else "pa_cache_and_attend_decode" if r["fused"]
                           else "pa_attention_decode"),
                 "workload": rw.name,
                 "attention_avg_us": round(r["attn_ms_avg"] * 1e3, 2),

@@ -222,7 +222,8 @@ int pa_attention_decode_shared_prefix(void* out, const void* q, const void* kv_c
  *   workspace           >= pa_attention_workspace_size(num_seqs, num_tokens,
  *                       ..., max_seq_len, max_query_len, num_splits) bytes.
  *   The new tokens' K/V must already be in the cache (pa_reshape_and_cache
- *   on the same stream first, as in [P1] §3.3.3).
+ *   on the same stream first, as in [P1] §3.3.3), or use
+ *   pa_cache_and_attend_mixed, which stores them in the same launch.
  */
 int pa_attention_mixed(void* out, const void* q, const void* kv_cache,
                        int64_t num_blocks, int32_t block_size,
@@ -234,6 +235,52 @@ int pa_attention_mixed(void* out, const void* q, const void* kv_cache,
                        int32_t max_seq_len, int32_t num_q_heads, float scale,
                        void* workspace, size_t workspace_bytes,
                        int32_t num_splits, void* stream);
+
+/*
+ * pa_cache_and_attend_decode / pa_cache_and_attend_mixed -- one layer's
+ * step in one attention launch: the slot of every new token ([P4] §3.4), the
+ * store of its K/V into the cache by that slot, and the attention that reads
+ * it ([P1] §3.3.3: the new keys/values are written before attention uses
+ * them).  Results are those of the three calls on one stream
+ *     pa_compute_slot_mapping -> pa_reshape_and_cache -> pa_attention_decode
+ *                                                        (or _mixed)
+ * with the same arguments: `out` as the attention call, kv_cache holding
+ * key[t] / value[t] at token t's position (bit-exact), and slot_mapping[t]
+ * (when not NULL) the slot written.  Inside the launch the new rows are read
+ * from key / value directly and each is stored into the cache once, so the
+ * stores and the reads do not depend on each other.
+ *
+ *   key, value     [rows, num_kv_heads, head_dim], cache dtype, 16-byte
+ *                  aligned; rows = num_seqs (decode) or num_tokens (mixed).
+ *   slot_mapping   out [rows] int64, or NULL.
+ *   Decode: request r's new token is row r at position seq_lens[r] - 1
+ *   (num_computed = seq_lens - 1); a row with seq_lens[r] = 0 has none.
+ *   Mixed: token t = query_start_loc[r] + i sits at num_computed_tokens[r] + i.
+ *   Preconditions, besides the attention call's: table entries for every new
+ *   position are valid block ids; the new tokens' slots are distinct and none
+ *   is a key that another request reads in the same call (a request writes
+ *   only into blocks it does not share, as copy-on-write guarantees).
+ *   Workspace and other arguments as the attention calls.
+ */
+int pa_cache_and_attend_decode(void* out, const void* q, const void* key, const void* value,
+                               void* kv_cache, int64_t num_blocks, int32_t block_size,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                               const int32_t* block_table, int32_t block_table_stride,
+                               const int32_t* seq_lens, int64_t* slot_mapping,
+                               int32_t num_seqs, int32_t max_seq_len, int32_t num_q_heads,
+                               float scale, void* workspace, size_t workspace_bytes,
+                               int32_t num_splits, void* stream);
+
+int pa_cache_and_attend_mixed(void* out, const void* q, const void* key, const void* value,
+                              void* kv_cache, int64_t num_blocks, int32_t block_size,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                              const int32_t* block_table, int32_t block_table_stride,
+                              const int32_t* seq_lens, const int32_t* query_start_loc,
+                              const int32_t* num_computed_tokens, int64_t* slot_mapping,
+                              int32_t num_seqs, int32_t num_tokens, int32_t max_query_len,
+                              int32_t max_seq_len, int32_t num_q_heads, float scale,
+                              void* workspace, size_t workspace_bytes, int32_t num_splits,
+                              void* stream);
 
 #ifdef __cplusplus
 }

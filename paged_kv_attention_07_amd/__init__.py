@@ -18,6 +18,7 @@ __all__ = [
     "pa_compute_slot_mapping", "pa_reshape_and_cache", "pa_copy_blocks",
     "pa_attention_workspace_size", "pa_attention_decode", "pa_attention_mixed",
     "pa_attention_decode_shared_prefix", "pa_attention_decode_shared_prefix_workspace_size",
+    "pa_cache_and_attend_decode", "pa_cache_and_attend_mixed",
     "pa_status_string", "pa_version",
 ]
 
@@ -72,6 +73,18 @@ lib.pa_attention_decode_shared_prefix.argtypes = [
     _vp, _i32, _vp, _i32, _i32, _i32, _f32,          # bt stride seq_lens R max_L Hq scale
     _i32, _vp, _sz, _i32, _vp]                       # prefix ws ws_bytes splits stream
 lib.pa_attention_decode_shared_prefix.restype = ctypes.c_int
+
+lib.pa_cache_and_attend_decode.argtypes = [
+    _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32,  # out q key value kv NB B Hkv D dtype
+    _vp, _i32, _vp, _vp, _i32, _i32, _i32, _f32,              # bt stride seq_lens slots R max_L Hq scale
+    _vp, _sz, _i32, _vp]                                      # ws ws_bytes splits stream
+lib.pa_cache_and_attend_decode.restype = ctypes.c_int
+lib.pa_cache_and_attend_mixed.argtypes = [
+    _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32,  # out q key value kv NB B Hkv D dtype
+    _vp, _i32, _vp, _vp, _vp, _vp, _i32, _i32,                # bt stride seq_lens qsl nc slots R T
+    _i32, _i32, _i32, _f32,                                   # max_q max_L Hq scale
+    _vp, _sz, _i32, _vp]                                      # ws ws_bytes splits stream
+lib.pa_cache_and_attend_mixed.restype = ctypes.c_int
 
 PA_F32, PA_BF16, PA_F16 = 0, 1, 2
 DTYPE_CODES = {"f32": PA_F32, "bf16": PA_BF16, "f16": PA_F16}
@@ -278,4 +291,74 @@ def pa_attention_mixed(q, kv_cache, block_table, seq_lens, query_start_loc,
         int(max_query_len), int(max_seq_len), hq, float(scale), _dev(ws, "workspace"),
         ws.numel() * ws.element_size(), int(num_splits), _stream())
     _check("pa_attention_mixed", st)
+    return out
+
+
+def _new_rows(t, name, rows, hkv, d, kv_cache):
+    if t.dim() != 3 or tuple(t.shape) != (rows, hkv, d) or t.dtype != kv_cache.dtype:
+        raise ValueError(f"{name} must be [{rows}, num_kv_heads, head_dim] in the cache dtype")
+    return _dev(t, name)
+
+
+def _slots_out(slot_mapping, rows):
+    torch = _torch()
+    if slot_mapping is None:
+        return None
+    if slot_mapping.dtype != torch.int64 or slot_mapping.numel() < rows:
+        raise ValueError("slot_mapping must be int64 with one entry per new token")
+    return _dev(slot_mapping, "slot_mapping")
+
+
+def pa_cache_and_attend_decode(q, key, value, kv_cache, block_table, seq_lens, scale: float,
+                               max_seq_len: int, out=None, slot_mapping=None, workspace=None,
+                               num_splits: int = 0):
+    """Decode step in one launch: stores key/value [R, Hkv, D] at position
+    seq_lens[r] - 1 of each request and attends; see pa.h."""
+    torch = _torch()
+    nb, bs, hkv, d = _cache_dims(kv_cache)
+    R, hq = int(q.shape[0]), int(q.shape[1])
+    if q.dim() != 3 or int(q.shape[2]) != d or q.dtype != kv_cache.dtype:
+        raise ValueError("q must be [num_seqs, num_q_heads, head_dim] in the cache dtype")
+    if out is None:
+        out = torch.empty_like(q)
+    need = pa_attention_workspace_size(R, R, hq, hkv, d, max_seq_len, 1, num_splits)
+    ws = _workspace(need, q.device, workspace)
+    st = lib.pa_cache_and_attend_decode(
+        _dev(out, "out"), _dev(q, "q"), _new_rows(key, "key", R, hkv, d, kv_cache),
+        _new_rows(value, "value", R, hkv, d, kv_cache), _dev(kv_cache, "kv_cache"), nb, bs,
+        hkv, d, _dtype_code(kv_cache), _dev(block_table, "block_table", torch.int32, 2),
+        int(block_table.shape[1]), _dev(seq_lens, "seq_lens", torch.int32, 1),
+        _slots_out(slot_mapping, R), R, int(max_seq_len), hq, float(scale),
+        _dev(ws, "workspace"), ws.numel() * ws.element_size(), int(num_splits), _stream())
+    _check("pa_cache_and_attend_decode", st)
+    return out
+
+
+def pa_cache_and_attend_mixed(q, key, value, kv_cache, block_table, seq_lens, query_start_loc,
+                              num_computed_tokens, scale: float, max_query_len: int,
+                              max_seq_len: int, out=None, slot_mapping=None, workspace=None,
+                              num_splits: int = 0):
+    """Mixed step in one launch: stores key/value [T, Hkv, D] of every new
+    token by its slot and attends; see pa.h."""
+    torch = _torch()
+    nb, bs, hkv, d = _cache_dims(kv_cache)
+    T, hq = int(q.shape[0]), int(q.shape[1])
+    R = int(seq_lens.shape[0])
+    if q.dim() != 3 or int(q.shape[2]) != d or q.dtype != kv_cache.dtype:
+        raise ValueError("q must be [num_tokens, num_q_heads, head_dim] in the cache dtype")
+    if out is None:
+        out = torch.empty_like(q)
+    need = pa_attention_workspace_size(R, T, hq, hkv, d, max_seq_len, max_query_len, num_splits)
+    ws = _workspace(need, q.device, workspace)
+    st = lib.pa_cache_and_attend_mixed(
+        _dev(out, "out"), _dev(q, "q"), _new_rows(key, "key", T, hkv, d, kv_cache),
+        _new_rows(value, "value", T, hkv, d, kv_cache), _dev(kv_cache, "kv_cache"), nb, bs,
+        hkv, d, _dtype_code(kv_cache), _dev(block_table, "block_table", torch.int32, 2),
+        int(block_table.shape[1]), _dev(seq_lens, "seq_lens", torch.int32, 1),
+        _dev(query_start_loc, "query_start_loc", torch.int32, 1),
+        _dev(num_computed_tokens, "num_computed_tokens", torch.int32, 1),
+        _slots_out(slot_mapping, T), R, T, int(max_query_len), int(max_seq_len), hq,
+        float(scale), _dev(ws, "workspace"), ws.numel() * ws.element_size(), int(num_splits),
+        _stream())
+    _check("pa_cache_and_attend_mixed", st)
     return out

@@ -223,30 +223,47 @@ static int attention_common(void* out, const void* q, const void* kv_cache, int6
   return 1;  // proceed
 }
 
-int pa_attention_decode(void* out, const void* q, const void* kv_cache, int64_t num_blocks,
-                        int32_t block_size, int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
-                        const int32_t* block_table, int32_t block_table_stride,
-                        const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len,
-                        int32_t num_q_heads, float scale, void* workspace, size_t workspace_bytes,
-                        int32_t num_splits, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// New-token rows handed to an attention launch that also stores them; null
+// pointers when the caller scattered them beforehand.
+int fresh_tokens(const void* key, const void* value, void* kv_cache, int64_t* slot_mapping,
+                 pa::NewTokens* f) {
+  if (!key || !value) return PA_ERR_INVALID_ARG;
+  if (!aligned16(key) || !aligned16(value)) return PA_ERR_INVALID_ARG;
+  f->k = key;
+  f->v = value;
+  f->kv = kv_cache;
+  f->slot_out = slot_mapping;
+  return PA_OK;
+}
+
+int decode_impl(void* out, const void* q, const void* kv_cache, int64_t num_blocks,
+                int32_t block_size, int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                const int32_t* block_table, int32_t block_table_stride, const int32_t* seq_lens,
+                int32_t num_seqs, int32_t max_seq_len, int32_t num_q_heads, float scale,
+                void* workspace, size_t workspace_bytes, int32_t num_splits,
+                const pa::NewTokens& fresh, void* stream) {
   pa::DecodeArgs a{};
   const int st = attention_common(out, q, kv_cache, num_blocks, block_size, num_kv_heads, head_dim,
                                   dtype, block_table, block_table_stride, seq_lens, num_seqs,
                                   max_seq_len, num_q_heads, scale, workspace, workspace_bytes,
                                   num_splits, 1, 0, &a);
   if (st <= 0) return st;
+  a.fresh = fresh;
   return hip_status(pa::launch_decode(a, dtype, head_dim, num_q_heads / num_kv_heads,
                                       static_cast<hipStream_t>(stream)));
 }
 
-int pa_attention_mixed(void* out, const void* q, const void* kv_cache, int64_t num_blocks,
-                       int32_t block_size, int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
-                       const int32_t* block_table, int32_t block_table_stride,
-                       const int32_t* seq_lens, const int32_t* query_start_loc,
-                       const int32_t* num_computed_tokens, int32_t num_seqs, int32_t num_tokens,
-                       int32_t max_query_len, int32_t max_seq_len, int32_t num_q_heads,
-                       float scale, void* workspace, size_t workspace_bytes, int32_t num_splits,
-                       void* stream) {
+int mixed_impl(void* out, const void* q, const void* kv_cache, int64_t num_blocks,
+               int32_t block_size, int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+               const int32_t* block_table, int32_t block_table_stride, const int32_t* seq_lens,
+               const int32_t* query_start_loc, const int32_t* num_computed_tokens,
+               int32_t num_seqs, int32_t num_tokens, int32_t max_query_len, int32_t max_seq_len,
+               int32_t num_q_heads, float scale, void* workspace, size_t workspace_bytes,
+               int32_t num_splits, const pa::NewTokens& fresh, void* stream) {
   if (num_tokens < 0 || max_query_len < 0) return PA_ERR_INVALID_ARG;
   pa::DecodeArgs a{};
   const int st = attention_common(out, q, kv_cache, num_blocks, block_size, num_kv_heads, head_dim,
@@ -256,6 +273,7 @@ int pa_attention_mixed(void* out, const void* q, const void* kv_cache, int64_t n
   if (st <= 0) return st;
   if (num_tokens == 0) return PA_OK;
   if (!query_start_loc || !num_computed_tokens) return PA_ERR_INVALID_ARG;
+  a.fresh = fresh;
   const int group = num_q_heads / num_kv_heads;
   if (max_query_len > 1 && !pa::prefill_supported(dtype, head_dim, group))
     return PA_ERR_UNSUPPORTED;
@@ -277,6 +295,7 @@ int pa_attention_mixed(void* out, const void* q, const void* kv_cache, int64_t n
     p.max_tiles = (int)(ceil_div(num_tokens, pa::kQueriesPerTile) + num_seqs);
     p.max_query_len = max_query_len;
     p.scale_log2 = a.scale_log2;
+    p.fresh = fresh;
     if (tiles_beside_decode(num_seqs, max_query_len)) {
       // tiles and decode ranges in one launch, then the merge
       p.beside_decode = 1;
@@ -289,6 +308,78 @@ int pa_attention_mixed(void* out, const void* q, const void* kv_cache, int64_t n
     if (num_seqs == 1) return PA_OK;  // the one request is the chunk: no decode rows
   }
   return hip_status(pa::launch_decode(a, dtype, head_dim, group, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_attention_decode(void* out, const void* q, const void* kv_cache, int64_t num_blocks,
+                        int32_t block_size, int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                        const int32_t* block_table, int32_t block_table_stride,
+                        const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len,
+                        int32_t num_q_heads, float scale, void* workspace, size_t workspace_bytes,
+                        int32_t num_splits, void* stream) {
+  return decode_impl(out, q, kv_cache, num_blocks, block_size, num_kv_heads, head_dim, dtype,
+                     block_table, block_table_stride, seq_lens, num_seqs, max_seq_len,
+                     num_q_heads, scale, workspace, workspace_bytes, num_splits, pa::NewTokens{},
+                     stream);
+}
+
+int pa_attention_mixed(void* out, const void* q, const void* kv_cache, int64_t num_blocks,
+                       int32_t block_size, int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                       const int32_t* block_table, int32_t block_table_stride,
+                       const int32_t* seq_lens, const int32_t* query_start_loc,
+                       const int32_t* num_computed_tokens, int32_t num_seqs, int32_t num_tokens,
+                       int32_t max_query_len, int32_t max_seq_len, int32_t num_q_heads,
+                       float scale, void* workspace, size_t workspace_bytes, int32_t num_splits,
+                       void* stream) {
+  return mixed_impl(out, q, kv_cache, num_blocks, block_size, num_kv_heads, head_dim, dtype,
+                    block_table, block_table_stride, seq_lens, query_start_loc,
+                    num_computed_tokens, num_seqs, num_tokens, max_query_len, max_seq_len,
+                    num_q_heads, scale, workspace, workspace_bytes, num_splits, pa::NewTokens{},
+                    stream);
+}
+
+int pa_cache_and_attend_decode(void* out, const void* q, const void* key, const void* value,
+                               void* kv_cache, int64_t num_blocks, int32_t block_size,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                               const int32_t* block_table, int32_t block_table_stride,
+                               const int32_t* seq_lens, int64_t* slot_mapping,
+                               int32_t num_seqs, int32_t max_seq_len, int32_t num_q_heads,
+                               float scale, void* workspace, size_t workspace_bytes,
+                               int32_t num_splits, void* stream) {
+  if (num_seqs > 0 && max_seq_len > 0 && !(key && value)) return PA_ERR_INVALID_ARG;
+  pa::NewTokens f{};
+  if (key || value) {
+    const int st = fresh_tokens(key, value, kv_cache, slot_mapping, &f);
+    if (st != PA_OK) return st;
+  }
+  return decode_impl(out, q, kv_cache, num_blocks, block_size, num_kv_heads, head_dim, dtype,
+                     block_table, block_table_stride, seq_lens, num_seqs, max_seq_len,
+                     num_q_heads, scale, workspace, workspace_bytes, num_splits, f, stream);
+}
+
+int pa_cache_and_attend_mixed(void* out, const void* q, const void* key, const void* value,
+                              void* kv_cache, int64_t num_blocks, int32_t block_size,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                              const int32_t* block_table, int32_t block_table_stride,
+                              const int32_t* seq_lens, const int32_t* query_start_loc,
+                              const int32_t* num_computed_tokens, int64_t* slot_mapping,
+                              int32_t num_seqs, int32_t num_tokens, int32_t max_query_len,
+                              int32_t max_seq_len, int32_t num_q_heads, float scale,
+                              void* workspace, size_t workspace_bytes, int32_t num_splits,
+                              void* stream) {
+  if (num_tokens > 0 && !(key && value)) return PA_ERR_INVALID_ARG;
+  pa::NewTokens f{};
+  if (key || value) {
+    const int st = fresh_tokens(key, value, kv_cache, slot_mapping, &f);
+    if (st != PA_OK) return st;
+  }
+  return mixed_impl(out, q, kv_cache, num_blocks, block_size, num_kv_heads, head_dim, dtype,
+                    block_table, block_table_stride, seq_lens, query_start_loc,
+                    num_computed_tokens, num_seqs, num_tokens, max_query_len, max_seq_len,
+                    num_q_heads, scale, workspace, workspace_bytes, num_splits, f, stream);
 }
 
 size_t pa_attention_decode_shared_prefix_workspace_size(int32_t num_seqs, int32_t num_q_heads,

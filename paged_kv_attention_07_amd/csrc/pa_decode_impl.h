@@ -171,20 +171,29 @@ struct BlockRegs {
   u32x4_t k0[S::NCH], k1[S::NCH], v0[S::NCH], v1[S::NCH];
 };
 
+// Load the lane's K and V pieces of tokens tg and tg + 8 from four row
+// addresses (K of token tg, K of token tg + 8, V of tg, V of tg + 8).
 template <typename E, int D, int HPW>
-__device__ __forceinline__ void load_block(BlockRegs<E, D, HPW>& b, const uint8_t* p,
-                                           int64_t tok8, int64_t half) {
+__device__ __forceinline__ void load_rows(BlockRegs<E, D, HPW>& b, const uint8_t* k0,
+                                          const uint8_t* k1, const uint8_t* v0,
+                                          const uint8_t* v1) {
   using S = Shape<E, D, HPW>;
 #pragma unroll
   for (int c = 0; c < S::NCH; ++c) {
-    b.k0[c] = load16(p + c * 128);
-    b.k1[c] = load16(p + tok8 + c * 128);
+    b.k0[c] = load16(k0 + c * 128);
+    b.k1[c] = load16(k1 + c * 128);
   }
 #pragma unroll
   for (int c = 0; c < S::NCH; ++c) {
-    b.v0[c] = load16(p + half + c * 128);
-    b.v1[c] = load16(p + half + tok8 + c * 128);
+    b.v0[c] = load16(v0 + c * 128);
+    b.v1[c] = load16(v1 + c * 128);
   }
+}
+
+template <typename E, int D, int HPW>
+__device__ __forceinline__ void load_block(BlockRegs<E, D, HPW>& b, const uint8_t* p,
+                                           int64_t tok8, int64_t half) {
+  load_rows<E, D, HPW>(b, p, p + tok8, p + half, p + half + tok8);
 }
 
 // One 16-token block of one request: scores of tokens tg and tg+8 of the
@@ -303,9 +312,12 @@ __device__ __forceinline__ void attend_block(BlockRegs<E, D, HPW>& b, int j, int
 }
 
 // Attention of one query row over keys [16*j0, min(16*j1, L)) of request r.
+// `writer`: this wave stores the request's new token into the cache when the
+// launch carries new tokens and the range holds the request's last block.
 template <typename E, int D, int HPW>
 __device__ __forceinline__ void process_range(const DecodeArgs& a, int r, int row, int L, int j0,
-                                              int j1, int h, int hq0, bool whole, int slot) {
+                                              int j1, int h, int hq0, bool whole, int slot,
+                                              bool writer) {
   using S = Shape<E, D, HPW>;
   const int lane = lane_id();
   const int tg = lane >> 3;
@@ -343,19 +355,58 @@ __device__ __forceinline__ void process_range(const DecodeArgs& a, int r, int ro
     for (int e = 0; e < S::DPL; ++e) acc[hh][e] = 0.f;
   }
 
+  // The step's new token (position L - 1) lives in the request's last block:
+  // when this range holds that block and the launch carries new tokens, the
+  // token's rows are read from the new-token input (its cache row is being
+  // written in this launch) and one wave per KV head stores them.
+  const bool fresh = a.fresh.k != nullptr && j1 + sk == nb;
+  const int jlast = fresh ? nb - 1 - sk : -1;  // range-local index of the last block
+  const int off = (L - 1) & (kBlockSize - 1);  // the new token's row in that block
+  const int64_t nrow = (int64_t)row * tok_stride + (int64_t)h * S::ROWB;
+  if (fresh && writer) {
+    constexpr int NL = S::ROWB / 16;           // 16-byte pieces per row
+    const int64_t id = load_scalar(bt + jlast);
+    if (lane < 2 * NL) {
+      const int hv = lane / NL;
+      const int64_t piece = nrow + (lane % NL) * 16;
+      const uint8_t* src = static_cast<const uint8_t*>(hv ? a.fresh.v : a.fresh.k) + piece;
+      uint8_t* dst = static_cast<uint8_t*>(a.fresh.kv) + id * blk_stride + hv * half_stride +
+                     (int64_t)off * tok_stride + (int64_t)h * S::ROWB + (lane % NL) * 16;
+      store16(dst, load16(src));
+    }
+    if (h == 0 && lane == 0 && a.fresh.slot_out) a.fresh.slot_out[row] = id * kBlockSize + off;
+  }
+
   // three register buffers: blocks j+1 and j+2 are in flight while block j
   // is processed; block ids are read one step before their loads are issued
   BlockRegs<E, D, HPW> b0, b1, b2;
+  auto load_at = [&](BlockRegs<E, D, HPW>& b, int jj, int id) {
+    const uint8_t* p = kvh + (int64_t)id * blk_stride;
+    if (jj != jlast) {
+      load_block<E, D, HPW>(b, p, tok8, half_stride);
+    } else {
+      // the lane whose token is the new one reads it from the input rows;
+      // that address differs from the lane's cache address by the same
+      // (wave-uniform) amount in every such lane: dk for K, dv for V
+      const int64_t cache_row = (int64_t)reinterpret_cast<uintptr_t>(a.kv) +
+                                (int64_t)id * blk_stride + (int64_t)off * tok_stride;
+      const int64_t dk =
+          (int64_t)reinterpret_cast<uintptr_t>(a.fresh.k) + (int64_t)row * tok_stride - cache_row;
+      const int64_t dv = (int64_t)reinterpret_cast<uintptr_t>(a.fresh.v) +
+                         (int64_t)row * tok_stride - cache_row - half_stride;
+      const bool s0 = tg == off, s1 = tg + 8 == off;
+      load_rows<E, D, HPW>(b, p + (s0 ? dk : 0), p + tok8 + (s1 ? dk : 0),
+                           p + half_stride + (s0 ? dv : 0), p + half_stride + tok8 + (s1 ? dv : 0));
+    }
+  };
   int id_next = (j0 + 2 < j1) ? load_scalar(bt + j0 + 2) : 0;
-  load_block<E, D, HPW>(b0, kvh + (int64_t)load_scalar(bt + j0) * blk_stride, tok8, half_stride);
-  if (j0 + 1 < j1)
-    load_block<E, D, HPW>(b1, kvh + (int64_t)load_scalar(bt + j0 + 1) * blk_stride, tok8,
-                          half_stride);
+  load_at(b0, j0, load_scalar(bt + j0));
+  if (j0 + 1 < j1) load_at(b1, j0 + 1, load_scalar(bt + j0 + 1));
   int j = j0;
   auto issue = [&](BlockRegs<E, D, HPW>& b) {
     // load block j + 2 into b, then fetch the id of block j + 3
     if (j + 2 < j1) {
-      load_block<E, D, HPW>(b, kvh + (int64_t)id_next * blk_stride, tok8, half_stride);
+      load_at(b, j + 2, id_next);
       id_next = (j + 3 < j1) ? load_scalar(bt + j + 3) : 0;
     }
   };
@@ -476,7 +527,8 @@ __device__ __forceinline__ void decode_split_body(const DecodeArgs& a, int wg) {
         int4 meta = {whole ? -1 : c, cl, W, 0};
         *reinterpret_cast<int4*>(a.ws_meta + 4 * (int64_t)(base + src)) = meta;
       }
-      process_range<E, D, HPW>(a, base + src, row, L, j0, j1, h, hq0, whole, base + src + c);
+      process_range<E, D, HPW>(a, base + src, row, L, j0, j1, h, hq0, whole, base + src + c,
+                               hs == 0);
     }
     running = readlane(incl, kWave - 1);
   }

@@ -9,6 +9,19 @@ namespace pa {
 
 constexpr int kBlockSize = 16;  // tokens per paged block
 
+// The step's new tokens when the attention launch also stores them into the
+// cache (k == null: the caller scattered them beforehand).  Token t of the
+// step (row t of k and v) sits at position num_computed + (t - qsl[r]) of its
+// request r -- for a decode row, seq_len - 1.  Every reader of such a key row
+// in the launch takes it from k / v, and exactly one work-group writes it to
+// the cache, so no access in the launch depends on another's store.
+struct NewTokens {
+  const void* k;              // [rows, Hkv, D], cache dtype
+  const void* v;
+  void* kv;                   // the cache (writable view of DecodeArgs::kv)
+  int64_t* slot_out;          // [rows] or null: the cache slot of each new token
+};
+
 // Arguments shared by the decode (split-KV) kernel and its merge kernel.
 struct DecodeArgs {
   void* out;                  // [rows, Hq, D]
@@ -32,6 +45,7 @@ struct DecodeArgs {
   // prefix partial (max, sum, output) is in workspace slot prefix_slot0 + r.
   int32_t skip_blocks;
   int32_t prefix_slot0;
+  NewTokens fresh;
 };
 
 // Arguments of the MFMA prefill-tile kernel.
@@ -61,6 +75,7 @@ struct PrefillArgs {
   int32_t prefix_slot0;
   float* ws_ml;
   float* ws_o;
+  NewTokens fresh;
 };
 
 constexpr int kQueriesPerTile = 16;  // fewest query tokens per prefill tile (grid bound)

@@ -5,8 +5,10 @@
 // request with q_len > 1 new tokens on top of num_computed cached ones, token
 // i (absolute position pos = num_computed + i) attends keys 0..pos of its own
 // request -- the cached history plus the earlier tokens of the chunk (causal
-// inside the chunk).  Keys are read through the request's block table; the
-// new tokens' K/V were scattered into the cache beforehand.
+// inside the chunk).  Keys are read through the request's block table.  The
+// new tokens' K/V were either scattered into the cache beforehand, or come
+// with the launch: then the chunk's keys are read from the new-token input
+// and each tile stores its own tokens' rows into the cache.
 //
 // Tiling.  A work-group owns one tile of query tokens of one request and one
 // group of query heads sharing a KV head.  Its waves form KSPLIT key parts of
@@ -228,6 +230,14 @@ __device__ __forceinline__ void prefill_tile_body(const PrefillArgs& a, int bx, 
       goff[hv][i] = (uint32_t)(hv * half_stride + rib * tok_stride + col * 16);
       zoff[hv][i] = (uint32_t)(col * 16);
     }
+  // Keys at positions >= nfresh are this step's new tokens when the launch
+  // also stores them: their cache rows are being written in this launch, so
+  // they are copied from the new-token input (row q0 + key - nc) instead.
+  const bool fresh = a.fresh.k != nullptr && !cascade;
+  const int nfresh = fresh ? nc : 0x7fffffff;
+  const uint8_t* fbase[2] = {
+      static_cast<const uint8_t*>(a.fresh.k) + (int64_t)q0 * tok_stride + (int64_t)h * S::ROWB,
+      static_cast<const uint8_t*>(a.fresh.v) + (int64_t)q0 * tok_stride + (int64_t)h * S::ROWB};
   auto dma = [&](int it, int phys, int buf) {
     const uint8_t* blk = kvh + (int64_t)phys * blk_stride;
     const int key0 = it * kKeysPerIter + 16 * w4;
@@ -236,7 +246,11 @@ __device__ __forceinline__ void prefill_tile_body(const PrefillArgs& a, int bx, 
 #pragma unroll
       for (int i = 0; i < CPB; ++i) {
         const int rib = S::RPI * i + lane / S::CPR;
-        const uint8_t* src = key0 + rib < kend ? blk + goff[hv][i] : g_zero_row + zoff[hv][i];
+        const int key = key0 + rib;
+        const uint8_t* src =
+            key >= kend      ? g_zero_row + zoff[hv][i]
+            : key >= nfresh  ? fbase[hv] + (int64_t)(key - nc) * tok_stride + zoff[hv][i]
+                             : blk + goff[hv][i];
         uint8_t* dst = &lds[part][buf][hv * S::KBUF + (16 * w4 + S::RPI * i) * S::ROWB];
         __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
       }
@@ -367,6 +381,28 @@ __device__ __forceinline__ void prefill_tile_body(const PrefillArgs& a, int bx, 
     __syncthreads();
     if (t + 1 < my_iters) dma(it_begin + t + 1, phys, buf ^ 1);
     if (t < my_iters) compute(it_begin + t, buf);
+  }
+  // ---- store the tile's new tokens into the cache: one work-group per KV
+  // head (the first query-head group) writes the K and V rows of tokens
+  // tile_start .. tile_start + tile_valid - 1 (step rows q0 + ...), which no
+  // work-group of this launch reads from the cache
+  if (fresh && hs == 0) {
+    constexpr int NL = S::ROWB / 16;           // 16-byte pieces per row
+    for (int x = tid; x < tile_valid * 2 * NL; x += 256 * KSPLIT) {
+      const int i = x / (2 * NL);
+      const int hv = (x / NL) & 1;
+      const int col = x % NL;
+      const int p = nc + tile_start + i;       // position in the request
+      const int64_t id = bt[p / kBlockSize];
+      const int64_t piece = (int64_t)h * S::ROWB + col * 16;
+      const uint8_t* src = static_cast<const uint8_t*>(hv ? a.fresh.v : a.fresh.k) +
+                           (int64_t)(q0 + tile_start + i) * tok_stride + piece;
+      uint8_t* dst = static_cast<uint8_t*>(a.fresh.kv) + id * blk_stride + hv * half_stride +
+                     (int64_t)(p % kBlockSize) * tok_stride + piece;
+      store16(dst, load16(src));
+      if (h == 0 && hv == 0 && col == 0 && a.fresh.slot_out)
+        a.fresh.slot_out[q0 + tile_start + i] = id * kBlockSize + p % kBlockSize;
+    }
   }
   if constexpr (KSPLIT == 2) __syncthreads();  // stages are reused for the merge
 

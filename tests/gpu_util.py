@@ -100,15 +100,45 @@ class Device:
                                      num_splits=num_splits)
 
 
-def run_step(w, *, poison=True, num_splits=0, force_mixed=False, shared_prefix=None):
-    """Slot mapping, scatter and attention on the GPU for one step of `w`.
-    Returns (pool_before, gpu_slots, gpu_pool, gpu_out) as host arrays."""
+    def cache_and_attend(self, num_splits=0, force_mixed=False, slots=True):
+        """The one-launch step: the attention call stores the new tokens
+        itself.  Returns (out, slot_mapping or None); the slot buffer starts
+        at -7 so an entry the library does not write shows."""
+        import torch
+        import paged_kv_attention_07_amd as pa
+        w = self.w
+        sm = (torch.full((w.num_tokens,), -7, dtype=torch.int64, device="cuda")
+              if slots else None)
+        if w.is_decode_only and not force_mixed:
+            out = pa.pa_cache_and_attend_decode(self.q, self.k_new, self.v_new, self.kv,
+                                                self.block_table, self.seq_lens, w.scale,
+                                                w.max_seq_len, slot_mapping=sm,
+                                                num_splits=num_splits)
+        else:
+            out = pa.pa_cache_and_attend_mixed(self.q, self.k_new, self.v_new, self.kv,
+                                               self.block_table, self.seq_lens, self.qsl,
+                                               self.num_computed, w.scale, w.max_query_len,
+                                               w.max_seq_len, slot_mapping=sm,
+                                               num_splits=num_splits)
+        return out, sm
+
+
+def run_step(w, *, poison=True, num_splits=0, force_mixed=False, shared_prefix=None,
+             fused=False):
+    """Slot mapping, scatter and attention on the GPU for one step of `w`
+    (fused: one cache-and-attend call).  Returns (pool_before, gpu_slots,
+    gpu_pool, gpu_out) as host arrays."""
     import torch
     pool = poisoned_pool(w) if poison else w.pool
     dev = Device(w, pool)
-    slots = dev.slot_mapping()
-    dev.scatter(slots)
-    out = dev.attend(num_splits=num_splits, force_mixed=force_mixed, shared_prefix=shared_prefix)
+    if fused:
+        assert shared_prefix is None
+        out, slots = dev.cache_and_attend(num_splits=num_splits, force_mixed=force_mixed)
+    else:
+        slots = dev.slot_mapping()
+        dev.scatter(slots)
+        out = dev.attend(num_splits=num_splits, force_mixed=force_mixed,
+                         shared_prefix=shared_prefix)
     torch.cuda.synchronize()
     return pool, slots.cpu().numpy(), from_device(dev.kv, w.dtype), from_device(out, w.dtype)
 
@@ -137,3 +167,17 @@ def check_close(w, got_bits: np.ndarray, want: np.ndarray, rows=None, what=""):
     assert mx <= tol["max_abs"], f"{what}: max abs err {mx:.3g} > {tol['max_abs']}"
     assert mean <= tol["mean_abs"], f"{what}: mean abs err {mean:.3g} > {tol['mean_abs']}"
     return mx, mean
+
+
+def sampled_rows_check(w, dev_out_bits, rows):
+    """Compare selected query rows with the oracle, each row computed as its
+    own one-token request at its absolute position (same table, same pool)."""
+    import dataclasses
+    qsl = w.query_start_loc
+    req_of = np.searchsorted(qsl, np.asarray(rows), side="right") - 1
+    nc = np.array([w.num_computed[r] + (t - qsl[r]) for t, r in zip(rows, req_of)], np.int32)
+    sub = dataclasses.replace(
+        w, q=w.q[rows], seq_lens=(nc + 1).astype(np.int32), num_computed=nc,
+        query_start_loc=np.arange(len(rows) + 1, dtype=np.int32),
+        block_table=w.block_table[req_of])
+    return sub

@@ -1,0 +1,187 @@
+"""One-launch steps (pa_cache_and_attend_decode / pa_cache_and_attend_mixed)
+vs the fp64 oracle and vs the three calls they replace, through the C ABI.
+
+The slots the step's tokens are written to are NaN-poisoned in the pool
+before the call, so a launch that read a new token's cache row instead of
+its input row would give a non-finite output.  Slots and the whole pool after
+the call are compared bit for bit with the oracle's slot formula and
+scatter; outputs to the same tolerances as the other parity tests, and bit
+for bit against slot mapping + reshape_and_cache + attention (the same
+arithmetic on the same values).
+"""
+
+import functools
+
+import numpy as np
+import pytest
+
+from workloads import make_workload
+from workloads.gen import build_workload
+
+import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # collected on CPU hosts, never run there
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import paged_kv_attention_07_amd as pa  # noqa: E402  (fails loudly if libpa.so is missing)
+
+SMALL = ["tiny_f32_decode", "tiny_f32_decode_alt", "decode_bf16_small", "mixed_bf16_small",
+         "prefix_shared_small", "long_decode_small"]
+
+
+@functools.lru_cache(maxsize=4)
+def workload(name, seed=None):
+    print(f"[workload] {name} seed={seed}", flush=True)
+    return make_workload(name, seed)
+
+
+def fused_check(w, requests=None, three_calls=True, **kw):
+    """The one-launch step vs the oracle; with three_calls, also bit for bit
+    vs the separate slot-mapping, scatter and attention calls."""
+    print(f"[case] fused {w.name} seed={w.seed} R={w.num_seqs} T={w.num_tokens} {kw}",
+          flush=True)
+    pool, g_slots, g_pool, g_out = gu.run_step(w, fused=True, **kw)
+    r_slots, r_pool, r_out = gu.oracle_step(w, pool, requests=requests)
+    assert np.array_equal(g_slots, r_slots), "slot mapping differs"
+    assert np.array_equal(gu.bits(g_pool), gu.bits(r_pool)), "pool differs after the step"
+    rows = None if requests is None else gu.rows_of(w, requests)
+    gu.check_close(w, g_out, r_out, rows=rows, what=w.name)
+    if three_calls:
+        _, s3, p3, o3 = gu.run_step(w, **kw)
+        assert np.array_equal(s3, g_slots)
+        assert np.array_equal(gu.bits(p3), gu.bits(g_pool))
+        assert np.array_equal(gu.bits(o3), gu.bits(g_out)), "differs from the three calls"
+    return g_out
+
+
+def _variant(dtype, Hq, Hkv, D, lens, seed, q_lens=None):
+    reqs = [(L - (1 if q_lens is None else q_lens[i]), 1 if q_lens is None else q_lens[i])
+            for i, L in enumerate(lens)]
+    return build_workload(f"fused_{dtype}_{Hq}x{Hkv}x{D}", dtype=dtype, num_q_heads=Hq,
+                          num_kv_heads=Hkv, head_dim=D, num_blocks=400, requests=reqs,
+                          seed=seed)
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_small_configs(name):
+    fused_check(workload(name))
+
+
+@pytest.mark.parametrize("dtype,Hq,Hkv,D", [
+    ("bf16", 32, 8, 128), ("bf16", 8, 8, 128), ("bf16", 16, 2, 128), ("f16", 8, 2, 64),
+    ("f32", 4, 4, 64), ("f32", 8, 2, 128)])
+def test_decode_new_token_at_every_row_of_a_block(dtype, Hq, Hkv, D):
+    """The new token at each of the 16 rows of its block (both token groups of
+    a lane), first tokens of a request, and every head grouping."""
+    lens = [1, 2] + [16 * (1 + k % 5) + off for k, off in enumerate(range(1, 17))]
+    w = _variant(dtype, Hq, Hkv, D, lens, seed=41 + Hq + D)
+    fused_check(w)
+    fused_check(w, num_splits=7)
+    fused_check(w, num_splits=1)
+
+
+@pytest.mark.parametrize("splits", [2, 3, 64, 2000])
+def test_decode_split_counts(splits):
+    fused_check(workload("decode_bf16_small"), num_splits=splits)
+
+
+@pytest.mark.parametrize("dtype,Hq,Hkv,D", [
+    ("bf16", 32, 8, 128), ("bf16", 8, 8, 128), ("bf16", 8, 4, 64), ("f16", 16, 2, 128),
+    ("bf16", 16, 2, 64)])
+def test_mixed_groupings(dtype, Hq, Hkv, D):
+    """Chunks starting mid-block and on block boundaries, decode rows, and a
+    request with no tokens this step."""
+    lens = [40, 17, 300, 5, 64, 129, 1, 700, 90]
+    q_lens = [40, 2, 33, 1, 16, 100, 1, 64, 0]
+    fused_check(_variant(dtype, Hq, Hkv, D, lens, seed=51 + Hq, q_lens=q_lens))
+
+
+@pytest.mark.parametrize("overlap", ["0", "1"])
+@pytest.mark.parametrize("shape", [0, 1])
+def test_mixed_schedules(overlap, shape, monkeypatch):
+    """Tiles beside the decode ranges in one launch, or launched apart; both
+    tile shapes; a one-request batch (tiles alone)."""
+    monkeypatch.setenv("PA_MIXED_OVERLAP", overlap)
+    monkeypatch.setenv("PA_PREFILL_SHAPE", str(shape))
+    fused_check(workload("mixed_bf16_small"))
+    fused_check(_variant("bf16", 32, 8, 128, [300, 40, 129, 2000, 17], seed=61,
+                         q_lens=[100, 1, 64, 1, 1]))
+    fused_check(_variant("f16", 8, 2, 64, [77], seed=62, q_lens=[60]))
+
+
+def test_mixed_decode_rows_only_through_mixed_entry():
+    w = workload("decode_bf16_small")
+    fused_check(w, force_mixed=True)
+
+
+def test_slot_output_optional():
+    """Without a slot buffer the cache and the output are the same."""
+    w = workload("mixed_bf16_small")
+    pool = gu.poisoned_pool(w)
+    outs, pools = [], []
+    for slots in (True, False):
+        dev = gu.Device(w, pool)
+        out, _ = dev.cache_and_attend(slots=slots)
+        outs.append(gu.from_device(out, w.dtype))
+        pools.append(gu.from_device(dev.kv, w.dtype))
+    assert np.array_equal(gu.bits(outs[0]), gu.bits(outs[1]))
+    assert np.array_equal(gu.bits(pools[0]), gu.bits(pools[1]))
+
+
+def test_argument_errors():
+    w = workload("decode_bf16_small")
+    dev = gu.Device(w)
+    with pytest.raises(ValueError):
+        pa.pa_cache_and_attend_decode(dev.q, dev.k_new[:1], dev.v_new, dev.kv, dev.block_table,
+                                      dev.seq_lens, w.scale, w.max_seq_len)
+    with pytest.raises(ValueError):
+        pa.pa_cache_and_attend_decode(dev.q, dev.k_new, dev.v_new, dev.kv, dev.block_table,
+                                      dev.seq_lens, w.scale, w.max_seq_len,
+                                      slot_mapping=torch.zeros(3, dtype=torch.int64,
+                                                               device="cuda"))
+    # a null key through the C ABI is rejected before any launch
+    st = pa.lib.pa_cache_and_attend_decode(
+        dev.q.data_ptr(), dev.q.data_ptr(), None, dev.v_new.data_ptr(), dev.kv.data_ptr(),
+        w.num_blocks, 16, w.num_kv_heads, w.head_dim, pa.DTYPE_CODES[w.dtype],
+        dev.block_table.data_ptr(), w.block_table.shape[1], dev.seq_lens.data_ptr(), None,
+        w.num_seqs, w.max_seq_len, w.num_q_heads, w.scale, None, 0, 0, None)
+    assert st == -1
+
+
+def test_full_decode_64req():
+    fused_check(workload("decode_bf16_64req"))
+
+
+def test_full_mixed_step():
+    fused_check(workload("mixed_chunked_prefill_bf16"))
+
+
+def test_full_long_context_sampled():
+    w = workload("long_context_decode_bf16")
+    fused_check(w, requests=[0, 7, 15], three_calls=False)
+
+
+def test_prefill_chunk_2048_sampled():
+    """A 2048-token chunk on cached history: every key of the chunk comes from
+    the input rows; pool bit-exact, sampled rows vs the oracle."""
+    import oracle
+    w = workload("prefill_chunk_2048_bf16")
+    pool = gu.poisoned_pool(w)
+    dev = gu.Device(w, pool)
+    out, slots = dev.cache_and_attend(force_mixed=True)
+    out = gu.from_device(out, w.dtype)
+    r_slots = oracle.slot_mapping(w.block_table, w.query_start_loc, w.num_computed, 16)
+    assert np.array_equal(slots.cpu().numpy(), r_slots)
+    r_pool = oracle.reshape_and_cache(pool, w.k_new, w.v_new, r_slots)
+    assert np.array_equal(gu.bits(gu.from_device(dev.kv, w.dtype)), gu.bits(r_pool))
+    T = w.num_tokens
+    rng = np.random.default_rng(23)
+    rows = np.unique(np.concatenate([[0, 1, 15, 16, 63, 64, T - 1, T - 2],
+                                     rng.choice(T, 40, replace=False)]))
+    sub = gu.sampled_rows_check(w, out, rows)
+    ref = oracle.paged_attention(sub.q, r_pool, sub.block_table, sub.seq_lens,
+                                 sub.query_start_loc, sub.num_computed, w.scale, w.dtype)
+    gu.check_close(w, out[rows], ref, what="prefill 2048 fused")

@@ -285,20 +285,6 @@ def test_workspace_reused_across_calls():
 # --------------------------------------------------------------------------
 
 
-def sampled_rows_check(w, dev_out_bits, rows):
-    """Compare selected query rows with the oracle, each row computed as its
-    own one-token request at its absolute position (same table, same pool)."""
-    import dataclasses
-    qsl = w.query_start_loc
-    req_of = np.searchsorted(qsl, np.asarray(rows), side="right") - 1
-    nc = np.array([w.num_computed[r] + (t - qsl[r]) for t, r in zip(rows, req_of)], np.int32)
-    sub = dataclasses.replace(
-        w, q=w.q[rows], seq_lens=(nc + 1).astype(np.int32), num_computed=nc,
-        query_start_loc=np.arange(len(rows) + 1, dtype=np.int32),
-        block_table=w.block_table[req_of])
-    return sub
-
-
 def _large_prefill_check(name, shape, monkeypatch):
     import dataclasses
     monkeypatch.setenv("PA_PREFILL_SHAPE", str(shape))
@@ -317,7 +303,7 @@ def _large_prefill_check(name, shape, monkeypatch):
     T = w.num_tokens
     edge = [0, 1, 15, 16, 31, 32, 63, 64, T - 1, T - 2, T - 17]
     rows = np.unique(np.concatenate([edge, rng.choice(T, 53, replace=False)]))
-    sub = sampled_rows_check(w, out, rows)
+    sub = gu.sampled_rows_check(w, out, rows)
     ref = oracle.paged_attention(sub.q, r_pool, sub.block_table, sub.seq_lens,
                                  sub.query_start_loc, sub.num_computed, w.scale, w.dtype)
     gu.check_close(w, out[rows], ref, what=f"{name}/shape{shape}")
