@@ -11,9 +11,10 @@
  *      [query_start_loc | num_computed | seq_lens | copy pairs | block table];
  *   3. pa_copy_blocks for the step's copy-on-write pairs, if any
  *      ("vLLM 架构源码解析（一）" §4.3.2);
- *   4. pa_compute_slot_mapping and pa_reshape_and_cache of the step's K/V
- *      ("vllm v1 源码精读（三）" §3.4);
- *   5. pa_attention_mixed over the packed batch (same page, §4.2).
+ *   4. pa_cache_and_attend_mixed over the packed batch: the slot of every
+ *      new token and the store of its K/V ("vllm v1 源码精读（三）" §3.4) in
+ *      the same launch as the attention (same page, §4.2), which reads the
+ *      new rows from k / v; the slots land in the device scratch.
  * The caller owns the KV cache and one device scratch buffer (sized by
  * pa_engine_device_bytes); the engine owns its scheduler, its page-locked
  * host arenas (allocated at creation) and two HIP events.  After each step

@@ -13,12 +13,14 @@ namespace {
 constexpr int kVersion = 100;  // 0.1.0
 
 // Partition plan for the balanced split: enough wavefronts to fill the chip
-// (256 CUs, ~8 resident waves each), but no range shorter than a few blocks.
-// Beside concurrent prefill tiles the decode rows take one wave per SIMD, so
-// each SIMD holds one bandwidth-bound decode wave and one compute-bound tile
-// wave.
+// (256 CUs, 8 resident waves each at two waves per SIMD), but no range
+// shorter than a few blocks.  Beside concurrent prefill tiles the decode rows
+// take the slots the tiles leave: the chip's 2048 wave slots minus the tiles
+// of the longest chunk (a lower bound on the tile count), between one and
+// one and a half waves per SIMD.
 constexpr int kTargetWaves = 256 * 8;
-constexpr int kTargetWavesBesidePrefill = 256 * 4;
+constexpr int kMinWavesBesidePrefill = 256 * 4;
+constexpr int kMaxWavesBesidePrefill = 256 * 6;
 constexpr int kMinBlocksPerRange = 4;
 
 int heads_per_wave(int group) { return group < 4 ? group : 4; }
@@ -41,12 +43,27 @@ bool tiles_beside_decode(int num_seqs, int max_query_len) {
   return max_query_len > 1 && num_seqs >= 2 && overlap_enabled();
 }
 
+// Decode waves beside the tiles of a chunk of up to max_query_len tokens
+// (tile shape of the fused launch: 4 waves per tile, 32 * 4 / group-per-wave
+// tokens per tile).
+int64_t waves_beside_prefill(int num_kv_heads, int group, int max_query_len) {
+  const int wpw = heads_per_wave(group);
+  const int64_t qt = 32 * (4 / wpw);
+  const int64_t tile_waves = 4 * ceil_div(max_query_len, qt) * num_kv_heads * (group / wpw);
+  int64_t w = kTargetWaves - tile_waves;
+  if (w < kMinWavesBesidePrefill) w = kMinWavesBesidePrefill;
+  if (w > kMaxWavesBesidePrefill) w = kMaxWavesBesidePrefill;
+  return w;
+}
+
 int plan_chunks(int num_seqs, int num_kv_heads, int group, int max_seq_len, int num_splits,
-                bool beside_prefill) {
+                bool beside_prefill, int max_query_len) {
   if (num_splits > 0) return num_splits;
   const int hg = group / heads_per_wave(group);
   const int64_t blocks_upper = (int64_t)num_seqs * ceil_div(max_seq_len, pa::kBlockSize);
-  const int waves = beside_prefill ? kTargetWavesBesidePrefill : kTargetWaves;
+  const int64_t waves = beside_prefill
+                            ? waves_beside_prefill(num_kv_heads, group, max_query_len)
+                            : kTargetWaves;
   int64_t n = ceil_div(waves, (int64_t)num_kv_heads * hg);
   const int64_t cap = ceil_div(blocks_upper, kMinBlocksPerRange);
   if (n > cap) n = cap;
@@ -167,7 +184,8 @@ size_t pa_attention_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t
   (void)max_query_len;
   // the plan without concurrent tiles has the most ranges: size for it, so the
   // buffer covers either plan
-  const int chunks = plan_chunks(num_seqs, num_kv_heads, group, max_seq_len, num_splits, false);
+  const int chunks =
+      plan_chunks(num_seqs, num_kv_heads, group, max_seq_len, num_splits, false, 0);
   return workspace_layout(num_seqs, num_q_heads, head_dim, chunks).total;
 }
 
@@ -195,7 +213,8 @@ static int attention_common(void* out, const void* q, const void* kv_cache, int6
   const int P = shared_prefix_blocks;
   const int chunks = plan_chunks(num_seqs, num_kv_heads, group,
                                  P > 0 ? max(max_seq_len - P * pa::kBlockSize, 1) : max_seq_len,
-                                 num_splits, P > 0 || tiles_beside_decode(num_seqs, max_query_len));
+                                 num_splits, P > 0 || tiles_beside_decode(num_seqs, max_query_len),
+                                 P > 0 ? num_seqs : max_query_len);
   const WsLayout lay = workspace_layout(num_seqs, num_q_heads, head_dim,
                                         chunks + (P > 0 ? num_seqs : 0));
   if (!workspace || workspace_bytes < lay.total) return PA_ERR_WORKSPACE;
@@ -395,7 +414,7 @@ size_t pa_attention_decode_shared_prefix_workspace_size(int32_t num_seqs, int32_
   if (shared_prefix_blocks == 0) return plain;
   const int group = num_q_heads / num_kv_heads;
   const int rest = max(max_seq_len - shared_prefix_blocks * pa::kBlockSize, 1);
-  const int chunks = plan_chunks(num_seqs, num_kv_heads, group, rest, num_splits, true);
+  const int chunks = plan_chunks(num_seqs, num_kv_heads, group, rest, num_splits, true, num_seqs);
   const size_t casc = workspace_layout(num_seqs, num_q_heads, head_dim, chunks + num_seqs).total;
   return casc > plain ? casc : plain;
 }

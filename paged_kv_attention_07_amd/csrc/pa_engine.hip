@@ -175,17 +175,13 @@ int pa_engine_step(pa_engine* e, const void* q, const void* k, const void* v, vo
                         g.dtype, stream);
     if (st != PA_OK) return st;
   }
+  // slots, K/V store and attention in one launch (+ the split merge)
   int64_t* slots = reinterpret_cast<int64_t*>(e->scratch + e->dlay.slots);
-  st = pa_compute_slot_mapping(slots, d + L.bt, L.W, d + L.qsl, d + L.nc, s.num_seqs,
-                               s.num_tokens, B, stream);
-  if (st != PA_OK) return st;
-  st = pa_reshape_and_cache(k, v, e->kv, slots, s.num_tokens, nb, B, g.num_kv_heads, g.head_dim,
-                            g.dtype, stream);
-  if (st != PA_OK) return st;
-  return pa_attention_mixed(out, q, e->kv, nb, B, g.num_kv_heads, g.head_dim, g.dtype, d + L.bt,
-                            L.W, d + L.sl, d + L.qsl, d + L.nc, s.num_seqs, s.num_tokens,
-                            s.max_query_len, s.max_seq_len, g.num_q_heads, g.scale,
-                            e->scratch + e->dlay.workspace, e->ws_bytes, g.num_splits, stream);
+  return pa_cache_and_attend_mixed(out, q, k, v, e->kv, nb, B, g.num_kv_heads, g.head_dim,
+                                   g.dtype, d + L.bt, L.W, d + L.sl, d + L.qsl, d + L.nc, slots,
+                                   s.num_seqs, s.num_tokens, s.max_query_len, s.max_seq_len,
+                                   g.num_q_heads, g.scale, e->scratch + e->dlay.workspace,
+                                   e->ws_bytes, g.num_splits, stream);
 }
 
 int pa_engine_update(pa_engine* e, const int32_t* sampled, int32_t num_seqs,
