@@ -377,9 +377,11 @@ __device__ __forceinline__ void process_range(const DecodeArgs& a, int r, int ro
     if (h == 0 && lane == 0 && a.fresh.slot_out) a.fresh.slot_out[row] = id * kBlockSize + off;
   }
 
-  // three register buffers: blocks j+1 and j+2 are in flight while block j
-  // is processed; block ids are read one step before their loads are issued
-  BlockRegs<E, D, HPW> b0, b1, b2;
+  // two register buffers: block j+1 is in flight while block j is processed
+  // (2048 waves keep ~16 MB of loads in flight, above the bandwidth-latency
+  // product; a third buffer measured no faster and costs 32 VGPRs); block
+  // ids are read one step before their loads are issued
+  BlockRegs<E, D, HPW> b0, b1;
   auto load_at = [&](BlockRegs<E, D, HPW>& b, int jj, int id) {
     const uint8_t* p = kvh + (int64_t)id * blk_stride;
     if (jj != jlast) {
@@ -399,26 +401,22 @@ __device__ __forceinline__ void process_range(const DecodeArgs& a, int r, int ro
                            p + half_stride + (s0 ? dv : 0), p + half_stride + tok8 + (s1 ? dv : 0));
     }
   };
-  int id_next = (j0 + 2 < j1) ? load_scalar(bt + j0 + 2) : 0;
+  int id_next = (j0 + 1 < j1) ? load_scalar(bt + j0 + 1) : 0;
   load_at(b0, j0, load_scalar(bt + j0));
-  if (j0 + 1 < j1) load_at(b1, j0 + 1, load_scalar(bt + j0 + 1));
   int j = j0;
   auto issue = [&](BlockRegs<E, D, HPW>& b) {
-    // load block j + 2 into b, then fetch the id of block j + 3
-    if (j + 2 < j1) {
-      load_at(b, j + 2, id_next);
-      id_next = (j + 3 < j1) ? load_scalar(bt + j + 3) : 0;
+    // load block j + 1 into b, then fetch the id of block j + 2
+    if (j + 1 < j1) {
+      load_at(b, j + 1, id_next);
+      id_next = (j + 2 < j1) ? load_scalar(bt + j + 2) : 0;
     }
   };
   while (true) {
-    issue(b2);
+    issue(b1);
     attend_block<E, D, HPW>(b0, j + sk, nb, L, tg, a.scale_log2, qv, m, l, acc);
     if (++j >= j1) break;
     issue(b0);
     attend_block<E, D, HPW>(b1, j + sk, nb, L, tg, a.scale_log2, qv, m, l, acc);
-    if (++j >= j1) break;
-    issue(b1);
-    attend_block<E, D, HPW>(b2, j + sk, nb, L, tg, a.scale_log2, qv, m, l, acc);
     if (++j >= j1) break;
   }
 
