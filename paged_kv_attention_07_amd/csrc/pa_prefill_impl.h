@@ -233,24 +233,41 @@ __device__ __forceinline__ void prefill_tile_body(const PrefillArgs& a, int bx, 
   // Keys at positions >= nfresh are this step's new tokens when the launch
   // also stores them: their cache rows are being written in this launch, so
   // they are copied from the new-token input (row q0 + key - nc) instead.
+  // The new-token rows are laid out like the cache's token rows (stride
+  // tok_stride, head h at h * ROWB), so row key of a block comes from
+  // fresh base + (key - nc) * tok_stride + the same in-block offset goff.
   const bool fresh = a.fresh.k != nullptr && !cascade;
   const int nfresh = fresh ? nc : 0x7fffffff;
   const uint8_t* fbase[2] = {
       static_cast<const uint8_t*>(a.fresh.k) + (int64_t)q0 * tok_stride + (int64_t)h * S::ROWB,
-      static_cast<const uint8_t*>(a.fresh.v) + (int64_t)q0 * tok_stride + (int64_t)h * S::ROWB};
+      static_cast<const uint8_t*>(a.fresh.v) + (int64_t)q0 * tok_stride + (int64_t)h * S::ROWB -
+          half_stride};
+  // the wave's 16 rows of an iteration start at key0: all cached, all new,
+  // or (at most twice per tile) mixed / past the tile's last key, which is
+  // the only case that selects a source per lane
   auto dma = [&](int it, int phys, int buf) {
     const uint8_t* blk = kvh + (int64_t)phys * blk_stride;
     const int key0 = it * kKeysPerIter + 16 * w4;
+    const uint8_t* fblk[2] = {fbase[0] + (int64_t)(key0 - nc) * tok_stride,
+                              fbase[1] + (int64_t)(key0 - nc) * tok_stride};
+    const bool cached = key0 + 15 < min(kend, nfresh);
+    const bool all_new = key0 >= nfresh && key0 + 15 < kend;
 #pragma unroll
     for (int hv = 0; hv < 2; ++hv) {
 #pragma unroll
       for (int i = 0; i < CPB; ++i) {
         const int rib = S::RPI * i + lane / S::CPR;
         const int key = key0 + rib;
-        const uint8_t* src =
-            key >= kend      ? g_zero_row + zoff[hv][i]
-            : key >= nfresh  ? fbase[hv] + (int64_t)(key - nc) * tok_stride + zoff[hv][i]
-                             : blk + goff[hv][i];
+        const uint8_t* src;
+        if (cached) {
+          src = blk + goff[hv][i];
+        } else if (all_new) {
+          src = fblk[hv] + goff[hv][i];
+        } else {
+          src = key >= kend     ? g_zero_row + zoff[hv][i]
+                : key >= nfresh ? fblk[hv] + goff[hv][i]
+                                : blk + goff[hv][i];
+        }
         uint8_t* dst = &lds[part][buf][hv * S::KBUF + (16 * w4 + S::RPI * i) * S::ROWB];
         __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
       }
@@ -372,6 +389,7 @@ __device__ __forceinline__ void prefill_tile_body(const PrefillArgs& a, int bx, 
   // landed and every wave is done with the other stage), starts the copies
   // of the next iteration into the other stage, and computes.
   if (my_iters > 0) dma(it_begin, block_id(it_begin), 0);
+
   int id_next = block_id(it_begin + 1);
   for (int t = 0; t < n0; ++t) {
     const int buf = t & 1;
@@ -385,23 +403,42 @@ __device__ __forceinline__ void prefill_tile_body(const PrefillArgs& a, int bx, 
   // ---- store the tile's new tokens into the cache: one work-group per KV
   // head (the first query-head group) writes the K and V rows of tokens
   // tile_start .. tile_start + tile_valid - 1 (step rows q0 + ...), which no
-  // work-group of this launch reads from the cache
+  // work-group of this launch reads from the cache.  It runs after the key
+  // loop (whose waits would otherwise also wait for these stores), all loads
+  // issued before any store.
   if (fresh && hs == 0) {
     constexpr int NL = S::ROWB / 16;           // 16-byte pieces per row
-    for (int x = tid; x < tile_valid * 2 * NL; x += 256 * KSPLIT) {
+    constexpr int NTH = 256 * KSPLIT;
+    constexpr int PER = (QT * 2 * NL + NTH - 1) / NTH;
+    u32x4_t val[PER];
+    int64_t id[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int x = tid + k * NTH;
       const int i = x / (2 * NL);
-      const int hv = (x / NL) & 1;
-      const int col = x % NL;
-      const int p = nc + tile_start + i;       // position in the request
-      const int64_t id = bt[p / kBlockSize];
-      const int64_t piece = (int64_t)h * S::ROWB + col * 16;
-      const uint8_t* src = static_cast<const uint8_t*>(hv ? a.fresh.v : a.fresh.k) +
-                           (int64_t)(q0 + tile_start + i) * tok_stride + piece;
-      uint8_t* dst = static_cast<uint8_t*>(a.fresh.kv) + id * blk_stride + hv * half_stride +
-                     (int64_t)(p % kBlockSize) * tok_stride + piece;
-      store16(dst, load16(src));
-      if (h == 0 && hv == 0 && col == 0 && a.fresh.slot_out)
-        a.fresh.slot_out[q0 + tile_start + i] = id * kBlockSize + p % kBlockSize;
+      if (x < tile_valid * 2 * NL) {
+        const int hv = (x / NL) & 1;
+        const int64_t piece = (int64_t)h * S::ROWB + (x % NL) * 16;
+        id[k] = bt[(nc + tile_start + i) / kBlockSize];
+        val[k] = load16(static_cast<const uint8_t*>(hv ? a.fresh.v : a.fresh.k) +
+                        (int64_t)(q0 + tile_start + i) * tok_stride + piece);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int x = tid + k * NTH;
+      if (x < tile_valid * 2 * NL) {
+        const int i = x / (2 * NL);
+        const int hv = (x / NL) & 1;
+        const int col = x % NL;
+        const int p = nc + tile_start + i;     // position in the request
+        const int64_t piece = (int64_t)h * S::ROWB + col * 16;
+        store16(static_cast<uint8_t*>(a.fresh.kv) + id[k] * blk_stride + hv * half_stride +
+                    (int64_t)(p % kBlockSize) * tok_stride + piece,
+                val[k]);
+        if (h == 0 && hv == 0 && col == 0 && a.fresh.slot_out)
+          a.fresh.slot_out[q0 + tile_start + i] = id[k] * kBlockSize + p % kBlockSize;
+      }
     }
   }
   if constexpr (KSPLIT == 2) __syncthreads();  // stages are reused for the merge
