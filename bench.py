@@ -243,6 +243,31 @@ def gpu_info():
             "cus": p.multi_processor_count, "hbm_gb": round(p.total_memory / 2**30, 1)}
 
 
+def copy_reference(nbytes: int = 1 << 30, reps: int = 10):
+    """Achievable-HBM reference: a device-to-device copy of `nbytes` (read +
+    write counted), median of `reps` event-timed copies."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        b.synchronize()
+        ms.append(a.elapsed_time(b))
+    del src, dst
+    torch.cuda.empty_cache()
+    t = float(np.median(ms)) * 1e-3
+    return {"kind": "device-to-device copy (torch), read + write bytes / median time",
+            "bytes": 2 * nbytes, "gbs": round(2 * nbytes / t / 1e9, 1),
+            "pct_peak_hbm": round(100 * 2 * nbytes / t / 1e9 / HBM_PEAK_GBS, 2)}
+
+
 # --------------------------------------------------------------------------
 # CPU oracle baseline (bounded sample)
 # --------------------------------------------------------------------------
@@ -329,6 +354,7 @@ def measure(name, args, rotations, shared_prefix=False):
     attn_avg = float(np.mean(attn_ms))
     res = dict(w=w, counts=c, ms_step=ms_step, attn_ms_avg=attn_avg, fused=st.fused,
                attn_ms_p10=float(np.percentile(attn_ms, 10)),
+               attn_ms_p50=float(np.percentile(attn_ms, 50)),
                attn_ms_p90=float(np.percentile(attn_ms, 90)))
     print(f"[bench] {name}: {ms_step * 1e3:.1f} us/step, attention {attn_avg * 1e3:.1f} us",
           file=sys.stderr, flush=True)
@@ -496,6 +522,7 @@ def main():
     achieved = c["attn_logical"] / (head["attn_ms_avg"] * 1e-3) / 1e9
     launch = {"avg_launch_us": round(head["attn_ms_avg"] * 1e3, 2),
               "p10_us": round(head["attn_ms_p10"] * 1e3, 2),
+              "p50_us": round(head["attn_ms_p50"] * 1e3, 2),
               "p90_us": round(head["attn_ms_p90"] * 1e3, 2)}
     if head_key in ("chunk", "prefill2k", "prefill8k", "prefillbatch"):
         tflops = c["chunk_flops"] / (head["attn_ms_avg"] * 1e-3) / 1e12
@@ -547,6 +574,7 @@ def main():
         "pct_peak_hbm": round(100 * value / HBM_PEAK_GBS, 2),
         "roofline": roofline,
         "gpu": gpu_info(),
+        "hbm_reference": copy_reference(),
     }
     if "mixed" in results:
         m = results["mixed"]
