@@ -168,9 +168,51 @@ class Stepper:
                                   w.max_query_len, w.max_seq_len, out=self.out,
                                   workspace=self.ws, num_splits=self.splits)
 
+    def capture(self):
+        """Capture the one-launch step over each pool copy in its own HIP
+        graph (kernels only: the entry points allocate and synchronise
+        nothing); `step` then replays them."""
+        torch = self.torch
+        assert self.fused, "graph replay covers the one-launch step"
+        self.graphs = []
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(len(self.pools)):
+                self._fused(self.pools[i])
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        for kv in self.pools:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                self._fused(kv)
+            self.graphs.append(g)
+        torch.cuda.synchronize()
+
+    def _fused(self, kv):
+        pa, w = self.pa, self.w
+        if self.decode:
+            pa.pa_cache_and_attend_decode(self.q, self.kn, self.vn, kv, self.bt, self.sl,
+                                          w.scale, w.max_seq_len, out=self.out,
+                                          slot_mapping=self.slots, workspace=self.ws,
+                                          num_splits=self.splits)
+        else:
+            pa.pa_cache_and_attend_mixed(self.q, self.kn, self.vn, kv, self.bt, self.sl,
+                                         self.qsl, self.nc, w.scale, w.max_query_len,
+                                         w.max_seq_len, out=self.out,
+                                         slot_mapping=self.slots, workspace=self.ws,
+                                         num_splits=self.splits)
+
     def step(self, i, ev=None):
         pa, w = self.pa, self.w
         kv = self.pools[i % len(self.pools)]
+        if getattr(self, "graphs", None):
+            if ev is not None:
+                ev[0].record()
+            self.graphs[i % len(self.graphs)].replay()
+            if ev is not None:
+                ev[1].record()
+            return
         if self.fused:
             if ev is not None:
                 ev[0].record()
@@ -349,10 +391,13 @@ def measure(name, args, rotations, shared_prefix=False):
     st = Stepper(w, rotations, args.splits,
                  w.meta.get("shared_prefix_blocks", 0) if shared_prefix else 0,
                  fused=not args.separate)
+    if args.graph and st.fused:
+        st.capture()
     ms_step, attn_ms = st.run(args.steps, args.warmup, args.event_every)
     c = alg_counts(w)
     attn_avg = float(np.mean(attn_ms))
     res = dict(w=w, counts=c, ms_step=ms_step, attn_ms_avg=attn_avg, fused=st.fused,
+               graph=bool(getattr(st, "graphs", None)),
                attn_ms_p10=float(np.percentile(attn_ms, 10)),
                attn_ms_p50=float(np.percentile(attn_ms, 50)),
                attn_ms_p90=float(np.percentile(attn_ms, 90)))
@@ -474,6 +519,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay each step from a captured HIP graph (one-launch steps only)")
     ap.add_argument("--event-every", type=int, default=10,
                     help="bracket every N-th timed step's attention call with HIP events "
                          "(1: every step)")
