@@ -166,6 +166,68 @@ def test_mixed_checks():
     assert mixed(T=0) == OK
 
 
+def cache_decode(**kw):
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, kv=FAKE, NB=64, B=16, Hkv=2, D=64, dtype=1,
+             bt=FAKE, stride=7, sl=FAKE, slots=None, R=4, L=100, Hq=4, scale=0.125,
+             ws=FAKE_WS, wsb=1 << 30, S=0)
+    a.update(kw)
+    return lib.pa_cache_and_attend_decode(
+        a["out"], a["q"], a["k"], a["v"], a["kv"], a["NB"], a["B"], a["Hkv"], a["D"],
+        a["dtype"], a["bt"], a["stride"], a["sl"], a["slots"], a["R"], a["L"], a["Hq"],
+        a["scale"], a["ws"], a["wsb"], a["S"], None)
+
+
+def cache_mixed(**kw):
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, kv=FAKE, NB=64, B=16, Hkv=2, D=64, dtype=1,
+             bt=FAKE, stride=7, sl=FAKE, qsl=FAKE, nc=FAKE, slots=None, R=4, T=20, Q=17, L=100,
+             Hq=4, scale=0.125, ws=FAKE_WS, wsb=1 << 30, S=0)
+    a.update(kw)
+    return lib.pa_cache_and_attend_mixed(
+        a["out"], a["q"], a["k"], a["v"], a["kv"], a["NB"], a["B"], a["Hkv"], a["D"],
+        a["dtype"], a["bt"], a["stride"], a["sl"], a["qsl"], a["nc"], a["slots"], a["R"],
+        a["T"], a["Q"], a["L"], a["Hq"], a["scale"], a["ws"], a["wsb"], a["S"], None)
+
+
+def test_cache_and_attend_checks():
+    """The one-launch steps check the new-token inputs on top of the
+    attention call's own checks."""
+    for f in (cache_decode, cache_mixed):
+        assert f(k=None) == INVALID
+        assert f(v=None) == INVALID
+        assert f(k=ctypes.c_void_p(0x10008)) == INVALID        # not 16-byte aligned
+        assert f(out=None) == INVALID
+        assert f(B=8) == UNSUPPORTED
+        assert f(D=256) == UNSUPPORTED
+        assert f(wsb=16) == WORKSPACE
+    assert cache_decode(R=0, k=None, v=None) == OK             # nothing to store or attend
+    assert cache_mixed(T=0, k=None, v=None) == OK
+    assert cache_mixed(dtype=0) == UNSUPPORTED                 # fp32 has no prefill-tile path
+
+
+def shared_prefix(**kw):
+    a = dict(out=FAKE, q=FAKE, kv=FAKE, NB=64, B=16, Hkv=2, D=64, dtype=1, bt=FAKE, stride=7,
+             sl=FAKE, R=4, L=100, Hq=4, scale=0.125, P=2, ws=FAKE_WS, wsb=1 << 30, S=0)
+    a.update(kw)
+    return lib.pa_attention_decode_shared_prefix(
+        a["out"], a["q"], a["kv"], a["NB"], a["B"], a["Hkv"], a["D"], a["dtype"], a["bt"],
+        a["stride"], a["sl"], a["R"], a["L"], a["Hq"], a["scale"], a["P"], a["ws"], a["wsb"],
+        a["S"], None)
+
+
+def test_shared_prefix_checks():
+    f = lib.pa_attention_decode_shared_prefix_workspace_size
+    assert f(4, 4, 2, 64, 100, 2, 0) > 0
+    assert f(4, 4, 2, 64, 100, 2, 0) >= f(4, 4, 2, 64, 100, 0, 0)  # covers the plain plan
+    assert f(4, 4, 2, 64, 100, -1, 0) == 0
+    assert f(4, 4, 2, 64, 100, 7, 0) == 0                          # 16 P > max_seq_len
+    assert shared_prefix(P=-1) == INVALID
+    assert shared_prefix(P=7) == INVALID                           # prefix longer than L
+    assert shared_prefix(q=None) == INVALID
+    assert shared_prefix(ws=None) == WORKSPACE
+    assert shared_prefix(wsb=16) == WORKSPACE
+    assert shared_prefix(R=0) == OK
+
+
 def test_slot_mapping_checks():
     f = lib.pa_compute_slot_mapping
     assert f(None, FAKE, 7, FAKE, FAKE, 4, 4, 16, None) == INVALID
