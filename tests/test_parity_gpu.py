@@ -167,6 +167,20 @@ def test_decode_head_groupings_and_dtypes(dtype, Hq, Hkv, D):
     full_check(_variant(dtype, Hq, Hkv, D, lens, seed=12 + Hq + D), num_splits=5)
 
 
+@pytest.mark.parametrize("R", [63, 64, 65, 257, 700])
+def test_decode_large_batches(R):
+    """Each wave scans the batch 64 requests at a time to find its ranges:
+    batches around one window and spanning many windows."""
+    rng = np.random.default_rng(R)
+    lens = [int(x) for x in rng.integers(1, 120, size=R)]
+    w = build_workload(f"many_{R}", dtype="bf16", num_q_heads=8, num_kv_heads=2, head_dim=64,
+                       num_blocks=sum(-(-L // 16) for L in lens) + 8,
+                       requests=[(L - 1, 1) for L in lens], seed=R)
+    full_check(w)
+    full_check(w, num_splits=37)
+    full_check(w, fused=True)
+
+
 def test_decode_single_key_returns_v0():
     w = _variant("bf16", 8, 2, 128, [1, 1, 1], seed=3)
     pool, _, g_pool, out = gu.run_step(w)
