@@ -210,7 +210,9 @@ int pa_attention_decode_shared_prefix(void* out, const void* q, const void* kv_c
  *   one launch (one tile wave and one decode wave per SIMD), so the
  *   compute-bound and the bandwidth-bound halves overlap; the decode merge
  *   follows.  PA_MIXED_OVERLAP=0 in the environment launches them one after
- *   the other instead.
+ *   the other instead.  An fp32 cache has no matrix-core tiles: its chunks
+ *   are attended in fp32 on the vector ALU (16-token tiles), in a launch
+ *   before the decode rows.
  *
  *   out, q              [num_tokens, num_q_heads, head_dim], cache dtype.
  *   seq_lens            [num_seqs]: keys of the request's last query,

@@ -37,10 +37,11 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 bool overlap_enabled();
 
-// Prefill tiles run beside the decode rows when the batch can hold both: a
-// chunk (max_query_len > 1) and at least one other request.
-bool tiles_beside_decode(int num_seqs, int max_query_len) {
-  return max_query_len > 1 && num_seqs >= 2 && overlap_enabled();
+// Matrix-core prefill tiles run beside the decode rows when the batch can
+// hold both: a chunk (max_query_len > 1) and at least one other request.
+// fp32 tiles (vector ALU) run before the decode rows instead.
+bool tiles_beside_decode(int num_seqs, int max_query_len, int dtype) {
+  return max_query_len > 1 && num_seqs >= 2 && dtype != PA_F32 && overlap_enabled();
 }
 
 // Decode waves beside the tiles of a chunk of up to max_query_len tokens
@@ -213,7 +214,8 @@ static int attention_common(void* out, const void* q, const void* kv_cache, int6
   const int P = shared_prefix_blocks;
   const int chunks = plan_chunks(num_seqs, num_kv_heads, group,
                                  P > 0 ? max(max_seq_len - P * pa::kBlockSize, 1) : max_seq_len,
-                                 num_splits, P > 0 || tiles_beside_decode(num_seqs, max_query_len),
+                                 num_splits,
+                                 P > 0 || tiles_beside_decode(num_seqs, max_query_len, dtype),
                                  P > 0 ? num_seqs : max_query_len);
   const WsLayout lay = workspace_layout(num_seqs, num_q_heads, head_dim,
                                         chunks + (P > 0 ? num_seqs : 0));
@@ -294,8 +296,6 @@ int mixed_impl(void* out, const void* q, const void* kv_cache, int64_t num_block
   if (!query_start_loc || !num_computed_tokens) return PA_ERR_INVALID_ARG;
   a.fresh = fresh;
   const int group = num_q_heads / num_kv_heads;
-  if (max_query_len > 1 && !pa::prefill_supported(dtype, head_dim, group))
-    return PA_ERR_UNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
   a.qsl = query_start_loc;
   if (max_query_len > 1) {
@@ -315,14 +315,15 @@ int mixed_impl(void* out, const void* q, const void* kv_cache, int64_t num_block
     p.max_query_len = max_query_len;
     p.scale_log2 = a.scale_log2;
     p.fresh = fresh;
-    if (tiles_beside_decode(num_seqs, max_query_len)) {
+    if (tiles_beside_decode(num_seqs, max_query_len, dtype)) {
       // tiles and decode ranges in one launch, then the merge
       p.beside_decode = 1;
       const hipError_t e = pa::launch_fused(a, p, dtype, head_dim, group, s);
       if (e != hipSuccess) return PA_ERR_HIP;
       return hip_status(pa::launch_decode_merge(a, dtype, head_dim, group, s));
     }
-    const hipError_t e = pa::launch_prefill(p, dtype, head_dim, group, s);
+    const hipError_t e = dtype == PA_F32 ? pa::launch_prefill_f32(p, head_dim, group, s)
+                                         : pa::launch_prefill(p, dtype, head_dim, group, s);
     if (e != hipSuccess) return PA_ERR_HIP;
     if (num_seqs == 1) return PA_OK;  // the one request is the chunk: no decode rows
   }

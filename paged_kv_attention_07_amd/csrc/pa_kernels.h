@@ -106,6 +106,10 @@ hipError_t launch_prefill(const PrefillArgs& a, int dtype, int head_dim, int gro
 
 bool prefill_supported(int dtype, int head_dim, int group);
 
+// fp32 cache: the same prefill-chunk attention on the vector ALU (16-token
+// tiles, grid max_tiles x num_kv_heads); head_dim 64 | 128, group 1|2|4|8.
+hipError_t launch_prefill_f32(const PrefillArgs& a, int head_dim, int group, hipStream_t stream);
+
 // Prefill tiles (32 tokens per wave) and the decode split in one launch; the
 // caller launches the decode merge afterwards on the same stream.
 hipError_t launch_fused(const DecodeArgs& da, const PrefillArgs& p, int dtype, int head_dim,

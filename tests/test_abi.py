@@ -161,7 +161,7 @@ def test_mixed_checks():
     assert mixed(nc=None) == INVALID
     assert mixed(T=-1) == INVALID
     assert mixed(Q=-1) == INVALID
-    assert mixed(dtype=0) == UNSUPPORTED      # fp32 has no prefill-tile path
+    assert mixed(dtype=0, wsb=8) == WORKSPACE  # fp32 chunks are accepted (vector-ALU tiles)
     assert mixed(wsb=8) == WORKSPACE
     assert mixed(T=0) == OK
 
@@ -201,7 +201,7 @@ def test_cache_and_attend_checks():
         assert f(wsb=16) == WORKSPACE
     assert cache_decode(R=0, k=None, v=None) == OK             # nothing to store or attend
     assert cache_mixed(T=0, k=None, v=None) == OK
-    assert cache_mixed(dtype=0) == UNSUPPORTED                 # fp32 has no prefill-tile path
+    assert cache_mixed(dtype=0, wsb=8) == WORKSPACE            # fp32 chunks are accepted
 
 
 def shared_prefix(**kw):

@@ -90,7 +90,8 @@ def test_decode_split_counts(splits):
 
 @pytest.mark.parametrize("dtype,Hq,Hkv,D", [
     ("bf16", 32, 8, 128), ("bf16", 8, 8, 128), ("bf16", 8, 4, 64), ("f16", 16, 2, 128),
-    ("bf16", 16, 2, 64)])
+    ("bf16", 16, 2, 64), ("f32", 32, 8, 128), ("f32", 4, 4, 64), ("f32", 8, 4, 64),
+    ("f32", 16, 2, 128)])
 def test_mixed_groupings(dtype, Hq, Hkv, D):
     """Chunks starting mid-block and on block boundaries, decode rows, and a
     request with no tokens this step."""

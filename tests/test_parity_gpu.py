@@ -205,11 +205,26 @@ def test_mixed_groupings(dtype, Hq, Hkv, D):
     full_check(_variant(dtype, Hq, Hkv, D, lens, seed=21 + Hq, q_lens=q_lens))
 
 
-def test_mixed_chunked_equivalence():
+@pytest.mark.parametrize("Hq,Hkv,D", [(4, 4, 64), (8, 4, 64), (8, 2, 128), (16, 2, 64),
+                                      (32, 8, 128)])
+def test_mixed_f32(Hq, Hkv, D):
+    """fp32 cache: chunks go to the vector-ALU tiles (every head grouping), decode
+    rows to the split; chunk lengths 2..100 across tile edges, chunks starting
+    mid-block, a request with no tokens this step, 1e-5 vs the oracle."""
+    lens = [40, 17, 300, 5, 64, 129, 1, 700, 90, 33]
+    q_lens = [40, 2, 33, 1, 16, 100, 1, 64, 0, 17]
+    full_check(_variant("f32", Hq, Hkv, D, lens, seed=71 + Hq + D, q_lens=q_lens))
+    # one request alone (tiles only), and one with its whole prompt as the chunk
+    full_check(_variant("f32", Hq, Hkv, D, [77], seed=72, q_lens=[60]))
+    full_check(_variant("f32", Hq, Hkv, D, [257], seed=73, q_lens=[257]))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_mixed_chunked_equivalence(dtype):
     """A 1000-token prompt prefilled in chunks 254/254/254/238 ("vllm v1 源码精读（三）"
     §4.2) gives, chunk by chunk, the rows of one full prefill (both vs the oracle)."""
     L = 1000
-    full = _variant("bf16", 32, 8, 128, [L], seed=31, q_lens=[L])
+    full = _variant(dtype, 32, 8, 128, [L], seed=31, q_lens=[L])
     pool = gu.poisoned_pool(full)
     _, _, _, out_full = gu.run_step(full, poison=False)
     _, r_pool, r_full = gu.oracle_step(full, full.pool)
