@@ -284,6 +284,52 @@ int pa_cache_and_attend_mixed(void* out, const void* q, const void* key, const v
                               void* workspace, size_t workspace_bytes, int32_t num_splits,
                               void* stream);
 
+/*
+ * pa_check_metadata -- check, on the device, the step metadata the calls
+ * above trust (the pages' model runner takes it from its scheduler
+ * unchecked: [P4] §3.4 block tables and slots, §4.2 packed query offsets and
+ * computed counts, §3.5 shared prefix blocks).  For a caller debugging its
+ * own scheduler: run it on the same stream before the attention call, then
+ * read *flags whenever convenient (it is not synchronised here).
+ *
+ *   flags                 [1] uint32, caller-zeroed; each violated condition
+ *                         ORs its pa_meta_flag bit (device atomics).
+ *   block_table, block_table_stride, seq_lens, num_seqs, max_seq_len,
+ *   num_blocks            as the attention calls.
+ *   query_start_loc, num_computed_tokens
+ *                         [num_seqs + 1], [num_seqs] for a mixed batch, or
+ *                         both null for a decode batch (one query per
+ *                         request, seq_lens >= 1).
+ *   slot_mapping          [num_tokens] int64 or null: checked inside the pool
+ *                         and distinct (negative = skipped token); the
+ *                         distinctness test compares all pairs, O(T^2).
+ *   num_tokens, max_query_len
+ *                         (host) as pa_attention_mixed (decode: num_seqs, 1).
+ *   shared_prefix_blocks  (host) P >= 0: also check that every row's first P
+ *                         entries equal row 0's and 16 P <= seq_lens[r];
+ *                         P <= block_table_stride.
+ *   Only the metadata is read, each array within its given extent whatever
+ *   its contents.  Host argument errors return PA_ERR_INVALID_ARG.
+ */
+typedef enum {
+  PA_META_SEQ_LEN = 1u << 0,       /* seq_len < 0 or > max_seq_len (decode: < 1) */
+  PA_META_TABLE_WIDTH = 1u << 1,   /* ceil(seq_len / 16) > block_table_stride */
+  PA_META_BLOCK_ID = 1u << 2,      /* a table entry read by attention not in [0, num_blocks) */
+  PA_META_QUERY_START = 1u << 3,   /* qsl[0] != 0, qsl decreasing, or qsl[R] != num_tokens */
+  PA_META_COMPUTED = 1u << 4,      /* num_computed < 0 or != seq_len - q_len */
+  PA_META_QUERY_LEN = 1u << 5,     /* q_len > max_query_len */
+  PA_META_SLOT_RANGE = 1u << 6,    /* slot >= num_blocks * 16 */
+  PA_META_SLOT_DUP = 1u << 7,      /* two tokens of the call share a slot */
+  PA_META_SHARED_PREFIX = 1u << 8  /* rows differ in the prefix blocks, or too short */
+} pa_meta_flag;
+
+int pa_check_metadata(uint32_t* flags, const int32_t* block_table, int32_t block_table_stride,
+                      const int32_t* seq_lens, const int32_t* query_start_loc,
+                      const int32_t* num_computed_tokens, const int64_t* slot_mapping,
+                      int32_t num_seqs, int32_t num_tokens, int32_t max_query_len,
+                      int32_t max_seq_len, int64_t num_blocks, int32_t block_size,
+                      int32_t shared_prefix_blocks, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

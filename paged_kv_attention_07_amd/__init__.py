@@ -19,7 +19,7 @@ __all__ = [
     "pa_attention_workspace_size", "pa_attention_decode", "pa_attention_mixed",
     "pa_attention_decode_shared_prefix", "pa_attention_decode_shared_prefix_workspace_size",
     "pa_cache_and_attend_decode", "pa_cache_and_attend_mixed",
-    "pa_status_string", "pa_version",
+    "pa_check_metadata", "META_FLAGS", "pa_status_string", "pa_version",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -85,6 +85,12 @@ lib.pa_cache_and_attend_mixed.argtypes = [
     _i32, _i32, _i32, _f32,                                   # max_q max_L Hq scale
     _vp, _sz, _i32, _vp]                                      # ws ws_bytes splits stream
 lib.pa_cache_and_attend_mixed.restype = ctypes.c_int
+
+lib.pa_check_metadata.argtypes = [
+    _vp, _vp, _i32, _vp, _vp, _vp, _vp,       # flags bt stride seq_lens qsl nc slots
+    _i32, _i32, _i32, _i32, _i64, _i32, _i32,  # R T max_q max_L NB B prefix_blocks
+    _vp]
+lib.pa_check_metadata.restype = ctypes.c_int
 
 PA_F32, PA_BF16, PA_F16 = 0, 1, 2
 DTYPE_CODES = {"f32": PA_F32, "bf16": PA_BF16, "f16": PA_F16}
@@ -362,3 +368,54 @@ def pa_cache_and_attend_mixed(q, key, value, kv_cache, block_table, seq_lens, qu
         _stream())
     _check("pa_cache_and_attend_mixed", st)
     return out
+
+
+# pa_meta_flag bits of pa_check_metadata (include/pa.h), in bit order
+META_FLAGS = ("seq_len", "table_width", "block_id", "query_start", "computed", "query_len",
+              "slot_range", "slot_dup", "shared_prefix")
+
+
+def pa_check_metadata(block_table, seq_lens, num_blocks: int, max_seq_len: int,
+                      query_start_loc=None, num_computed_tokens=None, slot_mapping=None,
+                      num_tokens: Optional[int] = None, max_query_len: Optional[int] = None,
+                      shared_prefix_blocks: int = 0, block_size: int = 16, flags=None):
+    """Check the step metadata on the device; see pa.h.  ``num_tokens`` is the
+    caller's token count for a mixed batch (default: the slot_mapping length,
+    else query_start_loc[-1], read back).  With ``flags`` (a zeroed one-element
+    int32 GPU tensor) the call only launches and returns ``flags``; without,
+    it synchronises the stream and returns the names of the violated
+    conditions (empty: all hold)."""
+    torch = _torch()
+    R = int(seq_lens.shape[0])
+    mixed = query_start_loc is not None
+    if mixed and (num_computed_tokens is None or int(query_start_loc.shape[0]) != R + 1):
+        raise ValueError("a mixed batch needs query_start_loc [R+1] and num_computed_tokens [R]")
+    if not mixed:
+        T = R
+    elif num_tokens is not None:
+        T = int(num_tokens)
+    elif slot_mapping is not None:
+        T = int(slot_mapping.shape[0])
+    else:
+        T = int(query_start_loc[-1].item())
+    if slot_mapping is not None and int(slot_mapping.shape[0]) != T:
+        raise ValueError(f"slot_mapping must have {T} entries")
+    if max_query_len is None:
+        max_query_len = 1 if not mixed else T
+    own = flags is None
+    if own:
+        flags = torch.zeros(1, dtype=torch.int32, device=seq_lens.device)
+    st = lib.pa_check_metadata(
+        _dev(flags, "flags", torch.int32, 1), _dev(block_table, "block_table", torch.int32, 2),
+        int(block_table.shape[1]), _dev(seq_lens, "seq_lens", torch.int32, 1),
+        _dev(query_start_loc, "query_start_loc", torch.int32, 1) if mixed else None,
+        _dev(num_computed_tokens, "num_computed_tokens", torch.int32, 1) if mixed else None,
+        _dev(slot_mapping, "slot_mapping", torch.int64, 1) if slot_mapping is not None else None,
+        R, T, int(max_query_len), int(max_seq_len), int(num_blocks), int(block_size),
+        int(shared_prefix_blocks), _stream())
+    _check("pa_check_metadata", st)
+    if not own:
+        return flags
+    torch.cuda.current_stream().synchronize()
+    bits = int(flags.item()) & 0xFFFFFFFF
+    return [name for i, name in enumerate(META_FLAGS) if bits >> i & 1]

@@ -402,6 +402,39 @@ int pa_cache_and_attend_mixed(void* out, const void* q, const void* key, const v
                     num_q_heads, scale, workspace, workspace_bytes, num_splits, f, stream);
 }
 
+int pa_check_metadata(uint32_t* flags, const int32_t* block_table, int32_t block_table_stride,
+                      const int32_t* seq_lens, const int32_t* query_start_loc,
+                      const int32_t* num_computed_tokens, const int64_t* slot_mapping,
+                      int32_t num_seqs, int32_t num_tokens, int32_t max_query_len,
+                      int32_t max_seq_len, int64_t num_blocks, int32_t block_size,
+                      int32_t shared_prefix_blocks, void* stream) {
+  if (block_size != pa::kBlockSize) return PA_ERR_UNSUPPORTED;
+  if (!flags || num_seqs < 0 || num_tokens < 0 || max_query_len < 0 || max_seq_len < 0 ||
+      block_table_stride < 0 || num_blocks < 0 || shared_prefix_blocks < 0 ||
+      shared_prefix_blocks > block_table_stride)
+    return PA_ERR_INVALID_ARG;
+  if ((query_start_loc == nullptr) != (num_computed_tokens == nullptr)) return PA_ERR_INVALID_ARG;
+  if (!query_start_loc && num_tokens != num_seqs) return PA_ERR_INVALID_ARG;  // decode: T = R
+  if (num_seqs > 0 && (!block_table || !seq_lens)) return PA_ERR_INVALID_ARG;
+  if (num_seqs == 0 && num_tokens == 0) return PA_OK;
+  if (num_seqs == 0 && query_start_loc) return PA_ERR_INVALID_ARG;  // tokens without requests
+  pa::MetaCheckArgs a{};
+  a.flags = flags;
+  a.block_table = block_table;
+  a.bt_stride = block_table_stride;
+  a.seq_lens = seq_lens;
+  a.qsl = query_start_loc;
+  a.num_computed = num_computed_tokens;
+  a.slots = slot_mapping;
+  a.num_seqs = num_seqs;
+  a.num_tokens = num_tokens;
+  a.max_query_len = max_query_len;
+  a.max_seq_len = max_seq_len;
+  a.num_blocks = num_blocks;
+  a.shared_prefix_blocks = num_seqs > 0 ? shared_prefix_blocks : 0;
+  return hip_status(pa::launch_check_metadata(a, static_cast<hipStream_t>(stream)));
+}
+
 size_t pa_attention_decode_shared_prefix_workspace_size(int32_t num_seqs, int32_t num_q_heads,
                                                         int32_t num_kv_heads, int32_t head_dim,
                                                         int32_t max_seq_len,

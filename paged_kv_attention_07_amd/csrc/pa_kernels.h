@@ -78,6 +78,25 @@ struct PrefillArgs {
   NewTokens fresh;
 };
 
+// Arguments of the metadata check (pa_check_metadata).
+struct MetaCheckArgs {
+  uint32_t* flags;            // OR of pa_meta_flag bits
+  const int32_t* block_table;
+  int32_t bt_stride;
+  const int32_t* seq_lens;
+  const int32_t* qsl;         // null: a decode batch (one query per request)
+  const int32_t* num_computed;
+  const int64_t* slots;       // or null
+  int32_t num_seqs;
+  int32_t num_tokens;
+  int32_t max_query_len;
+  int32_t max_seq_len;
+  int64_t num_blocks;
+  int32_t shared_prefix_blocks;  // 0: no shared prefix to check
+};
+
+hipError_t launch_check_metadata(const MetaCheckArgs& a, hipStream_t stream);
+
 constexpr int kQueriesPerTile = 16;  // fewest query tokens per prefill tile (grid bound)
 
 hipError_t launch_slot_mapping(int64_t* slot_mapping, const int32_t* block_table,

@@ -275,3 +275,26 @@ def test_engine_checks():
                                 ctypes.byref(h)) == WORKSPACE
     assert lib.pa_engine_create(ctypes.byref(cfg), ctypes.byref(geo), FAKE,
                                 ctypes.c_void_p(0x100010), size, ctypes.byref(h)) == INVALID
+
+
+def check_meta(**kw):
+    a = dict(flags=FAKE, bt=FAKE, stride=7, sl=FAKE, qsl=FAKE, nc=FAKE, slots=None, R=4, T=20,
+             Q=17, L=100, NB=64, B=16, P=0)
+    a.update(kw)
+    return lib.pa_check_metadata(a["flags"], a["bt"], a["stride"], a["sl"], a["qsl"], a["nc"],
+                                 a["slots"], a["R"], a["T"], a["Q"], a["L"], a["NB"], a["B"],
+                                 a["P"], None)
+
+
+def test_check_metadata_host_checks():
+    """Host arguments of the device metadata check are validated before any
+    launch."""
+    assert check_meta(flags=None) == INVALID
+    assert check_meta(B=8) == UNSUPPORTED
+    assert check_meta(R=-1) == INVALID and check_meta(T=-1) == INVALID
+    assert check_meta(nc=None) == INVALID                # offsets without computed counts
+    assert check_meta(qsl=None, nc=None) == INVALID      # decode batch: T must equal R
+    assert check_meta(bt=None) == INVALID and check_meta(sl=None) == INVALID
+    assert check_meta(P=8) == INVALID                    # prefix wider than the table
+    assert check_meta(R=0) == INVALID                    # tokens without requests
+    assert check_meta(R=0, T=0) == OK                    # nothing to check

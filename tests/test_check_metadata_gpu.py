@@ -1,0 +1,171 @@
+"""Device-side metadata check (pa_check_metadata) through the C ABI.
+
+Every committed workload's metadata passes; each planted violation (a change
+to the metadata only, on the host) sets its flag, and the oracle's host-side
+validate_metadata rejects the same metadata wherever it covers the condition.
+The check reads only the metadata arrays, each within its extent, so bad
+values are safe inputs for it.
+"""
+
+import dataclasses
+
+import numpy as np
+import pytest
+
+import oracle
+from workloads import make_workload
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # collected on CPU hosts, never run there
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import paged_kv_attention_07_amd as pa  # noqa: E402  (fails loudly if libpa.so is missing)
+
+
+def _t(a, dtype):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=dtype)).cuda()
+
+
+def device_check(w, slots=None, decode=False, max_query_len=None, max_seq_len=None,
+                 prefix=0, num_tokens=None):
+    print(f"[case] check {w.name} decode={decode} prefix={prefix}", flush=True)
+    args = dict(max_seq_len=int(w.seq_lens.max()) if max_seq_len is None else max_seq_len,
+                shared_prefix_blocks=prefix,
+                slot_mapping=None if slots is None else _t(slots, np.int64))
+    if not decode:
+        args.update(query_start_loc=_t(w.query_start_loc, np.int32),
+                    num_computed_tokens=_t(w.num_computed, np.int32),
+                    num_tokens=w.num_tokens if num_tokens is None else num_tokens,
+                    max_query_len=int(np.diff(w.query_start_loc).max())
+                    if max_query_len is None else max_query_len)
+    return pa.pa_check_metadata(_t(w.block_table, np.int32), _t(w.seq_lens, np.int32),
+                                w.num_blocks, **args)
+
+
+def oracle_rejects(w, slots=None):
+    try:
+        oracle.validate_metadata(w.block_table, w.seq_lens, w.query_start_loc, w.num_computed,
+                                 w.num_blocks, 16, slots)
+    except ValueError:
+        return True
+    return False
+
+
+def slots_of(w):
+    return oracle.slot_mapping(w.block_table, w.query_start_loc, w.num_computed, 16)
+
+
+@pytest.mark.parametrize("name", ["tiny_f32_decode", "decode_bf16_small", "mixed_bf16_small",
+                                  "prefix_shared_small", "long_decode_small",
+                                  "decode_bf16_64req", "mixed_chunked_prefill_bf16",
+                                  "prefill_chunk_2048_bf16"])
+def test_committed_workloads_pass(name):
+    w = make_workload(name, values=False)
+    s = slots_of(w)
+    assert not oracle_rejects(w, s)
+    assert device_check(w, s) == []
+    if w.is_decode_only:
+        assert device_check(w, s, decode=True) == []
+    P = int(w.meta.get("shared_prefix_blocks", 0))
+    if P:
+        assert device_check(w, s, decode=True, prefix=P) == []
+
+
+def _mixed():
+    return make_workload("mixed_bf16_small", values=False)
+
+
+def _copy(w, **arrays):
+    return dataclasses.replace(w, **{k: np.array(v) for k, v in arrays.items()})
+
+
+def _mutations():
+    """(label, metadata change, expected flag, whether the oracle covers it)."""
+    w = _mixed()
+    qlen = np.diff(w.query_start_loc)
+    long_r = int(np.argmax(qlen))
+    out = []
+
+    sl = w.seq_lens.copy(); nc = w.num_computed.copy()
+    r = int(np.argmax(w.seq_lens % 16 != 0))          # a request whose last block has room
+    sl[r] += 1
+    out.append(("seq_len != computed + q_len", _copy(w, seq_lens=sl), None, "computed", True))
+    nc = w.num_computed.copy(); nc[0] = -1
+    out.append(("negative computed", _copy(w, num_computed=nc), None, "computed", True))
+    bt = w.block_table.copy(); bt[long_r, 0] = w.num_blocks
+    out.append(("block id past the pool", _copy(w, block_table=bt), None, "block_id", True))
+    bt = w.block_table.copy(); bt[long_r, 0] = -1
+    out.append(("block id -1 inside seq_len", _copy(w, block_table=bt), None, "block_id", True))
+    q = w.query_start_loc.copy(); q[0] = 1
+    out.append(("qsl[0] != 0", _copy(w, query_start_loc=q), None, "query_start", True))
+    q = w.query_start_loc.copy(); q[2], q[3] = q[3], q[2]
+    out.append(("qsl decreasing", _copy(w, query_start_loc=q), None, "query_start", True))
+    q = w.query_start_loc.copy(); q[-1] -= 1
+    out.append(("qsl[R] != T", _copy(w, query_start_loc=q), None, "query_start", True))
+    bt = np.ascontiguousarray(w.block_table[:, :2])
+    out.append(("table narrower than seq_len", _copy(w, block_table=bt), None, "table_width",
+                True))
+    s = slots_of(w); s[5] = s[6]
+    out.append(("duplicate slot", w, s, "slot_dup", True))
+    s = slots_of(w); s[3] = w.num_blocks * 16
+    out.append(("slot past the pool", w, s, "slot_range", True))
+    return out
+
+
+@pytest.mark.parametrize("case", range(10))
+def test_planted_violation_sets_its_flag(case):
+    label, w, slots, flag, oracle_covers = _mutations()[case]
+    print(f"[case] planted: {label}", flush=True)
+    got = device_check(w, slots, num_tokens=_mixed().num_tokens)  # the caller's own count
+    assert flag in got, (label, got)
+    if oracle_covers:
+        assert oracle_rejects(w, slots), label
+    # skipped tokens (negative slots) are not violations
+    if slots is not None:
+        s = slots_of(w)
+        s[::3] = -1
+        assert device_check(w, s) == []
+
+
+def test_host_bounds_are_checked():
+    w = _mixed()
+    qmax = int(np.diff(w.query_start_loc).max())
+    assert device_check(w, max_query_len=qmax - 1) == ["query_len"]
+    assert "seq_len" in device_check(w, max_seq_len=int(w.seq_lens.max()) - 1)
+
+
+def test_decode_batch_rules():
+    w = make_workload("decode_bf16_small", values=False)
+    assert device_check(w, decode=True) == []
+    sl = w.seq_lens.copy(); sl[1] = 0
+    assert "seq_len" in device_check(_copy(w, seq_lens=sl), decode=True)
+
+
+def test_shared_prefix_rules():
+    w = make_workload("prefix_shared_small", values=False)
+    P = int(w.meta["shared_prefix_blocks"])
+    assert device_check(w, decode=True, prefix=P) == []
+    bt = w.block_table.copy(); bt[3, P - 1] = bt[3, P]     # a row leaves the prefix early
+    assert device_check(_copy(w, block_table=bt), decode=True, prefix=P) == ["shared_prefix"]
+    sl = w.seq_lens.copy(); sl[2] = 16 * P - 1                # shorter than the prefix
+    assert "shared_prefix" in device_check(_copy(w, seq_lens=sl), decode=True, prefix=P)
+
+
+def test_flags_accumulate_without_sync():
+    """With a caller-owned flag word the call only launches; a second call
+    ORs into the same word."""
+    w = _mixed()
+    flags = torch.zeros(1, dtype=torch.int32, device="cuda")
+    bt = w.block_table.copy(); bt[0, 0] = -5
+    nc = w.num_computed.copy(); nc[1] = -1
+    for m in (_copy(w, block_table=bt), _copy(w, num_computed=nc)):
+        pa.pa_check_metadata(_t(m.block_table, np.int32), _t(m.seq_lens, np.int32),
+                             m.num_blocks, int(m.seq_lens.max()),
+                             query_start_loc=_t(m.query_start_loc, np.int32),
+                             num_computed_tokens=_t(m.num_computed, np.int32),
+                             num_tokens=m.num_tokens, max_query_len=m.num_tokens, flags=flags)
+    torch.cuda.synchronize()
+    bits = int(flags.item())
+    assert bits == (1 << pa.META_FLAGS.index("block_id")) | (1 << pa.META_FLAGS.index("computed"))
