@@ -20,6 +20,10 @@ __all__ = [
     "pa_attention_decode_shared_prefix", "pa_attention_decode_shared_prefix_workspace_size",
     "pa_cache_and_attend_decode", "pa_cache_and_attend_mixed",
     "pa_check_metadata", "META_FLAGS", "pa_status_string", "pa_version",
+    # short names: host bounds read back from the device when not given
+    "compute_slot_mapping", "reshape_and_cache", "copy_blocks", "attention_decode",
+    "attention_mixed", "cache_and_attend_decode", "cache_and_attend_mixed",
+    "attention_decode_shared_prefix",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -419,3 +423,72 @@ def pa_check_metadata(block_table, seq_lens, num_blocks: int, max_seq_len: int,
     torch.cuda.current_stream().synchronize()
     bits = int(flags.item()) & 0xFFFFFFFF
     return [name for i, name in enumerate(META_FLAGS) if bits >> i & 1]
+
+
+# ---- short names ------------------------------------------------------------
+# The pa_* functions take the host bounds (max_seq_len, max_query_len) as
+# arguments, as the C ABI does, so they never synchronise.  These short forms
+# follow the pages' call shapes; a bound left as None is read back from the
+# device metadata (one synchronisation of the current stream).
+
+
+def _max_of(t) -> int:
+    return int(t.max().item()) if t.numel() else 0
+
+
+def _max_query_len(query_start_loc) -> int:
+    return _max_of(query_start_loc[1:] - query_start_loc[:-1]) if query_start_loc.numel() > 1 else 0
+
+
+compute_slot_mapping = pa_compute_slot_mapping
+reshape_and_cache = pa_reshape_and_cache
+copy_blocks = pa_copy_blocks
+
+
+def attention_decode(q, kv_cache, block_table, seq_lens, scale: float,
+                     max_seq_len: Optional[int] = None, **kw):
+    """pa_attention_decode with max_seq_len defaulting to max(seq_lens)."""
+    if max_seq_len is None:
+        max_seq_len = _max_of(seq_lens)
+    return pa_attention_decode(q, kv_cache, block_table, seq_lens, scale, max_seq_len, **kw)
+
+
+def attention_decode_shared_prefix(q, kv_cache, block_table, seq_lens, scale: float,
+                                   shared_prefix_blocks: int, max_seq_len: Optional[int] = None,
+                                   **kw):
+    if max_seq_len is None:
+        max_seq_len = _max_of(seq_lens)
+    return pa_attention_decode_shared_prefix(q, kv_cache, block_table, seq_lens, scale,
+                                             max_seq_len, shared_prefix_blocks, **kw)
+
+
+def attention_mixed(q, kv_cache, block_table, seq_lens, query_start_loc, num_computed_tokens,
+                    scale: float, max_query_len: Optional[int] = None,
+                    max_seq_len: Optional[int] = None, **kw):
+    """pa_attention_mixed with the bounds defaulting to the batch's own."""
+    if max_query_len is None:
+        max_query_len = _max_query_len(query_start_loc)
+    if max_seq_len is None:
+        max_seq_len = _max_of(seq_lens)
+    return pa_attention_mixed(q, kv_cache, block_table, seq_lens, query_start_loc,
+                              num_computed_tokens, scale, max_query_len, max_seq_len, **kw)
+
+
+def cache_and_attend_decode(q, key, value, kv_cache, block_table, seq_lens, scale: float,
+                            max_seq_len: Optional[int] = None, **kw):
+    if max_seq_len is None:
+        max_seq_len = _max_of(seq_lens)
+    return pa_cache_and_attend_decode(q, key, value, kv_cache, block_table, seq_lens, scale,
+                                      max_seq_len, **kw)
+
+
+def cache_and_attend_mixed(q, key, value, kv_cache, block_table, seq_lens, query_start_loc,
+                           num_computed_tokens, scale: float, max_query_len: Optional[int] = None,
+                           max_seq_len: Optional[int] = None, **kw):
+    if max_query_len is None:
+        max_query_len = _max_query_len(query_start_loc)
+    if max_seq_len is None:
+        max_seq_len = _max_of(seq_lens)
+    return pa_cache_and_attend_mixed(q, key, value, kv_cache, block_table, seq_lens,
+                                     query_start_loc, num_computed_tokens, scale, max_query_len,
+                                     max_seq_len, **kw)

@@ -510,3 +510,35 @@ def test_shared_prefix_matches_plain_decode(name, P):
     a = oracle.decode_bits(gu.from_device(dev.attend(), w.dtype), w.dtype)
     b = oracle.decode_bits(gu.from_device(dev.attend(shared_prefix=P), w.dtype), w.dtype)
     assert np.max(np.abs(a - b)) <= 6e-3
+
+
+@pytest.mark.parametrize("name", ["decode_bf16_small", "mixed_bf16_small", "tiny_f32_decode"])
+def test_short_names_match_full_names(name):
+    """The short-name wrappers (host bounds read back from the device) give the
+    bits of the pa_* calls given the same bounds, and the oracle's result."""
+    w = workload(name)
+    print(f"[case] short names {name}", flush=True)
+    pool = gu.poisoned_pool(w)
+    outs = []
+    for short in (False, True):
+        dev = gu.Device(w, pool)
+        if short:
+            slots = pa.compute_slot_mapping(dev.block_table, dev.qsl, dev.num_computed,
+                                            w.num_tokens)
+            pa.reshape_and_cache(dev.k_new, dev.v_new, dev.kv, slots)
+        else:
+            slots = pa.pa_compute_slot_mapping(dev.block_table, dev.qsl, dev.num_computed,
+                                               w.num_tokens)
+            pa.pa_reshape_and_cache(dev.k_new, dev.v_new, dev.kv, slots)
+        args = (dev.q, dev.kv, dev.block_table, dev.seq_lens)
+        if w.is_decode_only:
+            out = (pa.attention_decode(*args, w.scale) if short else
+                   pa.pa_attention_decode(*args, w.scale, w.max_seq_len))
+        else:
+            args += (dev.qsl, dev.num_computed)
+            out = (pa.attention_mixed(*args, w.scale) if short else
+                   pa.pa_attention_mixed(*args, w.scale, w.max_query_len, w.max_seq_len))
+        outs.append(gu.from_device(out, w.dtype))
+    assert np.array_equal(gu.bits(outs[0]), gu.bits(outs[1]))
+    _, _, r_out = gu.oracle_step(w, pool)
+    gu.check_close(w, outs[1], r_out, what=f"{name} short names")
