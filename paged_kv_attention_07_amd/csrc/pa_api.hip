@@ -23,6 +23,7 @@ constexpr int kMinWavesBesidePrefill = 256 * 4;
 constexpr int kMaxWavesBesidePrefill = 256 * 6;
 constexpr int kMinBlocksPerRange = 4;
 
+// query heads per wave of the matrix-core prefill tiles
 int heads_per_wave(int group) { return group < 4 ? group : 4; }
 
 bool group_ok(int group) { return group == 1 || group == 2 || group == 4 || group == 8; }
@@ -57,10 +58,14 @@ int64_t waves_beside_prefill(int num_kv_heads, int group, int max_query_len) {
   return w;
 }
 
+// Ranges per KV head.  dtype and head_dim set the waves per GQA group; the
+// workspace-size queries, which have no dtype, plan with PA_BF16: its waves
+// serve the most heads each, so its plan has the most ranges and bounds the
+// others.
 int plan_chunks(int num_seqs, int num_kv_heads, int group, int max_seq_len, int num_splits,
-                bool beside_prefill, int max_query_len) {
+                bool beside_prefill, int max_query_len, int dtype, int head_dim) {
   if (num_splits > 0) return num_splits;
-  const int hg = group / heads_per_wave(group);
+  const int hg = group / pa::decode_heads_per_wave(dtype, head_dim, group);
   const int64_t blocks_upper = (int64_t)num_seqs * ceil_div(max_seq_len, pa::kBlockSize);
   const int64_t waves = beside_prefill
                             ? waves_beside_prefill(num_kv_heads, group, max_query_len)
@@ -186,7 +191,8 @@ size_t pa_attention_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t
   // the plan without concurrent tiles has the most ranges: size for it, so the
   // buffer covers either plan
   const int chunks =
-      plan_chunks(num_seqs, num_kv_heads, group, max_seq_len, num_splits, false, 0);
+      plan_chunks(num_seqs, num_kv_heads, group, max_seq_len, num_splits, false, 0, PA_BF16,
+                  head_dim);
   return workspace_layout(num_seqs, num_q_heads, head_dim, chunks).total;
 }
 
@@ -216,7 +222,7 @@ static int attention_common(void* out, const void* q, const void* kv_cache, int6
                                  P > 0 ? max(max_seq_len - P * pa::kBlockSize, 1) : max_seq_len,
                                  num_splits,
                                  P > 0 || tiles_beside_decode(num_seqs, max_query_len, dtype),
-                                 P > 0 ? num_seqs : max_query_len);
+                                 P > 0 ? num_seqs : max_query_len, dtype, head_dim);
   const WsLayout lay = workspace_layout(num_seqs, num_q_heads, head_dim,
                                         chunks + (P > 0 ? num_seqs : 0));
   if (!workspace || workspace_bytes < lay.total) return PA_ERR_WORKSPACE;
@@ -233,7 +239,7 @@ static int attention_common(void* out, const void* q, const void* kv_cache, int6
   a->num_kv_heads = num_kv_heads;
   a->num_q_heads = num_q_heads;
   a->num_chunks = chunks;
-  a->head_groups = group / heads_per_wave(group);
+  a->head_groups = group / pa::decode_heads_per_wave(dtype, head_dim, group);
   a->scale_log2 = scale * 1.4426950408889634f;
   char* ws = static_cast<char*>(workspace);
   a->ws_meta = reinterpret_cast<int32_t*>(ws + lay.meta);
@@ -448,7 +454,8 @@ size_t pa_attention_decode_shared_prefix_workspace_size(int32_t num_seqs, int32_
   if (shared_prefix_blocks == 0) return plain;
   const int group = num_q_heads / num_kv_heads;
   const int rest = max(max_seq_len - shared_prefix_blocks * pa::kBlockSize, 1);
-  const int chunks = plan_chunks(num_seqs, num_kv_heads, group, rest, num_splits, true, num_seqs);
+  const int chunks = plan_chunks(num_seqs, num_kv_heads, group, rest, num_splits, true, num_seqs,
+                                 PA_BF16, head_dim);
   const size_t casc = workspace_layout(num_seqs, num_q_heads, head_dim, chunks + num_seqs).total;
   return casc > plain ? casc : plain;
 }

@@ -26,11 +26,13 @@ hipError_t launch_merge_typed(const DecodeArgs& a, hipStream_t stream) {
 template <typename E, int D>
 hipError_t launch_hpw(const DecodeArgs& a, int group, bool split, hipStream_t stream) {
   if (!split) return launch_merge_typed<E, D>(a, stream);
-  switch (group) {
+  if (group != 1 && group != 2 && group != 4 && group != 8) return hipErrorInvalidValue;
+  switch (decode_heads_per_wave(E::kind, D, group)) {
     case 1: return launch_split_typed<E, D, 1>(a, stream);
     case 2: return launch_split_typed<E, D, 2>(a, stream);
     case 4:
-    case 8: return launch_split_typed<E, D, 4>(a, stream);
+      if constexpr (E::kind == F32::kind && D == 128) return hipErrorInvalidValue;  // never chosen
+      else return launch_split_typed<E, D, 4>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -8,6 +8,7 @@
 namespace pa {
 
 constexpr int kBlockSize = 16;  // tokens per paged block
+constexpr int F32_KIND = 0;     // pa_dtype value of fp32
 
 // The step's new tokens when the attention launch also stores them into the
 // cache (k == null: the caller scattered them beforehand).  Token t of the
@@ -110,6 +111,14 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* kv
 
 hipError_t launch_copy_blocks(void* kv_cache, const int32_t* pairs, int32_t num_pairs,
                               int64_t block_bytes, hipStream_t stream);
+
+// Query heads one decode wave serves (the rest of a GQA group goes to more
+// waves): up to 4, and 2 for fp32 rows of 128 dims, whose four heads of
+// queries, accumulators and two in-flight blocks do not fit 256 VGPRs.
+inline int decode_heads_per_wave(int dtype, int head_dim, int group) {
+  const int h = group < 4 ? group : 4;
+  return (dtype == F32_KIND && head_dim == 128 && h > 2) ? 2 : h;
+}
 
 // dtype: pa_dtype value; head_dim 64 | 128; group = Hq / Hkv in {1,2,4,8}.
 // launch_decode = launch_decode_split then launch_decode_merge.
