@@ -548,6 +548,9 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   const int lane = lane_id();
   const int r = blockIdx.x / a.num_q_heads;
   const int hq = blockIdx.x - r * a.num_q_heads;
+  // the request's cut record is loaded beside its length (one round trip);
+  // it is used only where the split wrote it
+  const int4 meta = *reinterpret_cast<const int4*>(a.ws_meta + 4 * (int64_t)r);
   bool active = a.seq_lens[r] > 0;
   int row = r;
   if (a.qsl) {
@@ -562,7 +565,6 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   const bool ranges = !prefix || (a.seq_lens[r] + kBlockSize - 1) / kBlockSize > a.skip_blocks;
   int cf = 0, cl = -1, W = 1;
   if (ranges) {
-    const int4 meta = *reinterpret_cast<const int4*>(a.ws_meta + 4 * (int64_t)r);
     if (meta.x < 0) return;  // finished in place by its range
     cf = uniform(meta.x);
     cl = uniform(meta.y);

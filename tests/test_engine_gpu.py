@@ -16,7 +16,8 @@ pytestmark = pytest.mark.gpu
 pa = pytest.importorskip("paged_kv_attention_07_amd")
 
 
-@pytest.mark.parametrize("dtype,Hq,Hkv,D", [("bf16", 8, 2, 128), ("f16", 4, 4, 64)])
+@pytest.mark.parametrize("dtype,Hq,Hkv,D", [("bf16", 8, 2, 128), ("f16", 4, 4, 64),
+                                            ("f32", 16, 2, 128)])
 def test_engine_matches_oracle_every_step(dtype, Hq, Hkv, D):
     import torch
     from paged_kv_attention_07_amd.engine import Engine
@@ -26,8 +27,11 @@ def test_engine_matches_oracle_every_step(dtype, Hq, Hkv, D):
                  max_num_seqs=t.max_num_seqs, max_model_len=t.max_model_len, num_q_heads=Hq,
                  num_kv_heads=Hkv, head_dim=D, dtype=dtype)
     o = S.Scheduler(t.num_blocks, B, t.max_num_batched_tokens, t.max_num_seqs, t.max_model_len)
-    nan = np.uint16(0x7FC0) if dtype == "bf16" else np.uint16(0x7E00)
-    pool = np.full((t.num_blocks, 2, B, Hkv, D), nan, np.uint16)
+    if dtype == "f32":
+        pool = np.full((t.num_blocks, 2, B, Hkv, D), np.nan, np.float32)
+    else:
+        nan = np.uint16(0x7FC0) if dtype == "bf16" else np.uint16(0x7E00)
+        pool = np.full((t.num_blocks, 2, B, Hkv, D), nan, np.uint16)
     width = -(-t.max_model_len // B)
     seen = {"copies": 0, "preempted": 0, "prefill_rows": 0, "steps": 0}
     for step in range(t.num_steps):
@@ -72,4 +76,4 @@ def test_engine_matches_oracle_every_step(dtype, Hq, Hkv, D):
     # the GPU cache holds exactly the oracle's bits wherever the oracle wrote
     g_pool = gu.from_device(eng.kv, dtype)
     written = ~np.isnan(oracle.decode_bits(pool, dtype))
-    assert np.array_equal(g_pool[written], pool[written])
+    assert np.array_equal(gu.bits(g_pool[written]), gu.bits(pool[written]))
