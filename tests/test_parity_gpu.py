@@ -280,6 +280,26 @@ def test_full_long_context_sampled():
     full_check(w, requests=[0, 7, 15])
 
 
+CONFIGS = ["tiny_f32_decode", "decode_bf16_64req", "mixed_chunked_prefill_bf16",
+           "prefix_shared_decode_bf16", "long_context_decode_bf16"]
+
+
+@pytest.mark.parametrize("i", range(1, 6))
+@pytest.mark.parametrize("seed_base", [2000, 3000])
+def test_configs_at_more_seeds(seed_base, i):
+    """Configuration i of the five (tiny fp32, 64-request decode, mixed step,
+    prefix-shared, long-context) at seeds 2000 + i and 3000 + i: new lengths,
+    tables and values of the same shapes and distributions."""
+    name = CONFIGS[i - 1]
+    w = workload(name, seed_base + i)
+    if name == "prefix_shared_decode_bf16":
+        full_check(w, requests=list(range(3, w.num_seqs, 16)))
+    elif name == "long_context_decode_bf16":
+        full_check(w, requests=[2, 11])
+    else:
+        full_check(w)
+
+
 def test_workspace_reused_across_calls():
     """One workspace serves many calls with different batches and split
     counts: nothing a call leaves in it affects the next call."""
