@@ -239,6 +239,27 @@ class Stepper:
         if ev is not None:
             ev[1].record()
 
+    def run_flushed(self, launches: int, flush_bytes: int = 512 << 20):
+        """Cold-cache launches: before each step a `flush_bytes` write and then
+        a read of another `flush_bytes` buffer evict L2 and the 256 MB
+        Infinity Cache (the read pass also takes the write-backs of the
+        write, which would otherwise land inside the timed launch); HIP
+        events bracket the attention call alone.  Returns the per-launch
+        durations (ms)."""
+        torch = self.torch
+        scratch = torch.empty(flush_bytes, dtype=torch.uint8, device="cuda")
+        other = torch.ones(flush_bytes // 4, dtype=torch.float32, device="cuda")
+        ms = []
+        for i in range(launches):
+            scratch.fill_(i & 0xFF)
+            other.sum()
+            ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            self.step(i, ev)
+            torch.cuda.synchronize()
+            ms.append(ev[0].elapsed_time(ev[1]))
+        del scratch, other
+        return ms
+
     def run(self, steps: int, warmup: int, event_every: int = 1):
         """Time `steps` steps; the attention call of every `event_every`-th
         step is bracketed by HIP events on the launch stream (an event record
@@ -382,7 +403,7 @@ def cpu_baseline(w, budget_s: float = 12.0):
 # --------------------------------------------------------------------------
 
 
-def measure(name, args, rotations, shared_prefix=False):
+def measure(name, args, rotations, shared_prefix=False, flushed: int = 0):
     from workloads import make_workload
     t0 = time.perf_counter()
     w = make_workload(name)
@@ -403,6 +424,10 @@ def measure(name, args, rotations, shared_prefix=False):
                attn_ms_p90=float(np.percentile(attn_ms, 90)))
     print(f"[bench] {name}: {ms_step * 1e3:.1f} us/step, attention {attn_avg * 1e3:.1f} us",
           file=sys.stderr, flush=True)
+    if flushed:
+        res["flushed_ms"] = st.run_flushed(flushed)
+        print(f"[bench] {name}: flushed launches median "
+              f"{np.median(res['flushed_ms']) * 1e3:.1f} us", file=sys.stderr, flush=True)
     del st
     import torch
     torch.cuda.empty_cache()
@@ -530,6 +555,9 @@ def main():
     ap.add_argument("--extra", action="store_true", help="also time the prefix-shared and "
                     "long-context decode batches")
     ap.add_argument("--only", choices=sorted(WORKLOADS) + ["copy", "serve"], default=None)
+    ap.add_argument("--flushed", type=int, default=60,
+                    help="cold-cache launches of the headline leg, each after a 512 MiB "
+                         "flush (0: skip)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after timing, copy 1 GiB device-to-device 3 times (a kernel of "
                          "known traffic, to calibrate the profiler's FETCH_SIZE/WRITE_SIZE)")
@@ -556,7 +584,8 @@ def main():
     # the prefix-shared batch runs the shared-prefix decode ("prefix") and the
     # plain decode ("prefixplain") on the same inputs
     results = {k: measure(WORKLOADS[k], args, rot if k != "long" else 2,
-                          shared_prefix=(k == "prefix")) for k in names}
+                          shared_prefix=(k == "prefix"),
+                          flushed=args.flushed if k == names[0] else 0) for k in names}
 
     # the headline is the decode batch; with --only <leg> it is that leg, with
     # the roofline of the kernel that dominates it
@@ -598,6 +627,19 @@ def main():
                     if head_key == "decode" else None,
                     "traffic_kernel": "decode_split_kernel (profiles/traffic.json)",
                     "kernel": kernel, "alg_bytes_per_launch": int(alg), **launch}
+    if head.get("flushed_ms"):
+        fm = np.asarray(head["flushed_ms"])
+        alg_bytes = roofline.get("alg_bytes_per_launch")
+        roofline["flushed"] = {
+            "method": "before each launch a 512 MiB write, then a 512 MiB read of another "
+                      "buffer, evict L2 and the Infinity Cache; HIP events around the "
+                      "attention call alone",
+            "launches": int(fm.size),
+            "median_us": round(float(np.median(fm)) * 1e3, 2),
+            "p10_us": round(float(np.percentile(fm, 10)) * 1e3, 2),
+            "p90_us": round(float(np.percentile(fm, 90)) * 1e3, 2),
+            "achieved_at_median": (round(alg_bytes / (float(np.median(fm)) * 1e-3) / 1e9, 1)
+                                   if alg_bytes else None)}
     line = {
         "metric": METRIC,
         "value": round(value, 1),
