@@ -39,6 +39,7 @@ namespace pa {
 namespace {
 
 constexpr int kTileTokens = 16;  // query tokens per work-group
+constexpr int kXcds = 8;         // accelerator dies of the chip, each with its own L2
 
 // Request and tile (index within the request) owned by work-group `bx`:
 // requests with more than one query token contribute ceil(qlen / 16) tiles
@@ -83,10 +84,18 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(PrefillArgs a) {
   __shared__ int s_tile[2];
 
   const int tid = threadIdx.x;
-  const int h = blockIdx.y;
+  // XCD-aware numbering: work-groups go to the 8 XCDs in turn; renumber them
+  // (a bijection of the grid) so each XCD runs a contiguous block of (head,
+  // tile) pairs and the keys a head's tiles all re-read stay in one L2
+  const int tiles = gridDim.x;
+  const int total = tiles * gridDim.y;
+  const int lin = blockIdx.y * tiles + blockIdx.x;
+  const int xcd = lin % kXcds, local = lin / kXcds;
+  const int idx = xcd * (total / kXcds) + min(xcd, total % kXcds) + local;
+  const int h = idx / tiles;
   if (tid < kWave) {
     int r, t;
-    find_tile(a, blockIdx.x, &r, &t);
+    find_tile(a, idx % tiles, &r, &t);
     if (tid == 0) {
       s_tile[0] = r;
       s_tile[1] = t;
