@@ -30,7 +30,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   } else {
     __builtin_amdgcn_s_setprio(3);
     const int t = b - decode_wgs;
-    prefill_tile_body<E, D, WPW, 2, 1>(pa, t / tile_heads, t % tile_heads);
+    prefill_tile_body<E, D, WPW, 2, 1, true>(pa, t / tile_heads, t % tile_heads);
   }
 }
 

@@ -95,18 +95,25 @@ constexpr int tile_tokens() {
 }
 
 // One work-group of tiles: tile slot bx (over requests' tiles), head group by.
-template <typename E, int D, int WPW, int NT, int KSPLIT>
+// BESIDE_DECODE: the work-group shares the launch with decode work-groups
+// (the fused mixed-step launch).
+template <typename E, int D, int WPW, int NT, int KSPLIT, bool BESIDE_DECODE = false>
 __device__ __forceinline__ void prefill_tile_body(const PrefillArgs& a, int bx, int by) {
   using S = TileShape<D>;
   constexpr int QT = tile_tokens<WPW, NT>();   // tokens per tile
-  // [part][stage]: each part's next 64 keys are copied in while the current
-  // ones are used.  Two stages keep a 4-wave work-group at 64 KiB of LDS, so
-  // two work-groups share a CU and their barriers do not couple (a third
-  // stage, or 8-wave groups sharing the stages, left one group per CU and
-  // measured slower).
-  constexpr int NSTAGE = 2;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[KSPLIT][NSTAGE][S::STAGE];
-  __shared__ int s_tile[2];
+  // Two stages per part: each part's next 64 keys are copied in while the
+  // current ones are used.  Two stages keep a 4-wave work-group at 64 KiB of
+  // LDS, so two work-groups share a CU and their barriers do not couple (a
+  // third stage, or 8-wave groups sharing the stages, left one group per CU
+  // and measured slower).  The stages are two separate LDS arrays, and every
+  // trip names the one it reads and the one it fills at compile time (the
+  // trip loop is unrolled by two): the compiler then knows a trip's reads
+  // cannot touch the bytes its copies are filling and does not wait for
+  // those copies before the reads (with one array indexed at run time it
+  // waited, and every trip paid the full copy latency).
+  __shared__ __attribute__((aligned(16))) uint8_t lds0[KSPLIT][S::STAGE];  // even trips
+  __shared__ __attribute__((aligned(16))) uint8_t lds1[KSPLIT][S::STAGE];  // odd trips
+  __shared__ int s_tile[3];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -120,27 +127,35 @@ __device__ __forceinline__ void prefill_tile_body(const PrefillArgs& a, int bx, 
 
   // ---- which request / tile this work-group owns (a shared-prefix pass has
   // one virtual request: tile = work-group index)
+  // Beside decode rows the work-group also notes whether the batch has any
+  // (a request with one query token): then its copies are waited for before
+  // each trip's reads rather than overlapped with them, leaving the memory
+  // system to the decode reads that bound such a launch (overlapping them
+  // made the mixed step ~1% slower; a batch of chunks alone gains 10%).
   const bool cascade = a.cascade_rows > 0;
   if (cascade) {
     if (lane == 0 && wave == 0) {
       const bool live = bx * QT < a.cascade_rows;
       s_tile[0] = live ? 0 : -1;
       s_tile[1] = bx;
+      s_tile[2] = 1;                           // the shared-prefix pass runs beside decode
     }
   } else if (wave == 0) {
     int found_r = -1, found_t = 0, running = 0;
+    bool decode_rows = false;
     const int want = bx;
-    for (int base = 0; base < a.num_seqs && found_r < 0; base += kWave) {
+    for (int base = 0; base < a.num_seqs && (BESIDE_DECODE || found_r < 0); base += kWave) {
       const int r = base + lane;
-      int nt = 0;
+      int nt = 0, ql = 0;
       if (r < a.num_seqs) {
-        const int ql = a.qsl[r + 1] - a.qsl[r];
+        ql = a.qsl[r + 1] - a.qsl[r];
         nt = ql > 1 ? (ql + QT - 1) / QT : 0;
       }
+      decode_rows = decode_rows || __ballot(ql == 1) != 0;
       const int incl = wave_incl_scan(nt) + running;
       const int excl = incl - nt;
       const uint64_t hit = __ballot(nt > 0 && want >= excl && want < incl);
-      if (hit) {
+      if (hit && found_r < 0) {
         const int src = __builtin_ctzll(hit);
         found_r = base + src;
         // a request's tiles are handed out last-first: the tiles with the
@@ -152,12 +167,14 @@ __device__ __forceinline__ void prefill_tile_body(const PrefillArgs& a, int bx, 
     if (lane == 0) {
       s_tile[0] = found_r;
       s_tile[1] = found_t;
+      s_tile[2] = BESIDE_DECODE && decode_rows;
     }
   }
   __syncthreads();
   const int r = uniform(s_tile[0]);
   if (r < 0) return;
   const int tile = uniform(s_tile[1]);
+  const bool wait_copies = uniform(s_tile[2]) != 0;
 
   // a shared-prefix pass: rows 0 .. cascade_rows - 1 all placed after the
   // cascade_keys prefix keys, so every prefix key is visible to every row
@@ -206,11 +223,15 @@ __device__ __forceinline__ void prefill_tile_body(const PrefillArgs& a, int bx, 
   const uint8_t* kvh = static_cast<const uint8_t*>(a.kv) + (int64_t)h * S::ROWB;
   const int32_t* bt = a.block_table + (int64_t)r * a.bt_stride;
 
-  // id of the paged block this wavefront stages in (global) iteration it
+  // Ids of the paged blocks this wavefront stages: one vector load per 64 of
+  // its trips (lane l holds the id for trip t0 + l, i.e. iteration
+  // it_begin + t0 + l), picked per trip with a lane read.  A scalar load per
+  // trip would put its latency before every barrier: scalar loads share the
+  // counter that the barrier's LDS wait drains.
   const int nb_need = (kend + kBlockSize - 1) / kBlockSize;
-  auto block_id = [&](int it) {
-    const int lb = it * 4 + w4;
-    return lb < nb_need ? load_scalar(bt + lb) : 0;
+  auto load_ids = [&](int t0) {
+    const int lb = (it_begin + t0 + lane) * 4 + w4;
+    return (t0 + lane < my_iters && lb < nb_need) ? bt[lb] : 0;
   };
 
   // Staging: wavefront w4 of a part copies paged block w4 of the part's
@@ -246,7 +267,7 @@ __device__ __forceinline__ void prefill_tile_body(const PrefillArgs& a, int bx, 
   // the wave's 16 rows of an iteration start at key0: all cached, all new,
   // or (at most twice per tile) mixed / past the tile's last key, which is
   // the only case that selects a source per lane
-  auto dma = [&](int it, int phys, int buf) {
+  auto dma = [&](int it, int phys, uint8_t* stage) {
     const uint8_t* blk = kvh + (int64_t)phys * blk_stride;
     const int key0 = it * kKeysPerIter + 16 * w4;
     const uint8_t* fblk[2] = {fbase[0] + (int64_t)(key0 - nc) * tok_stride,
@@ -269,7 +290,7 @@ __device__ __forceinline__ void prefill_tile_body(const PrefillArgs& a, int bx, 
                 : key >= nfresh ? fblk[hv] + goff[hv][i]
                                 : blk + goff[hv][i];
         }
-        uint8_t* dst = &lds[part][buf][hv * S::KBUF + (16 * w4 + S::RPI * i) * S::ROWB];
+        uint8_t* dst = stage + hv * S::KBUF + (16 * w4 + S::RPI * i) * S::ROWB;
         __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
       }
     }
@@ -285,10 +306,10 @@ __device__ __forceinline__ void prefill_tile_body(const PrefillArgs& a, int bx, 
     for (int mt = 0; mt < S::NMT; ++mt) acc[j][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  // One 64-key iteration from LDS stage `buf`: S^T, online softmax, O^T.
-  auto compute = [&](int it, int buf) {
-    const uint8_t* lds_kc = lds[part][buf];
-    const uint8_t* lds_vc = lds[part][buf] + S::KBUF;
+  // One 64-key iteration from LDS stage `stage`: S^T, online softmax, O^T.
+  auto compute = [&](int it, const uint8_t* stage) {
+    const uint8_t* lds_kc = stage;
+    const uint8_t* lds_vc = stage + S::KBUF;
     // ---- S^T for 64 keys x 16 tokens per sub-tile: 4 tiles of 16 keys
     f32x4_t st[NT][4];
 #pragma unroll
@@ -389,17 +410,27 @@ __device__ __forceinline__ void prefill_tile_body(const PrefillArgs& a, int bx, 
   // other waves at the barrier (after which every copy of that iteration has
   // landed and every wave is done with the other stage), starts the copies
   // of the next iteration into the other stage, and computes.
-  if (my_iters > 0) dma(it_begin, block_id(it_begin), 0);
+  int ids = load_ids(0);                       // trips 0 .. 63
+  int ids_ahead = my_iters > 64 ? load_ids(64) : 0;  // trips 64 .. 127
+  uint8_t* const st0 = lds0[part];
+  uint8_t* const st1 = lds1[part];
+  if (my_iters > 0) dma(it_begin, readlane(ids, 0), st0);
 
-  int id_next = block_id(it_begin + 1);
-  for (int t = 0; t < n0; ++t) {
-    const int buf = t & 1;
-    const int phys = id_next;
-    id_next = block_id(it_begin + t + 2);
+  auto trip = [&](int t, const uint8_t* cur, uint8_t* nxt) __attribute__((always_inline)) {
+    const int tn = t + 1;                      // trip whose copies start now
+    const bool wrap = (tn & 63) == 0 && tn < my_iters;
+    if (wrap) ids = ids_ahead;                 // next window of ids
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (t + 1 < my_iters) dma(it_begin + t + 1, phys, buf ^ 1);
-    if (t < my_iters) compute(it_begin + t, buf);
+    if (tn < my_iters) dma(it_begin + tn, readlane(ids, tn & 63), nxt);
+    // the window after it, loaded beside this trip's copies
+    if (wrap) ids_ahead = tn + 64 < my_iters ? load_ids(tn + 64) : 0;
+    if (wait_copies) __builtin_amdgcn_s_waitcnt(0);
+    if (t < my_iters) compute(it_begin + t, cur);
+  };
+  for (int t = 0; t < n0; t += 2) {
+    trip(t, st0, st1);
+    if (t + 1 < n0) trip(t + 1, st1, st0);
   }
   // ---- store the tile's new tokens into the cache: one work-group per KV
   // head (the first query-head group) writes the K and V rows of tokens
@@ -451,26 +482,28 @@ __device__ __forceinline__ void prefill_tile_body(const PrefillArgs& a, int bx, 
   }
   if constexpr (KSPLIT == 2) {
     // ---- merge the parts: part 1 leaves (max, row sum, O^T) in its LDS stages
-    constexpr int NF = NT * (S::NMT * 4 + 2);  // floats per lane
-    static_assert(4 * kWave * NF * 4 <= NSTAGE * S::STAGE, "merge buffer must fit in part 1's stages");
-    float* xch = reinterpret_cast<float*>(&lds[1][0][0]) + (w4 * kWave + lane) * NF;
+    // the accumulators go to part 1's first stage, (max, sum) to its second
+    constexpr int NA = NT * S::NMT * 4;        // accumulator floats per lane
+    static_assert(4 * kWave * NA * 4 <= S::STAGE, "merge buffer must fit in part 1's stage");
+    float* xa = reinterpret_cast<float*>(lds0[1]) + (w4 * kWave + lane) * NA;
+    float* xm = reinterpret_cast<float*>(lds1[1]) + (w4 * kWave + lane) * 2 * NT;
     if (part == 1) {
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
 #pragma unroll
         for (int mt = 0; mt < S::NMT; ++mt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) xch[j * (S::NMT * 4 + 2) + 4 * mt + i] = acc[j][mt][i];
-        xch[j * (S::NMT * 4 + 2) + S::NMT * 4] = m[j];
-        xch[j * (S::NMT * 4 + 2) + S::NMT * 4 + 1] = lsum[j];
+          for (int i = 0; i < 4; ++i) xa[j * S::NMT * 4 + 4 * mt + i] = acc[j][mt][i];
+        xm[2 * j] = m[j];
+        xm[2 * j + 1] = lsum[j];
       }
     }
     __syncthreads();
     if (part == 1) return;
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-      const float* src = xch + j * (S::NMT * 4 + 2);
-      const float m1 = src[S::NMT * 4], l1 = src[S::NMT * 4 + 1];
+      const float* src = xa + j * S::NMT * 4;
+      const float m1 = xm[2 * j], l1 = xm[2 * j + 1];
       const float M = fmaxf(m[j], m1);         // m is finite: key 0 is visible
       const float a0 = __builtin_amdgcn_exp2f(m[j] - M);
       const float a1 = (m1 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m1 - M);
