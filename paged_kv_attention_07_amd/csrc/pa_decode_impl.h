@@ -401,15 +401,22 @@ __device__ __forceinline__ void process_range(const DecodeArgs& a, int r, int ro
                            p + half_stride + (s0 ? dv : 0), p + half_stride + tok8 + (s1 ? dv : 0));
     }
   };
-  int id_next = (j0 + 1 < j1) ? load_scalar(bt + j0 + 1) : 0;
+  // Every issue loads a block, also past the range (then block j1 - 1 again,
+  // which this wave has just read and L2 still holds): with the same loads in
+  // flight on every path the compiler keeps the next block's loads
+  // outstanding while the current one is processed.  Issued only when a next
+  // block exists, its wait counts were merged with the path that issued
+  // nothing, and each block ended up waiting for the next block's loads.
+  int id_next = load_scalar(bt + min(j0 + 1, j1 - 1));  // id of block min(j + 1, j1 - 1)
   load_at(b0, j0, load_scalar(bt + j0));
   int j = j0;
   auto issue = [&](BlockRegs<E, D, HPW>& b) {
-    // load block j + 1 into b, then fetch the id of block j + 2
-    if (j + 1 < j1) {
-      load_at(b, j + 1, id_next);
-      id_next = (j + 2 < j1) ? load_scalar(bt + j + 2) : 0;
-    }
+    // fetch the id after block j + 1, then load block j + 1 (clamped) into
+    // b: loads complete in order, so waiting for that id at the next issue
+    // leaves this block's loads in flight
+    const int id = id_next;
+    id_next = load_scalar(bt + min(j + 2, j1 - 1));
+    load_at(b, min(j + 1, j1 - 1), id);
   };
   while (true) {
     issue(b1);
