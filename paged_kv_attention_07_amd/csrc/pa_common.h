@@ -120,6 +120,16 @@ __device__ __forceinline__ T load_scalar(const T* p) {
   return *(const __attribute__((address_space(4))) T*)p;
 }
 
+// A pointer the whole wavefront agrees on, in scalar registers (so loads
+// through it can be scalar loads).
+template <typename T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<T*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
 // Uniform value of `x` in lane `l` (l uniform).
 __device__ __forceinline__ int readlane(int x, int l) { return __builtin_amdgcn_readlane(x, l); }
 

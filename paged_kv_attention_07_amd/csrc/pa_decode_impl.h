@@ -323,6 +323,13 @@ __device__ __forceinline__ void process_range(const DecodeArgs& a, int r, int ro
   const int tg = lane >> 3;
   const int ds = lane & 7;
 
+  // ids of the range's first two blocks, fetched before the queries (scalar
+  // loads, beside the vector loads of the queries)
+  const int sk = a.skip_blocks;
+  const int32_t* bt = uniform_ptr(a.block_table + (int64_t)r * a.bt_stride + sk);
+  const int id_first = load_scalar(bt + uniform(j0));
+  const int id_first_next = load_scalar(bt + uniform(min(j0 + 1, j1 - 1)));
+
   // this lane's slice of the HPW query vectors
   u32x4_t qv[HPW][S::NCH];
   {
@@ -342,8 +349,6 @@ __device__ __forceinline__ void process_range(const DecodeArgs& a, int r, int ro
                        tg * tok_stride + ds * 16;
   // j runs over the blocks after a shared prefix of sk blocks; attend_block
   // takes full-table indices (for the partial last block)
-  const int sk = a.skip_blocks;
-  const int32_t* bt = a.block_table + (int64_t)r * a.bt_stride + sk;
   const int nb = (L + kBlockSize - 1) / kBlockSize;
 
   float m[HPW], l[HPW], acc[HPW][S::DPL];
@@ -407,15 +412,14 @@ __device__ __forceinline__ void process_range(const DecodeArgs& a, int r, int ro
   // outstanding while the current one is processed.  Issued only when a next
   // block exists, its wait counts were merged with the path that issued
   // nothing, and each block ended up waiting for the next block's loads.
-  int id_next = load_scalar(bt + min(j0 + 1, j1 - 1));  // id of block min(j + 1, j1 - 1)
-  load_at(b0, j0, load_scalar(bt + j0));
+  int id_next = id_first_next;                 // id of block min(j + 1, j1 - 1)
+  load_at(b0, j0, id_first);
   int j = j0;
   auto issue = [&](BlockRegs<E, D, HPW>& b) {
-    // fetch the id after block j + 1, then load block j + 1 (clamped) into
-    // b: loads complete in order, so waiting for that id at the next issue
-    // leaves this block's loads in flight
+    // fetch the id after block j + 1 (a scalar load: the index is marked
+    // wave-uniform), then load block j + 1 (clamped) into b
     const int id = id_next;
-    id_next = load_scalar(bt + min(j + 2, j1 - 1));
+    id_next = load_scalar(bt + uniform(min(j + 2, j1 - 1)));
     load_at(b, min(j + 1, j1 - 1), id);
   };
   while (true) {
