@@ -383,9 +383,8 @@ __device__ __forceinline__ void process_range(const DecodeArgs& a, int r, int ro
   }
 
   // two register buffers: block j+1 is in flight while block j is processed
-  // (2048 waves keep ~16 MB of loads in flight, above the bandwidth-latency
-  // product; a third buffer measured no faster and costs 32 VGPRs); block
-  // ids are read one step before their loads are issued
+  // (a third buffer, two blocks in flight, measured no faster and costs 32
+  // VGPRs); block ids are read one step before their loads are issued
   BlockRegs<E, D, HPW> b0, b1;
   auto load_at = [&](BlockRegs<E, D, HPW>& b, int jj, int id) {
     const uint8_t* p = kvh + (int64_t)id * blk_stride;
