@@ -193,13 +193,15 @@ size_t pa_attention_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t
   if (check_heads(num_q_heads, num_kv_heads) != PA_OK) return 0;
   const int group = num_q_heads / num_kv_heads;
   // size for the larger of the plans with and without concurrent tiles, so
-  // the buffer serves either call
+  // the buffer serves either call; beside tiles, for the shortest chunk (2
+  // tokens), which leaves the decode rows the most waves: a call may pass any
+  // max_query_len up to the one given here
   const int alone =
       plan_chunks(num_seqs, num_kv_heads, group, max_seq_len, num_splits, false, 0, PA_BF16,
                   head_dim);
   const int beside =
       max_query_len > 1 ? plan_chunks(num_seqs, num_kv_heads, group, max_seq_len, num_splits,
-                                      true, max_query_len, PA_BF16, head_dim)
+                                      true, 2, PA_BF16, head_dim)
                         : 0;
   const int chunks = alone > beside ? alone : beside;
   return workspace_layout(num_seqs, num_q_heads, head_dim, chunks).total;

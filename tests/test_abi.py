@@ -298,3 +298,20 @@ def test_check_metadata_host_checks():
     assert check_meta(P=8) == INVALID                    # prefix wider than the table
     assert check_meta(R=0) == INVALID                    # tokens without requests
     assert check_meta(R=0, T=0) == OK                    # nothing to check
+
+
+def test_workspace_size_covers_every_shorter_call():
+    """A buffer sized for (R, T, max_seq_len, max_query_len) serves any call
+    within those bounds: the size never shrinks as a bound grows (a call
+    with a shorter chunk leaves its decode rows more waves, so more ranges)."""
+    ws = lib.pa_attention_workspace_size
+    for hq, hkv, d in ((32, 8, 128), (8, 2, 64), (4, 4, 128), (64, 8, 128)):
+        for R in (1, 2, 7, 64, 256, 1024):
+            for L in (1, 17, 600, 4096, 32768):
+                sizes = [ws(R, 4096, hq, hkv, d, L, q, 0) for q in (1, 2, 3, 17, 100, 512, 2048, 8192)]
+                assert all(s > 0 for s in sizes)
+                assert sizes == sorted(sizes), (hq, hkv, d, R, L, sizes)
+                # and it covers the plans of smaller batches and shorter contexts
+                for R2 in (1, max(1, R // 2), R):
+                    for L2 in (1, max(1, L // 3), L):
+                        assert ws(R2, 4096, hq, hkv, d, L2, 2, 0) <= ws(R, 4096, hq, hkv, d, L, 2, 0)

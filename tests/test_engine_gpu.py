@@ -77,3 +77,44 @@ def test_engine_matches_oracle_every_step(dtype, Hq, Hkv, D):
     g_pool = gu.from_device(eng.kv, dtype)
     written = ~np.isnan(oracle.decode_bits(pool, dtype))
     assert np.array_equal(gu.bits(g_pool[written]), gu.bits(pool[written]))
+
+
+def test_engine_runs_the_serving_trace():
+    """The serving trace (256 requests, prompts of 64-1536 tokens, shared system
+    prompts, chunked prefill under a 2048-token budget) through the native
+    engine: every step's attention call succeeds with the engine's one
+    workspace, sized once for the largest plan any step can need (steps mix
+    short and long chunks with decode rows), and the schedule matches the
+    oracle scheduler's step for step."""
+    import torch
+    from paged_kv_attention_07_amd.engine import Engine
+    t = trace("serve_llama3_2k")
+    Hq, Hkv, D = 32, 8, 128
+    q, k, v = step_inputs(t.seed, 0, t.max_num_batched_tokens, Hq, Hkv, D, "bf16")
+    qd, kd, vd = (gu.to_device(x, "bf16") for x in (q, k, v))
+    eng = Engine(num_blocks=t.num_blocks, max_num_batched_tokens=t.max_num_batched_tokens,
+                 max_num_seqs=t.max_num_seqs, max_model_len=t.max_model_len, num_q_heads=Hq,
+                 num_kv_heads=Hkv, head_dim=D, dtype="bf16")
+    o = S.Scheduler(t.num_blocks, t.block_size, t.max_num_batched_tokens, t.max_num_seqs,
+                    t.max_model_len)
+    tokens = chunk_steps = 0
+    for step in range(t.num_steps):
+        for rid, prompt, n in t.arrivals.get(step, []):
+            eng.add_request(rid, prompt, n)
+            o.add_request(rid, prompt, n)
+        for parent, child, n in t.forks.get(step, []):
+            assert eng.fork(parent, child, n) == o.fork(parent, child, n)
+        ro = o.schedule()
+        st = eng.step(qd, kd, vd)                      # raises on any non-zero status
+        assert st.request_ids.tolist() == ro.request_ids, step
+        assert st.num_new.tolist() == ro.num_new, step
+        tokens += st.num_tokens
+        chunk_steps += int(any(n > 1 for n in ro.num_new) and any(n == 1 for n in ro.num_new))
+        sampled = [t.sampled(r, o.requests[r].num_generated) for r in ro.request_ids]
+        assert eng.update(sampled) == o.update(sampled)
+    torch.cuda.synchronize()
+    assert torch.isfinite(eng.out.float()).all()
+    assert all(r.status == S.FINISHED for r in o.requests.values())
+    assert tokens > 100000 and chunk_steps > 10
+    print(f"[engine] serving trace: {tokens} tokens, {chunk_steps} steps mixing chunks and "
+          f"decode rows", flush=True)
