@@ -52,14 +52,19 @@ bool tiles_beside_decode(int num_seqs, int max_query_len, int dtype) {
 
 // Decode waves beside the tiles of a chunk of up to max_query_len tokens
 // (tile shape of the fused launch: 4 waves per tile, 32 * 4 / group-per-wave
-// tokens per tile).
-int64_t waves_beside_prefill(int num_kv_heads, int group, int max_query_len) {
+// tokens per tile).  With exact_tiles (the shared-prefix pass: one virtual
+// request of exactly max_query_len rows) the tiles and the decode waves fill
+// the chip's wave slots exactly, so every CU holds the same number of
+// work-groups (2048 - tile waves, at least 1024); otherwise the tile count
+// is only a lower bound and the decode waves stay within 1024-1536.
+int64_t waves_beside_prefill(int num_kv_heads, int group, int max_query_len,
+                             bool exact_tiles) {
   const int wpw = heads_per_wave(group);
   const int64_t qt = 32 * (4 / wpw);
   const int64_t tile_waves = 4 * ceil_div(max_query_len, qt) * num_kv_heads * (group / wpw);
   int64_t w = kWaveSlots - tile_waves;
   if (w < kMinWavesBesidePrefill) w = kMinWavesBesidePrefill;
-  if (w > kMaxWavesBesidePrefill) w = kMaxWavesBesidePrefill;
+  if (!exact_tiles && w > kMaxWavesBesidePrefill) w = kMaxWavesBesidePrefill;
   return w;
 }
 
@@ -68,12 +73,14 @@ int64_t waves_beside_prefill(int num_kv_heads, int group, int max_query_len) {
 // serve the most heads each, so its plan has the most ranges and bounds the
 // others.
 int plan_chunks(int num_seqs, int num_kv_heads, int group, int max_seq_len, int num_splits,
-                bool beside_prefill, int max_query_len, int dtype, int head_dim) {
+                bool beside_prefill, int max_query_len, int dtype, int head_dim,
+                bool exact_tiles = false) {
   if (num_splits > 0) return num_splits;
   const int hg = group / pa::decode_heads_per_wave(dtype, head_dim, group);
   const int64_t blocks_upper = (int64_t)num_seqs * ceil_div(max_seq_len, pa::kBlockSize);
   const int64_t waves = beside_prefill
-                            ? waves_beside_prefill(num_kv_heads, group, max_query_len)
+                            ? waves_beside_prefill(num_kv_heads, group, max_query_len,
+                                                   exact_tiles)
                             : kTargetWaves;
   int64_t n = ceil_div(waves, (int64_t)num_kv_heads * hg);
   const int64_t cap = ceil_div(blocks_upper, kMinBlocksPerRange);
@@ -233,7 +240,7 @@ static int attention_common(void* out, const void* q, const void* kv_cache, int6
                                  P > 0 ? max(max_seq_len - P * pa::kBlockSize, 1) : max_seq_len,
                                  num_splits,
                                  P > 0 || tiles_beside_decode(num_seqs, max_query_len, dtype),
-                                 P > 0 ? num_seqs : max_query_len, dtype, head_dim);
+                                 P > 0 ? num_seqs : max_query_len, dtype, head_dim, P > 0);
   const WsLayout lay = workspace_layout(num_seqs, num_q_heads, head_dim,
                                         chunks + (P > 0 ? num_seqs : 0));
   if (!workspace || workspace_bytes < lay.total) return PA_ERR_WORKSPACE;
@@ -466,7 +473,7 @@ size_t pa_attention_decode_shared_prefix_workspace_size(int32_t num_seqs, int32_
   const int group = num_q_heads / num_kv_heads;
   const int rest = max(max_seq_len - shared_prefix_blocks * pa::kBlockSize, 1);
   const int chunks = plan_chunks(num_seqs, num_kv_heads, group, rest, num_splits, true, num_seqs,
-                                 PA_BF16, head_dim);
+                                 PA_BF16, head_dim, true);
   const size_t casc = workspace_layout(num_seqs, num_q_heads, head_dim, chunks + num_seqs).total;
   return casc > plain ? casc : plain;
 }
