@@ -104,6 +104,38 @@ __device__ __forceinline__ float sum8(float x) {
 
 __device__ __forceinline__ float shfl_xor(float x, int mask) { return __shfl_xor(x, mask, kWave); }
 
+// gfx950's row-swap moves.  swap32(a, b) exchanges the upper 32 lanes of `a`
+// with the lower 32 lanes of `b`; swap16(a, b) exchanges rows 1 and 3 of `a`
+// with rows 0 and 2 of `b` (a row is 16 lanes).  Both are plain VALU moves,
+// with no LDS round trip.  Returned as {new a, new b}.
+struct F2 {
+  float a, b;
+};
+__device__ __forceinline__ F2 swap32(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+__device__ __forceinline__ F2 swap16(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+// Max / sum over lanes l, l ^ 16, l ^ 32, l ^ 48 (the same position in the
+// four rows); every lane gets the result.  swap32(x, x) leaves lane l with
+// x[l mod 32] in one register and x[l mod 32 + 32] in the other, and swap16
+// does the same for pairs of rows.  Needs the whole wavefront active.
+__device__ __forceinline__ float max_over_rows(float x) {
+  const F2 h = swap32(x, x);
+  x = fmaxf(h.a, h.b);
+  const F2 r = swap16(x, x);
+  return fmaxf(r.a, r.b);
+}
+__device__ __forceinline__ float sum_over_rows(float x) {
+  const F2 h = swap32(x, x);
+  x = h.a + h.b;
+  const F2 r = swap16(x, x);
+  return r.a + r.b;
+}
+
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
 // Mark a value the whole wavefront agrees on as uniform, so that the compiler

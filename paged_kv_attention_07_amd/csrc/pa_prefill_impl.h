@@ -274,6 +274,18 @@ __device__ __forceinline__ void prefill_tile_body(const PrefillArgs& a, int bx, 
                               fbase[1] + (int64_t)(key0 - nc) * tok_stride};
     const bool cached = key0 + 15 < min(kend, nfresh);
     const bool all_new = key0 >= nfresh && key0 + 15 < kend;
+    if (cached) {
+      // the common case, with one branch for all copies: a wave-uniform
+      // block address plus a 32-bit per-lane offset
+#pragma unroll
+      for (int hv = 0; hv < 2; ++hv)
+#pragma unroll
+        for (int i = 0; i < CPB; ++i)
+          __builtin_amdgcn_global_load_lds(blk + goff[hv][i],
+                                           stage + hv * S::KBUF + (16 * w4 + S::RPI * i) * S::ROWB,
+                                           16, 0, 0);
+      return;
+    }
 #pragma unroll
     for (int hv = 0; hv < 2; ++hv) {
 #pragma unroll
@@ -281,9 +293,7 @@ __device__ __forceinline__ void prefill_tile_body(const PrefillArgs& a, int bx, 
         const int rib = S::RPI * i + lane / S::CPR;
         const int key = key0 + rib;
         const uint8_t* src;
-        if (cached) {
-          src = blk + goff[hv][i];
-        } else if (all_new) {
+        if (all_new) {
           src = fblk[hv] + goff[hv][i];
         } else {
           src = key >= kend     ? g_zero_row + zoff[hv][i]
@@ -346,8 +356,7 @@ __device__ __forceinline__ void prefill_tile_body(const PrefillArgs& a, int bx, 
       for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) mx = fmaxf(mx, x[tt][i]);
-      mx = fmaxf(mx, shfl_xor(mx, 16));
-      mx = fmaxf(mx, shfl_xor(mx, 32));
+      mx = max_over_rows(mx);
       mx *= a.scale_log2;  // scale > 0: max of scaled = scaled max
       const float mn = fmaxf(m[j], mx);
       const bool grow = mn > m[j] + 8.f;
@@ -477,8 +486,7 @@ __device__ __forceinline__ void prefill_tile_body(const PrefillArgs& a, int bx, 
 
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
-    lsum[j] += shfl_xor(lsum[j], 16);
-    lsum[j] += shfl_xor(lsum[j], 32);
+    lsum[j] = sum_over_rows(lsum[j]);
   }
   if constexpr (KSPLIT == 2) {
     // ---- merge the parts: part 1 leaves (max, row sum, O^T) in its LDS stages
