@@ -135,6 +135,22 @@ __device__ __forceinline__ float sum_over_rows(float x) {
   const F2 r = swap16(x, x);
   return r.a + r.b;
 }
+// The value of lane l ^ 8 (rotating a 16-lane row by 8 swaps its halves).
+__device__ __forceinline__ float xor8(float x) { return dpp<kDppRowRor8>(x); }
+// Max / sum over the whole wavefront, in registers; every lane gets the same
+// bits.  Needs the whole wavefront active.
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp<kDppQuadXor1>(x));
+  x = fmaxf(x, dpp<kDppQuadXor2>(x));
+  x = fmaxf(x, dpp<kDppRowHalfMirror>(x));
+  x = fmaxf(x, xor8(x));
+  return max_over_rows(x);
+}
+__device__ __forceinline__ float wave_sum(float x) {
+  x = sum8(x);
+  x += xor8(x);
+  return sum_over_rows(x);
+}
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 

@@ -435,21 +435,24 @@ __device__ __forceinline__ void process_range(const DecodeArgs& a, int r, int ro
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh) {
     float M = m[hh];
-    M = fmaxf(M, shfl_xor(M, 8));
-    M = fmaxf(M, shfl_xor(M, 16));
-    M = fmaxf(M, shfl_xor(M, 32));
+    M = fmaxf(M, xor8(M));
+    M = max_over_rows(M);
     const float sc = (m[hh] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m[hh] - M);
     float lt = l[hh] * sc;
-    lt += shfl_xor(lt, 8);
-    lt += shfl_xor(lt, 16);
-    lt += shfl_xor(lt, 32);
+    lt += xor8(lt);
+    lt = sum_over_rows(lt);
 #pragma unroll
     for (int e = 0; e < S::DPL; ++e) acc[hh][e] *= sc;
     Mh[hh] = M;
     Lh[hh] = lt;
   }
   // reduce-scatter over the groups: lane keeps NOUT consecutive values of
-  // the flattened [HPW][DPL] accumulator, starting at `base`
+  // the flattened [HPW][DPL] accumulator, starting at `base`.  Step st pairs
+  // token group tg with tg ^ (1 << st) (lanes l and l ^ (8 << st)): the one
+  // whose bit st is 0 keeps the low half, its partner the high half, and each
+  // adds the other's copy of the half it keeps.  Steps 1 and 2 pair whole
+  // rows / half-waves, which the row-swap moves exchange in one instruction
+  // per pair of halves.
   float* v = &acc[0][0];
   int base = 0;
 #pragma unroll
@@ -459,9 +462,14 @@ __device__ __forceinline__ void process_range(const DecodeArgs& a, int r, int ro
 #pragma unroll
     for (int i = 0; i < n / 2; ++i) {
       const float lo = v[i], hi = v[i + n / 2];
-      const float send = bit ? lo : hi;
-      const float keep = bit ? hi : lo;
-      v[i] = keep + shfl_xor(send, 8 << st);
+      if (st == 0) {
+        const float send = bit ? lo : hi;
+        const float keep = bit ? hi : lo;
+        v[i] = keep + xor8(send);
+      } else {
+        const F2 r = st == 1 ? swap16(lo, hi) : swap32(lo, hi);
+        v[i] = r.a + r.b;
+      }
     }
     base += bit * (n / 2);
   }
@@ -593,8 +601,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
       mc = a.ws_ml[(base + (int64_t)c * a.num_q_heads) * 2];
     M = fmaxf(M, mc);
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, shfl_xor(M, o));
+  M = wave_max(M);
   f32x2_t pml = {-INFINITY, 0.f};
   if (prefix) {
     pml = *reinterpret_cast<const f32x2_t*>(a.ws_ml + pslot * 2);
@@ -628,8 +635,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
       float v[8][DPT], wk[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        wk[k] = __shfl(w, k0 + k < n ? k0 + k : 0, kWave);
-        wk[k] = k0 + k < n ? wk[k] : 0.f;
+        wk[k] = k0 + k < n ? __int_as_float(readlane(__float_as_int(w), k0 + k)) : 0.f;
 #pragma unroll
         for (int i = 0; i < DPT; ++i) v[k][i] = 0.f;
         if (wk[k] != 0.f) {
@@ -645,8 +651,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
         for (int i = 0; i < DPT; ++i) acc[i] = fmaf(wk[k], v[k][i], acc[i]);
     }
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) lsum += shfl_xor(lsum, o);
+  lsum = wave_sum(lsum);
   uint8_t* ob = static_cast<uint8_t*>(a.out) +
                 (((int64_t)row * a.num_q_heads + hq) * D + lane * DPT) * E::bytes;
   store_run<E, DPT>(ob, acc, 1.f / lsum);
