@@ -318,6 +318,10 @@ __device__ __forceinline__ void prefill_tile_body(const PrefillArgs& a, int bx, 
 
   // One 64-key iteration from LDS stage `stage`: S^T, online softmax, O^T.
   auto compute = [&](int it, const uint8_t* stage) {
+    // LLVM's single-wave MFMA interleaving strategy for this scheduling
+    // region: measured ~2% faster on long prompts than the default schedule
+    // (the small-GEMM strategy is equal, the exp-interleaving ones slower)
+    __builtin_amdgcn_iglp_opt(1);
     const uint8_t* lds_kc = stage;
     const uint8_t* lds_vc = stage + S::KBUF;
     // ---- S^T for 64 keys x 16 tokens per sub-tile: 4 tiles of 16 keys
