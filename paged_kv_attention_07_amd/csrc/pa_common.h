@@ -102,7 +102,6 @@ __device__ __forceinline__ float sum8(float x) {
   return x;
 }
 
-__device__ __forceinline__ float shfl_xor(float x, int mask) { return __shfl_xor(x, mask, kWave); }
 
 // gfx950's row-swap moves.  swap32(a, b) exchanges the upper 32 lanes of `a`
 // with the lower 32 lanes of `b`; swap16(a, b) exchanges rows 1 and 3 of `a`
@@ -137,20 +136,21 @@ __device__ __forceinline__ float sum_over_rows(float x) {
 }
 // The value of lane l ^ 8 (rotating a 16-lane row by 8 swaps its halves).
 __device__ __forceinline__ float xor8(float x) { return dpp<kDppRowRor8>(x); }
-// Max / sum over the whole wavefront, in registers; every lane gets the same
-// bits.  Needs the whole wavefront active.
-__device__ __forceinline__ float wave_max(float x) {
+// Max / sum over the 16 lanes of a row, in registers; every lane of the row
+// gets the same bits.
+__device__ __forceinline__ float row_max16(float x) {
   x = fmaxf(x, dpp<kDppQuadXor1>(x));
   x = fmaxf(x, dpp<kDppQuadXor2>(x));
   x = fmaxf(x, dpp<kDppRowHalfMirror>(x));
-  x = fmaxf(x, xor8(x));
-  return max_over_rows(x);
+  return fmaxf(x, xor8(x));
 }
-__device__ __forceinline__ float wave_sum(float x) {
+__device__ __forceinline__ float row_sum16(float x) {
   x = sum8(x);
-  x += xor8(x);
-  return sum_over_rows(x);
+  return x + xor8(x);
 }
+// The same over the whole wavefront.  Needs the whole wavefront active.
+__device__ __forceinline__ float wave_max(float x) { return max_over_rows(row_max16(x)); }
+__device__ __forceinline__ float wave_sum(float x) { return sum_over_rows(row_sum16(x)); }
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 

@@ -194,8 +194,7 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(PrefillArgs a) {
       const bool vis = tok < tile_valid && j <= nc + tile_start + tok && j < kend;
       const float sv_ = vis ? s[k] : -INFINITY;
       float mx = sv_;
-#pragma unroll
-      for (int o_ = 8; o_ > 0; o_ >>= 1) mx = fmaxf(mx, shfl_xor(mx, o_));
+      mx = row_max16(mx);
       const float mn = fmaxf(m[k], mx);
       float alpha = 1.f, p = 0.f;
       if (mn != -INFINITY) {  // row has a visible key so far
@@ -203,8 +202,7 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(PrefillArgs a) {
         p = vis ? __builtin_amdgcn_exp2f(sv_ - mn) : 0.f;
       }
       float ps = p;
-#pragma unroll
-      for (int o_ = 8; o_ > 0; o_ >>= 1) ps += shfl_xor(ps, o_);
+      ps = row_sum16(ps);
       l[k] = l[k] * alpha + ps;
       m[k] = mn;
       sp[row * kBlockSize + key] = p;
