@@ -1,23 +1,32 @@
 """Benchmark of the paged-KV-attention hot path on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
-                    [--extra] [--only decode|mixed|prefix|long] [--splits S]
-                    [--separate]
+                    [--extra] [--only LEG] [--splits S] [--separate] [--graph]
 
 A step is one pass of the whole path over one batch: slot mapping of the new
 tokens, reshape_and_cache of their K/V, then attention (decode for the decode
-batch, mixed for the chunked-prefill batch).  By default the three run as one
-attention launch (pa_cache_and_attend_*: the launch stores the new tokens and
-reads them from the input rows) plus the split merge; --separate times the
-three calls one after the other.  The shared-prefix leg always runs them
-apart (its entry takes the cache as written).  Inputs are resident in HBM
-before timing starts; several copies of the KV pool are rotated so that
-successive steps do not hit in the 256 MB Infinity Cache.
+batches, mixed for the chunked-prefill batch).  By default the three run as
+one attention launch (pa_cache_and_attend_*: the launch stores the new tokens
+and reads them from the input rows) plus the split merge; --separate times
+the three calls one after the other.  Inputs are resident in HBM before
+timing starts; several copies of the KV pool are rotated so that successive
+steps do not hit in the 256 MB Infinity Cache.
 
-Headline (`value`): algorithmic HBM bytes per decode step / step time, on the
-64-request Llama-3-8B-layer decode batch.  Also reported: tokens/s of the
-mixed chunked-prefill step, the roofline of the attention call (HIP events on
-the launch stream), and the CPU oracle timed on a bounded sample.
+Legs of a plain run, one per workload of the five configurations:
+  decode  64-request Llama-3-8B-layer decode batch (the headline `value`)
+  mixed   chunked-prefill mixed step (593 query tokens)
+  chunk   that step's 512-token prefill chunk alone (matrix-core utilisation)
+  prefix  256-request decode sharing a 1024-token prefix (priced on unique bytes)
+  long    16 x 32768-token decode (split-KV partition-and-reduce)
+  tiny    the tiny fp32 decode (launch-bound: microseconds only)
+--extra adds the long-prefill legs, the prefix batch through plain decode,
+pa_copy_blocks and the serving-trace engine.
+
+Each leg times K steps back to back.  `ms_per_step` is host wall time; the
+GPU time per step comes from one pair of HIP events recorded on the launch
+stream around the same K steps, and every leg's `roofline` divides the
+step's algorithmic bytes (or flops) by it.  The CPU oracle is timed on the
+headline batch over all host cores, before the GPU is first touched.
 """
 
 from __future__ import annotations
@@ -41,14 +50,19 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 WORKLOADS = {
     "decode": "decode_bf16_64req",
     "mixed": "mixed_chunked_prefill_bf16",
+    "chunk": "prefill_chunk_bf16",
     "prefix": "prefix_shared_decode_bf16",
     "long": "long_context_decode_bf16",
-    "chunk": "prefill_chunk_bf16",
+    "tiny": "tiny_f32_decode",
     "prefixplain": "prefix_shared_decode_bf16",
     "prefill2k": "prefill_chunk_2048_bf16",
     "prefill8k": "prefill_8192_bf16",
     "prefillbatch": "prefill_batch_4x1024_bf16",
 }
+DEFAULT_LEGS = ["decode", "mixed", "chunk", "prefix", "long", "tiny"]
+EXTRA_LEGS = ["prefixplain", "prefill2k", "prefill8k", "prefillbatch"]
+MFMA_LEGS = {"chunk", "prefill2k", "prefill8k", "prefillbatch"}
+UNIQUE_LEGS = {"prefix", "prefixplain"}    # priced on unique bytes (shared prefix once)
 
 DESCR = {
     "decode_bf16_64req": "Llama-3-8B layer decode (Hq 32, Hkv 8, D 128, bf16, block 16): 64 requests, "
@@ -58,6 +72,8 @@ DESCR = {
     "prefix_shared_decode_bf16": "Llama-3-8B layer decode, 256 requests sharing a 1024-token prefix "
                                  "(64 blocks) + private suffix U[64,512]",
     "long_context_decode_bf16": "Llama-3-8B layer decode, 16 requests at 32768 tokens, pool 36000 blocks",
+    "tiny_f32_decode": "fp32 decode, Hq 4, Hkv 2, D 64, 4 requests with seq_lens {5,16,17,100}, "
+                       "64-block pool",
     "prefill_chunk_bf16": "Llama-3-8B layer prefill chunk alone: 512 new tokens on 1024 cached",
     "prefill_chunk_2048_bf16": "Llama-3-8B layer prefill: 2048 new tokens on 2048 cached",
     "prefill_8192_bf16": "Llama-3-8B layer prefill: fresh 8192-token prompt",
@@ -71,7 +87,13 @@ DESCR = {
 
 
 def alg_counts(w):
-    """Bytes each part of one step must move, and the attention's flops."""
+    """Bytes one step must move, and the attention's flops.
+
+    attention: K/V of every visible key (logical: per request; unique: each
+    physical slot once), q in and out, one table entry per block read and
+    three int32 of metadata per request.  step: attention plus the new
+    tokens' K/V read from the input and stored into the cache, and their
+    slots written (the one-launch step returns them)."""
     esz = 4 if w.dtype == "f32" else 2
     Hq, Hkv, D, B = w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size
     T, R = w.num_tokens, w.num_seqs
@@ -79,37 +101,111 @@ def alg_counts(w):
     ql = w.q_lens
     rows = ql > 0
     keys_read = int(w.seq_lens[rows].astype(np.int64).sum())
-    # unique KV bytes: shared physical blocks counted once
     used_tokens = 0
     seen = set()
     for r in np.nonzero(rows)[0]:
         L = int(w.seq_lens[r])
-        nb = -(-L // B)
-        for j in range(nb):
+        for j in range(-(-L // B)):
             blk = int(w.block_table[r, j])
-            n_tok = min(B, L - j * B)
             if blk in seen:
                 continue
             seen.add(blk)
-            used_tokens += n_tok
+            used_tokens += min(B, L - j * B)
     nblocks = int(sum(-(-int(L) // B) for L in w.seq_lens[rows]))
-    attn_bytes_logical = keys_read * kb + 2 * T * Hq * D * esz + nblocks * 4 + R * 4 * 3
-    attn_bytes_unique = used_tokens * kb + 2 * T * Hq * D * esz + nblocks * 4 + R * 4 * 3
-    scatter_bytes = 2 * T * kb + T * 8
-    slot_bytes = T * 4 + R * 8 + T * 8
-    # flops: 4*D per (query head, visible key) pair (QK^T and PV)
-    pairs = 0
+    qo = 2 * T * Hq * D * esz
+    meta = nblocks * 4 + R * 4 * 3
+    attn_logical = keys_read * kb + qo + meta
+    attn_unique = used_tokens * kb + qo + meta
+    new_rows = 2 * T * kb + 8 * T
+    pairs = chunk_pairs = 0
     for r in np.nonzero(rows)[0]:
         c, n = int(w.num_computed[r]), int(ql[r])
         pairs += n * c + n * (n + 1) // 2
-    flops = 4 * D * Hq * pairs
-    chunk_pairs = 0
-    for r in np.nonzero(ql > 1)[0]:
-        c, n = int(w.num_computed[r]), int(ql[r])
-        chunk_pairs += n * c + n * (n + 1) // 2
-    return dict(attn_logical=attn_bytes_logical, attn_unique=attn_bytes_unique,
-                scatter=scatter_bytes, slots=slot_bytes, flops=flops,
-                chunk_flops=4 * D * Hq * chunk_pairs, kv_bytes_per_token=kb)
+        if n > 1:
+            chunk_pairs += n * c + n * (n + 1) // 2
+    return dict(attn_logical=attn_logical, attn_unique=attn_unique, new_rows=new_rows,
+                step_logical=attn_logical + new_rows, step_unique=attn_unique + new_rows,
+                flops=4 * D * Hq * pairs, chunk_flops=4 * D * Hq * chunk_pairs,
+                kv_bytes_per_token=kb)
+
+
+# --------------------------------------------------------------------------
+# CPU oracle baseline, all host cores (run before the GPU is touched)
+# --------------------------------------------------------------------------
+
+_CPU_STATE = {}
+
+
+def _cpu_worker_init():
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(limits=1)
+    except ImportError:  # pragma: no cover
+        pass
+
+
+def _cpu_worker(reqs):
+    import oracle
+    w, pool = _CPU_STATE["w"], _CPU_STATE["pool"]
+    out = oracle.paged_attention(w.q, pool, w.block_table, w.seq_lens, w.query_start_loc,
+                                 w.num_computed, w.scale, w.dtype, requests=reqs)
+    rows = np.concatenate([np.arange(w.query_start_loc[r], w.query_start_loc[r + 1])
+                           for r in reqs])
+    return out[rows]
+
+
+def cpu_baseline(w, budget_s: float = 10.0):
+    """The oracle as it stands on the whole batch: its scatter (a copy of the
+    pool with the new rows stored) once, then its attention with the requests
+    dealt over one worker process per host core (BLAS one thread each),
+    full passes until about `budget_s` of wall time, best pass kept.
+    Returns the step's algorithmic bytes per second, as the GPU figure."""
+    import multiprocessing as mp
+
+    import oracle
+    cores = len(os.sched_getaffinity(0))
+    slots = oracle.slot_mapping(w.block_table, w.query_start_loc, w.num_computed, w.block_size)
+    t0 = time.perf_counter()
+    pool = oracle.reshape_and_cache(w.pool, w.k_new, w.v_new, slots)
+    t_scatter = time.perf_counter() - t0
+    order = sorted((r for r in range(w.num_seqs) if w.q_lens[r] > 0),
+                   key=lambda r: -int(w.seq_lens[r]) * int(w.q_lens[r]))
+    groups = [[] for _ in range(cores)]
+    load = [0] * cores
+    for r in order:                               # longest first, to the lightest worker
+        i = int(np.argmin(load))
+        groups[i].append(r)
+        load[i] += int(w.seq_lens[r]) * int(w.q_lens[r])
+    groups = [g for g in groups if g]
+    _CPU_STATE.update(w=w, pool=pool)
+    best, spent, passes = float("inf"), 0.0, 0
+    try:
+        with mp.get_context("fork").Pool(len(groups), initializer=_cpu_worker_init) as p:
+            p.map(_cpu_worker, [[g[0]] for g in groups], chunksize=1)   # start-up
+            while passes < 3 or (spent < budget_s and passes < 50):
+                t0 = time.perf_counter()
+                p.map(_cpu_worker, groups, chunksize=1)
+                dt = time.perf_counter() - t0
+                best, spent, passes = min(best, dt), spent + dt, passes + 1
+    finally:
+        _CPU_STATE.clear()
+    c = alg_counts(w)
+    toks = int(sum(int(w.q_lens[r]) for r in order))
+    t_total = t_scatter + best
+    return {
+        "value": round(c["step_logical"] / t_total / 1e9, 4), "unit": "GB/s",
+        "cores": len(groups), "kind": "oracle",
+        "sample": f"all {len(order)} requests of {w.name} ({toks} query tokens, "
+                  f"{int(w.seq_lens.sum())} keys): the oracle's scatter once on one core "
+                  f"({t_scatter:.3f} s, a copy of the {w.pool.nbytes / 1e9:.2f} GB pool with "
+                  f"the new rows stored) + its fp64 numpy attention with the requests dealt "
+                  f"over {len(groups)} worker processes, BLAS 1 thread each, best of {passes} "
+                  f"full passes ({best:.3f} s)",
+        "scatter_s": round(t_scatter, 4), "attention_s": round(best, 4),
+        "tokens_per_s": round(toks / t_total, 3),
+        "cpu": platform.processor() or platform.machine(),
+        "host_cores_available": cores,
+    }
 
 
 # --------------------------------------------------------------------------
@@ -168,6 +264,20 @@ class Stepper:
                                   w.max_query_len, w.max_seq_len, out=self.out,
                                   workspace=self.ws, num_splits=self.splits)
 
+    def _fused(self, kv):
+        pa, w = self.pa, self.w
+        if self.decode:
+            pa.pa_cache_and_attend_decode(self.q, self.kn, self.vn, kv, self.bt, self.sl,
+                                          w.scale, w.max_seq_len, out=self.out,
+                                          slot_mapping=self.slots, workspace=self.ws,
+                                          num_splits=self.splits)
+        else:
+            pa.pa_cache_and_attend_mixed(self.q, self.kn, self.vn, kv, self.bt, self.sl,
+                                         self.qsl, self.nc, w.scale, w.max_query_len,
+                                         w.max_seq_len, out=self.out,
+                                         slot_mapping=self.slots, workspace=self.ws,
+                                         num_splits=self.splits)
+
     def capture(self):
         """Capture the one-launch step over each pool copy in its own HIP
         graph (kernels only: the entry points allocate and synchronise
@@ -189,21 +299,9 @@ class Stepper:
             self.graphs.append(g)
         torch.cuda.synchronize()
 
-    def _fused(self, kv):
-        pa, w = self.pa, self.w
-        if self.decode:
-            pa.pa_cache_and_attend_decode(self.q, self.kn, self.vn, kv, self.bt, self.sl,
-                                          w.scale, w.max_seq_len, out=self.out,
-                                          slot_mapping=self.slots, workspace=self.ws,
-                                          num_splits=self.splits)
-        else:
-            pa.pa_cache_and_attend_mixed(self.q, self.kn, self.vn, kv, self.bt, self.sl,
-                                         self.qsl, self.nc, w.scale, w.max_query_len,
-                                         w.max_seq_len, out=self.out,
-                                         slot_mapping=self.slots, workspace=self.ws,
-                                         num_splits=self.splits)
-
     def step(self, i, ev=None):
+        """One step over pool copy i; with `ev`, HIP events bracket the
+        attention call alone."""
         pa, w = self.pa, self.w
         kv = self.pools[i % len(self.pools)]
         if getattr(self, "graphs", None):
@@ -216,17 +314,7 @@ class Stepper:
         if self.fused:
             if ev is not None:
                 ev[0].record()
-            if self.decode:
-                pa.pa_cache_and_attend_decode(self.q, self.kn, self.vn, kv, self.bt, self.sl,
-                                              w.scale, w.max_seq_len, out=self.out,
-                                              slot_mapping=self.slots, workspace=self.ws,
-                                              num_splits=self.splits)
-            else:
-                pa.pa_cache_and_attend_mixed(self.q, self.kn, self.vn, kv, self.bt, self.sl,
-                                             self.qsl, self.nc, w.scale, w.max_query_len,
-                                             w.max_seq_len, out=self.out,
-                                             slot_mapping=self.slots, workspace=self.ws,
-                                             num_splits=self.splits)
+            self._fused(kv)
             if ev is not None:
                 ev[1].record()
             return
@@ -260,36 +348,35 @@ class Stepper:
         del scratch, other
         return ms
 
-    def run(self, steps: int, warmup: int, event_every: int = 1):
-        """Time `steps` steps; the attention call of every `event_every`-th
-        step is bracketed by HIP events on the launch stream (an event record
-        between two launches leaves the GPU idle for a moment, so sampling
-        keeps that measurement cost out of most steps)."""
+    def run(self, steps: int, warmup: int):
+        """Time `steps` steps back to back.  Returns (host ms per step, GPU ms
+        per step): the host figure is wall time between two synchronisations;
+        the GPU figure comes from one pair of HIP events recorded on the
+        launch stream before the first and after the last timed step, so no
+        event sits between two steps."""
         torch = self.torch
         for i in range(warmup):
             self.step(i)
         torch.cuda.synchronize()
-        sampled = [i for i in range(steps) if i % max(1, event_every) == 0]
-        events = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                  for i in sampled}
-        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
+        e0.record()
         for i in range(steps):
-            self.step(warmup + i, events.get(i))
+            self.step(warmup + i)
+        e1.record()
         torch.cuda.synchronize()
         t1 = time.perf_counter()
-        attn_ms = [a.elapsed_time(b) for a, b in events.values()]
-        return (t1 - t0) * 1e3 / steps, attn_ms
+        return (t1 - t0) * 1e3 / steps, e0.elapsed_time(e1) / steps
 
 
-def recorded_traffic(kernel: str):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
-    passes (profiles/traffic.json), or None if the kernel's sources changed
-    since the counters were taken."""
+def recorded_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` on `workload` from the committed
+    rocprofv3 counter passes (profiles/traffic.json), or None when the
+    kernel's sources changed since the counters were taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
-        rec = json.load(open(path))[kernel]
+        rec = json.load(open(path))[f"{kernel}@{workload}"]
     except (OSError, KeyError, ValueError):
         return None
     h = hashlib.sha256()
@@ -306,132 +393,135 @@ def gpu_info():
             "cus": p.multi_processor_count, "hbm_gb": round(p.total_memory / 2**30, 1)}
 
 
-def copy_reference(nbytes: int = 1 << 30, reps: int = 10):
-    """Achievable-HBM reference: a device-to-device copy of `nbytes` (read +
-    write counted), median of `reps` event-timed copies."""
+def _median_event_ms(fn, reps: int):
     import torch
-    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
-    dst = torch.empty_like(src)
-    src.fill_(1)
-    dst.copy_(src)
-    torch.cuda.synchronize()
     ms = []
     for _ in range(reps):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
-        dst.copy_(src)
+        fn()
         b.record()
         b.synchronize()
         ms.append(a.elapsed_time(b))
+    return float(np.median(ms))
+
+
+def hbm_references(copy_bytes: int = 1 << 30, read_bytes: int = 4 << 30, reps: int = 10):
+    """Achievable-bandwidth references from plain torch kernels: a
+    device-to-device copy (read + write counted) and a read-only reduction
+    (torch sum over `read_bytes` of fp32), median of `reps` event-timed runs."""
+    import torch
+    src = torch.ones(copy_bytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    t_copy = _median_event_ms(lambda: dst.copy_(src), reps) * 1e-3
     del src, dst
+    x = torch.ones(read_bytes // 4, dtype=torch.float32, device="cuda")
+    x.sum()
+    torch.cuda.synchronize()
+    t_read = _median_event_ms(lambda: x.sum(), reps) * 1e-3
+    del x
     torch.cuda.empty_cache()
-    t = float(np.median(ms)) * 1e-3
-    return {"kind": "device-to-device copy (torch), read + write bytes / median time",
-            "bytes": 2 * nbytes, "gbs": round(2 * nbytes / t / 1e9, 1),
-            "pct_peak_hbm": round(100 * 2 * nbytes / t / 1e9 / HBM_PEAK_GBS, 2)}
-
-
-# --------------------------------------------------------------------------
-# CPU oracle baseline (bounded sample)
-# --------------------------------------------------------------------------
-
-
-def cpu_baseline(w, budget_s: float = 12.0):
-    """Time the oracle (as it stands, BLAS limited to one thread) on the
-    first n requests of the same batch, n chosen so the run takes about
-    `budget_s`; scaled to the same unit as the GPU figure (GB/s of
-    algorithmic attention bytes)."""
-    import oracle
-    try:
-        from threadpoolctl import threadpool_limits
-    except ImportError:  # pragma: no cover
-        threadpool_limits = None
-    ctx = threadpool_limits(limits=1) if threadpool_limits else None
-    try:
-        if ctx is not None:
-            ctx.__enter__()
-        slots = oracle.slot_mapping(w.block_table, w.query_start_loc, w.num_computed, w.block_size)
-        t0 = time.perf_counter()
-        pool = oracle.reshape_and_cache(w.pool, w.k_new, w.v_new, slots)
-        t_scatter = time.perf_counter() - t0
-        order = [r for r in range(w.num_seqs) if w.q_lens[r] > 0]
-        # requests one at a time, in batch order, until the time budget is used
-        sample, t_attn = [], 0.0
-        for r in order:
-            t0 = time.perf_counter()
-            oracle.paged_attention(w.q, pool, w.block_table, w.seq_lens, w.query_start_loc,
-                                   w.num_computed, w.scale, w.dtype, requests=[r])
-            t_attn += time.perf_counter() - t0
-            sample.append(r)
-            if t_attn >= budget_s:
-                break
-        n = len(sample)
-        passes = 1
-        if n == len(order):
-            # the whole batch fit the budget: time more full passes, keep the best
-            best, spent = t_attn, t_attn
-            while passes < 3 and spent + best < budget_s:
-                t0 = time.perf_counter()
-                oracle.paged_attention(w.q, pool, w.block_table, w.seq_lens,
-                                       w.query_start_loc, w.num_computed, w.scale, w.dtype,
-                                       requests=order)
-                dt = time.perf_counter() - t0
-                best, spent, passes = min(best, dt), spent + dt, passes + 1
-            t_attn = best
-    finally:
-        if ctx is not None:
-            ctx.__exit__(None, None, None)
-    esz = 4 if w.dtype == "f32" else 2
-    kb = 2 * w.num_kv_heads * w.head_dim * esz
-    keys = int(sum(int(w.seq_lens[r]) for r in sample))
-    toks = int(sum(int(w.q_lens[r]) for r in sample))
-    byts = keys * kb + 2 * toks * w.num_q_heads * w.head_dim * esz
-    # scatter of the sample's tokens is charged pro rata
-    t_total = t_attn + t_scatter * toks / max(1, w.num_tokens)
+    cgbs = 2 * copy_bytes / t_copy / 1e9
+    rgbs = read_bytes / t_read / 1e9
     return {
-        "value": round(byts / t_total / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-        "sample": f"{n} of {len(order)} requests of {w.name} (slot mapping excluded, "
-                  f"scatter charged pro rata): {toks} query tokens, {keys} keys, "
-                  f"{t_total:.2f} s fp64 numpy, BLAS 1 thread"
-                  + (f", best of {passes} full passes" if passes > 1 else ""),
-        "tokens_per_s": round(toks / t_total, 3),
-        "cpu": platform.processor() or platform.machine(),
-        "host_cores_available": len(os.sched_getaffinity(0)),
+        "copy": {"kind": "device-to-device copy (torch), read + write bytes / median time",
+                 "bytes": 2 * copy_bytes, "gbs": round(cgbs, 1),
+                 "pct_peak_hbm": round(100 * cgbs / HBM_PEAK_GBS, 2)},
+        "read": {"kind": "read-only reduction (torch sum of fp32), bytes read / median time",
+                 "bytes": read_bytes, "gbs": round(rgbs, 1),
+                 "pct_peak_hbm": round(100 * rgbs / HBM_PEAK_GBS, 2)},
     }
 
 
 # --------------------------------------------------------------------------
+# legs
+# --------------------------------------------------------------------------
 
 
-def measure(name, args, rotations, shared_prefix=False, flushed: int = 0):
+def _entry(key, fused):
+    if key == "prefix":
+        return "pa_attention_decode_shared_prefix (after slot mapping and reshape_and_cache)"
+    if key in ("decode", "long", "tiny", "prefixplain"):
+        return "pa_cache_and_attend_decode" if fused else "pa_attention_decode (three calls)"
+    return "pa_cache_and_attend_mixed" if fused else "pa_attention_mixed (three calls)"
+
+
+DOMINANT = {
+    "decode": "decode_split_kernel", "long": "decode_split_kernel",
+    "prefixplain": "decode_split_kernel", "tiny": "decode_split_kernel",
+    "mixed": "fused_attention_kernel", "prefix": "fused_attention_kernel",
+    "chunk": "prefill_tile_kernel", "prefill2k": "prefill_tile_kernel",
+    "prefill8k": "prefill_tile_kernel", "prefillbatch": "fused_attention_kernel",
+}
+
+
+def measure(key, args, w=None, flushed: int = 0):
+    import torch
     from workloads import make_workload
-    t0 = time.perf_counter()
-    w = make_workload(name)
-    print(f"[bench] {name}: generated in {time.perf_counter() - t0:.1f}s", file=sys.stderr,
-          flush=True)
-    st = Stepper(w, rotations, args.splits,
-                 w.meta.get("shared_prefix_blocks", 0) if shared_prefix else 0,
-                 fused=not args.separate)
+    name = WORKLOADS[key]
+    if w is None:
+        t0 = time.perf_counter()
+        w = make_workload(name)
+        print(f"[bench] {name}: generated in {time.perf_counter() - t0:.1f}s", file=sys.stderr,
+              flush=True)
+    rotations = 1 if key == "tiny" else 4
+    sp = w.meta.get("shared_prefix_blocks", 0) if key == "prefix" else 0
+    st = Stepper(w, rotations, args.splits, sp, fused=not args.separate)
     if args.graph and st.fused:
         st.capture()
-    ms_step, attn_ms = st.run(args.steps, args.warmup, args.event_every)
+    ms_step, gpu_ms = st.run(args.steps, args.warmup)
     c = alg_counts(w)
-    attn_avg = float(np.mean(attn_ms))
-    res = dict(w=w, counts=c, ms_step=ms_step, attn_ms_avg=attn_avg, fused=st.fused,
-               graph=bool(getattr(st, "graphs", None)),
-               attn_ms_p10=float(np.percentile(attn_ms, 10)),
-               attn_ms_p50=float(np.percentile(attn_ms, 50)),
-               attn_ms_p90=float(np.percentile(attn_ms, 90)))
-    print(f"[bench] {name}: {ms_step * 1e3:.1f} us/step, attention {attn_avg * 1e3:.1f} us",
-          file=sys.stderr, flush=True)
+    print(f"[bench] {key} ({name}): {ms_step * 1e3:.1f} us/step host, {gpu_ms * 1e3:.1f} us/step "
+          f"GPU", file=sys.stderr, flush=True)
+    res = dict(key=key, w=w, counts=c, ms_step=ms_step, gpu_ms=gpu_ms, fused=st.fused,
+               graph=bool(getattr(st, "graphs", None)), rotations=rotations)
     if flushed:
         res["flushed_ms"] = st.run_flushed(flushed)
-        print(f"[bench] {name}: flushed launches median "
+        print(f"[bench] {key}: flushed launches median "
               f"{np.median(res['flushed_ms']) * 1e3:.1f} us", file=sys.stderr, flush=True)
     del st
-    import torch
     torch.cuda.empty_cache()
     return res
+
+
+def leg_line(r):
+    """JSON record of one leg: step times and the roofline of its step."""
+    key, w, c = r["key"], r["w"], r["counts"]
+    gpu_s = r["gpu_ms"] * 1e-3
+    line = {"workload": w.name, "description": DESCR.get(w.name, ""),
+            "entry": _entry(key, r["fused"]), "graph_replay": r["graph"],
+            "ms_per_step": round(r["ms_step"], 5), "gpu_us_per_step": round(r["gpu_ms"] * 1e3, 2),
+            "query_tokens": w.num_tokens, "num_seqs": w.num_seqs,
+            "tokens_per_s": round(w.num_tokens / (r["ms_step"] * 1e-3), 1)}
+    if key == "tiny":
+        line["roofline"] = None
+        line["note"] = "launch-bound (a 1 MiB pool): microseconds only"
+        return line
+    if key in MFMA_LEGS:
+        tf = c["chunk_flops"] / gpu_s / 1e12
+        line["roofline"] = {
+            "bound": "mfma", "achieved": round(tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": None, "kernel": DOMINANT[key],
+            "alg_flops_per_launch": int(c["chunk_flops"])}
+        return line
+    unique = key in UNIQUE_LEGS
+    alg = c["step_unique"] if unique else c["step_logical"]
+    gbs = alg / gpu_s / 1e9
+    line["roofline"] = {
+        "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "frac": round(gbs / HBM_PEAK_GBS, 4),
+        "traffic": recorded_traffic(DOMINANT[key], w.name), "kernel": DOMINANT[key],
+        "alg_bytes_per_launch": int(alg)}
+    if unique:
+        line["roofline"]["priced_on"] = "unique bytes (the shared prefix once)"
+        line["effective_gbs_logical"] = round(c["step_logical"] / gpu_s / 1e9, 1)
+    if key == "mixed":
+        line["chunk_gflop"] = round(c["chunk_flops"] / 1e9, 3)
+        line["chunk_tflops_over_step"] = round(c["chunk_flops"] / gpu_s / 1e12, 1)
+    return line
 
 
 def measure_copy(args, pairs_n: int, num_blocks: int = 20000):
@@ -449,14 +539,13 @@ def measure_copy(args, pairs_n: int, num_blocks: int = 20000):
     for i in range(args.warmup):
         pa.pa_copy_blocks(pools[i % 2], pairs)
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
     for i in range(args.steps):
-        ev[i][0].record()
         pa.pa_copy_blocks(pools[i % 2], pairs)
-        ev[i][1].record()
+    e1.record()
     torch.cuda.synchronize()
-    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    ms = e0.elapsed_time(e1) / args.steps
     block_bytes = 2 * 16 * 8 * 128 * 2
     moved = 2 * pairs_n * block_bytes  # read src + write dst
     print(f"[bench] copy_blocks {pairs_n} pairs: {ms * 1e3:.1f} us", file=sys.stderr, flush=True)
@@ -490,25 +579,18 @@ def measure_serve(name: str = "serve_llama3_2k"):
         eng = Engine(num_blocks=t.num_blocks, max_num_batched_tokens=t.max_num_batched_tokens,
                      max_num_seqs=t.max_num_seqs, max_model_len=t.max_model_len, num_q_heads=Hq,
                      num_kv_heads=Hkv, head_dim=D, dtype="bf16")
-        host_s, tokens, steps, gpu_ms = 0.0, 0, 0, []
-        # events around every tenth step only: each record costs host time,
-        # which this host-and-GPU loop would otherwise pay on every step
-        events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                  if i % 10 == 0 else None for i in range(t.num_steps)]
+        host_s, tokens, steps = 0.0, 0, 0
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
+        e0.record()
         for step in range(t.num_steps):
             for rid, prompt, n in t.arrivals.get(step, []):
                 eng.add_request(rid, prompt, n)
             for parent, child, n in t.forks.get(step, []):
                 eng.fork(parent, child, n)
             h0 = time.perf_counter()
-            ev = events[steps]
-            if ev:
-                ev[0].record()
             st = eng.step(*dev)
-            if ev:
-                ev[1].record()
             if st.num_seqs == 0:
                 eng.update([])
                 if not eng.stats()["num_waiting"] and step > max(t.arrivals):
@@ -518,24 +600,23 @@ def measure_serve(name: str = "serve_llama3_2k"):
             host_s += time.perf_counter() - h0
             tokens += st.num_tokens
             steps += 1
-
+        e1.record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        gpu_ms.extend(ev[0].elapsed_time(ev[1]) for ev in events[:steps] if ev)
         stats = eng.stats()
         eng.close()
         del eng
         torch.cuda.empty_cache()
-        return wall, host_s, tokens, steps, stats, float(np.mean(gpu_ms))
+        return wall, host_s, tokens, steps, stats, e0.elapsed_time(e1)
 
     run()                                   # warm-up pass over the same trace
-    wall, host_s, tokens, steps, stats, gpu_step_ms = run()
+    wall, host_s, tokens, steps, stats, gpu_span_ms = run()
     print(f"[bench] serve {name}: {steps} steps, {tokens} tokens in {wall * 1e3:.1f} ms",
           file=sys.stderr, flush=True)
     return {"trace": name, "steps": steps, "tokens": tokens,
             "tokens_per_s": round(tokens / wall, 1), "ms_per_step": round(wall * 1e3 / steps, 4),
             "host_us_per_step": round(host_s * 1e6 / steps, 1),
-            "gpu_us_per_step": round(gpu_step_ms * 1e3, 1),
+            "gpu_span_us_per_step": round(gpu_span_ms * 1e3 / steps, 1),
             "prefix_hit_tokens": stats["total_prefix_hit_tokens"],
             "preemptions": stats["total_preemptions"],
             "layer": "Llama-3-8B attention layer (Hq 32, Hkv 8, D 128, bf16)"}
@@ -550,14 +631,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",
                     help="replay each step from a captured HIP graph (one-launch steps only)")
-    ap.add_argument("--event-every", type=int, default=10,
-                    help="bracket every N-th timed step's attention call with HIP events "
-                         "(1: every step)")
     ap.add_argument("--separate", action="store_true",
                     help="slot mapping, reshape_and_cache and attention as three calls "
                          "(default: one cache-and-attend launch)")
-    ap.add_argument("--extra", action="store_true", help="also time the prefix-shared and "
-                    "long-context decode batches")
+    ap.add_argument("--extra", action="store_true",
+                    help="also the long-prefill legs, plain decode of the prefix batch, "
+                         "pa_copy_blocks and the serving-trace engine")
     ap.add_argument("--only", choices=sorted(WORKLOADS) + ["copy", "serve"], default=None)
     ap.add_argument("--flushed", type=int, default=60,
                     help="cold-cache launches of the headline leg, each after a 512 MiB "
@@ -571,66 +650,56 @@ def main():
               "(run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
 
+    if args.only in ("copy", "serve"):
+        keys = []
+    elif args.only:
+        keys = [args.only]
+    else:
+        keys = DEFAULT_LEGS + (EXTRA_LEGS if args.extra else [])
+
+    # the oracle baseline forks one worker per host core: it runs first, on the
+    # headline batch, before anything initialises the GPU in this process
+    from workloads import make_workload
+    head_key = keys[0] if keys else "decode"
+    t0 = time.perf_counter()
+    head_w = make_workload(WORKLOADS[head_key])
+    print(f"[bench] {head_w.name}: generated in {time.perf_counter() - t0:.1f}s",
+          file=sys.stderr, flush=True)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(head_w)
+        print(f"[bench] cpu baseline: {cpu['value']} GB/s on {cpu['cores']} cores",
+              file=sys.stderr, flush=True)
+
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    rot = 4
-    names = [args.only] if args.only else ["decode", "mixed", "chunk"] + (
-        ["prefix", "prefixplain", "long", "prefill2k", "prefill8k", "prefillbatch"]
-        if args.extra else [])
+    results = {}
+    for k in keys:
+        results[k] = measure(k, args, w=head_w if k == head_key else None,
+                             flushed=args.flushed if k == head_key else 0)
     copy_lines, serve_line = [], None
     if args.only == "copy" or (args.extra and not args.only):
         copy_lines = [measure_copy(args, n) for n in (16, 256, 4096)]
     if args.only == "serve" or (args.extra and not args.only):
         serve_line = measure_serve()
-    if args.only in ("copy", "serve"):
-        names = ["decode"]
-    names = [n for n in names if n in WORKLOADS]
-    # the prefix-shared batch runs the shared-prefix decode ("prefix") and the
-    # plain decode ("prefixplain") on the same inputs
-    results = {k: measure(WORKLOADS[k], args, rot if k != "long" else 2,
-                          shared_prefix=(k == "prefix"),
-                          flushed=args.flushed if k == names[0] else 0) for k in names}
+    if not results:   # copy / serve alone: the decode leg stays the headline
+        results["decode"] = measure("decode", args, w=head_w)
+        head_key = "decode"
 
-    # the headline is the decode batch; with --only <leg> it is that leg, with
-    # the roofline of the kernel that dominates it
-    head_key = "decode" if "decode" in results else next(iter(results))
+    legs = {k: leg_line(r) for k, r in results.items()}
     head = results[head_key]
-    w, c = head["w"], head["counts"]
-    attn_bytes = c["attn_unique"] if head_key in ("prefix", "prefixplain") else c["attn_logical"]
-    step_bytes = attn_bytes + c["scatter"] + c["slots"]
-    value = step_bytes / (head["ms_step"] * 1e-3) / 1e9
-    achieved = c["attn_logical"] / (head["attn_ms_avg"] * 1e-3) / 1e9
-    launch = {"avg_launch_us": round(head["attn_ms_avg"] * 1e3, 2),
-              "p10_us": round(head["attn_ms_p10"] * 1e3, 2),
-              "p50_us": round(head["attn_ms_p50"] * 1e3, 2),
-              "p90_us": round(head["attn_ms_p90"] * 1e3, 2)}
-    if head_key in ("chunk", "prefill2k", "prefill8k", "prefillbatch"):
-        tflops = c["chunk_flops"] / (head["attn_ms_avg"] * 1e-3) / 1e12
-        roofline = {"bound": "mfma", "achieved": round(tflops, 1),
-                    "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
-                    "kernel": ("pa_cache_and_attend_mixed" if head["fused"]
-                               else "pa_attention_mixed") + " (prefill_tile_kernel)",
-                    "alg_flops_per_launch": int(c["chunk_flops"]), **launch}
+    hw, hc, hl = head["w"], head["counts"], legs[head_key]
+    if head_key in MFMA_LEGS or head_key == "tiny":
+        value, unit = hl["tokens_per_s"], "tokens/s"
     else:
-        # shared-prefix batches are priced on unique bytes (the prefix once)
-        alg = c["attn_unique"] if head_key in ("prefix", "prefixplain") else c["attn_logical"]
-        if head["fused"]:
-            # the launch also reads the new K/V rows, stores them and the slots
-            alg += c["scatter"] + 8 * w.num_tokens
-        achieved = alg / (head["attn_ms_avg"] * 1e-3) / 1e9
-        dec = "pa_cache_and_attend_decode" if head["fused"] else "pa_attention_decode"
-        kernel = {"decode": dec + " (decode_split_kernel + decode_merge_kernel)",
-                  "prefix": "pa_attention_decode_shared_prefix",
-                  "prefixplain": dec, "long": dec,
-                  "mixed": "pa_cache_and_attend_mixed" if head["fused"]
-                  else "pa_attention_mixed"}.get(head_key, head_key)
-        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                    "traffic": recorded_traffic("decode_split_kernel")
-                    if head_key == "decode" else None,
-                    "traffic_kernel": "decode_split_kernel (profiles/traffic.json)",
-                    "kernel": kernel, "alg_bytes_per_launch": int(alg), **launch}
+        step_bytes = hc["step_unique"] if head_key in UNIQUE_LEGS else hc["step_logical"]
+        value, unit = step_bytes / (head["ms_step"] * 1e-3) / 1e9, "GB/s"
+    roofline = dict(hl["roofline"] or {})
+    if roofline:
+        roofline["gpu_us_per_step"] = hl["gpu_us_per_step"]
+        roofline["timing"] = ("algorithmic bytes (flops) of the step / GPU time per step from "
+                              "one pair of HIP events on the launch stream around the "
+                              f"{args.steps} timed steps")
     if head.get("flushed_ms"):
         fm = np.asarray(head["flushed_ms"])
         alg_bytes = roofline.get("alg_bytes_per_launch")
@@ -647,7 +716,7 @@ def main():
     line = {
         "metric": METRIC,
         "value": round(value, 1),
-        "unit": "GB/s",
+        "unit": unit,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -655,67 +724,26 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.dtype,
+        "dtype": hw.dtype,
         "data": "synthetic",
-        "config": {"workload": w.name, "description": DESCR.get(w.name, ""),
-                   "num_seqs": w.num_seqs, "query_tokens": w.num_tokens,
-                   "keys": int(w.seq_lens.sum()), "pool_blocks": w.num_blocks,
+        "config": {"workload": hw.name, "description": DESCR.get(hw.name, ""),
+                   "num_seqs": hw.num_seqs, "query_tokens": hw.num_tokens,
+                   "keys": int(hw.seq_lens.sum()), "pool_blocks": hw.num_blocks,
                    "step": ("slot_mapping + reshape_and_cache + attention in one launch "
                             "(pa_cache_and_attend_*) + split merge" if head["fused"] else
                             "slot_mapping + reshape_and_cache + attention (three calls)"),
-                   "pool_rotation": rot, "num_splits": args.splits or "auto"},
-        "pct_peak_hbm": round(100 * value / HBM_PEAK_GBS, 2),
-        "roofline": roofline,
-        "gpu": gpu_info(),
-        "hbm_reference": copy_reference(),
+                   "pool_rotation": head["rotations"], "num_splits": args.splits or "auto"},
+        "pct_peak_hbm": round(100 * value / HBM_PEAK_GBS, 2) if unit == "GB/s" else None,
+        "roofline": roofline or None,
+        "legs": legs,
     }
-    if "mixed" in results:
-        m = results["mixed"]
-        mw, mc = m["w"], m["counts"]
-        mbytes = mc["attn_logical"] + mc["scatter"] + mc["slots"]
-        line["mixed_step"] = {
-            "workload": mw.name, "tokens_per_s": round(mw.num_tokens / (m["ms_step"] * 1e-3), 1),
-            "ms_per_step": round(m["ms_step"], 5), "query_tokens": mw.num_tokens,
-            "hbm_gbs": round(mbytes / (m["ms_step"] * 1e-3) / 1e9, 1),
-            "pct_peak_hbm": round(100 * mbytes / (m["ms_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
-            "attention_avg_us": round(m["attn_ms_avg"] * 1e3, 2),
-            "chunk_gflop": round(mc["chunk_flops"] / 1e9, 3),
-        }
-    if "chunk" in results:
-        ch = results["chunk"]
-        cw, cc = ch["w"], ch["counts"]
-        tflops = cc["chunk_flops"] / (ch["attn_ms_avg"] * 1e-3) / 1e12
-        line["prefill_chunk"] = {
-            "workload": cw.name, "attention_avg_us": round(ch["attn_ms_avg"] * 1e3, 2),
-            "gflop": round(cc["chunk_flops"] / 1e9, 3), "tflops": round(tflops, 1),
-            "mfma_util": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-            "tokens_per_s": round(cw.num_tokens / (ch["ms_step"] * 1e-3), 1),
-        }
-    for key in ("prefill2k", "prefill8k", "prefillbatch"):
-        if key in results:
-            r = results[key]
-            rw, rc = r["w"], r["counts"]
-            tf = rc["chunk_flops"] / (r["attn_ms_avg"] * 1e-3) / 1e12
-            line[key] = {
-                "workload": rw.name, "attention_avg_us": round(r["attn_ms_avg"] * 1e3, 2),
-                "gflop": round(rc["chunk_flops"] / 1e9, 2), "tflops": round(tf, 1),
-                "mfma_util": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
-                "tokens_per_s": round(rw.num_tokens / (r["ms_step"] * 1e-3), 1),
-            }
-    for key in ("prefix", "prefixplain", "long"):
-        if key in results:
-            r = results[key]
-            rw, rc = r["w"], r["counts"]
-            line[f"{key}_decode"] = {
-                "entry": ("pa_attention_decode_shared_prefix" if key == "prefix"
-                          else "pa_cache_and_attend_decode" if r["fused"]
-                          else "pa_attention_decode"),
-                "workload": rw.name,
-                "attention_avg_us": round(r["attn_ms_avg"] * 1e3, 2),
-                "hbm_gbs_unique": round(rc["attn_unique"] / (r["attn_ms_avg"] * 1e-3) / 1e9, 1),
-                "effective_gbs_logical": round(rc["attn_logical"] / (r["attn_ms_avg"] * 1e-3) / 1e9, 1),
-                "ms_per_step": round(r["ms_step"], 5),
-            }
+    if "mixed" in legs:
+        m = legs["mixed"]
+        line["mixed_step"] = {"workload": m["workload"], "tokens_per_s": m["tokens_per_s"],
+                              "ms_per_step": m["ms_per_step"],
+                              "hbm_frac": m["roofline"]["frac"]}
+    line["gpu"] = gpu_info()
+    line["hbm_reference"] = hbm_references()
     if copy_lines:
         line["copy_blocks"] = copy_lines
     if serve_line:
@@ -729,8 +757,8 @@ def main():
         torch.cuda.synchronize()
         line["copy_probe_bytes"] = 1 << 30
         del src, dst
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w)
+    if cpu is not None:
+        line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
 
 
