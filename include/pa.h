@@ -9,6 +9,9 @@
  * Conventions shared by every entry point
  *   - Pointers are DEVICE pointers owned by the caller unless marked (host).
  *     The library keeps no pointer after a call returns and never allocates.
+ *     (The one exception, pa_cache_and_attend_mixed_no_workspace, uses a
+ *     fixed-size scratch array the library holds in device memory instead of
+ *     a caller's workspace.)
  *   - Every call is asynchronous on `stream` (a hipStream_t passed as void*;
  *     NULL = the default stream) and never synchronises.
  *   - Tensors are dense, row-major, with the shapes given below.
@@ -23,9 +26,9 @@
  *     scheduler: preconditions are listed per call; violating them gives
  *     unspecified results (never a write outside `out`/`kv_cache`/workspace,
  *     as long as table entries for positions < seq_len are valid block ids).
- *   - Thread safety: no global mutable state; concurrent calls on different
- *     streams must not share `out`, `kv_cache` slots being written, or
- *     `workspace`.
+ *   - Thread safety: no global mutable state besides that scratch array;
+ *     concurrent calls on different streams must not share `out`, `kv_cache`
+ *     slots being written, or `workspace`.
  */
 #ifndef PA_H_
 #define PA_H_
@@ -44,7 +47,9 @@ typedef enum {
   PA_ERR_INVALID_ARG = -1, /* null pointer, negative size, bad stride/shape   */
   PA_ERR_UNSUPPORTED = -2, /* block_size != 16, head_dim, dtype, head grouping */
   PA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required      */
-  PA_ERR_HIP = -4          /* a HIP launch reported an error                  */
+  PA_ERR_HIP = -4,         /* a HIP launch reported an error                  */
+  PA_ERR_SCRATCH = -5      /* the call needs more scratch than the library's
+                              built-in array holds (no-workspace entry only)  */
 } pa_status;
 
 /* Static, NUL-terminated description of a status code. */
@@ -283,6 +288,39 @@ int pa_cache_and_attend_mixed(void* out, const void* q, const void* key, const v
                               int32_t max_seq_len, int32_t num_q_heads, float scale,
                               void* workspace, size_t workspace_bytes, int32_t num_splits,
                               void* stream);
+
+/*
+ * pa_cache_and_attend_mixed_no_workspace -- for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation): pa_cache_and_attend_mixed without the workspace
+ * arguments.  Same kernels, same plan, same results bit for bit; the split-KV
+ * partials go to a scratch array of PA_NO_WORKSPACE_MAX_BYTES that the
+ * library holds in device memory (one per GPU it runs on, kept until the
+ * process ends).
+ *   - The call allocates nothing: no hipMalloc, no hipFree.  Its first call
+ *     on a device looks up that device's copy of the array (the current HIP
+ *     device must be the one `stream` belongs to).
+ *   - Sizes: a call whose pa_attention_workspace_size(num_seqs, num_tokens,
+ *     ..., max_seq_len, max_query_len, num_splits) exceeds
+ *     PA_NO_WORKSPACE_MAX_BYTES returns PA_ERR_SCRATCH and launches nothing
+ *     (e.g. 32 query heads of 128 dims: about 1,900 requests).
+ *   - Every call on a GPU uses that GPU's one array: calls that overlap in
+ *     time on one GPU (different streams, or different threads without an
+ *     ordering between their streams) race and give unspecified results.
+ *     Calls on one stream are ordered and safe.  Nothing in the array needs
+ *     to be cleared between calls.
+ *   Other arguments, preconditions and errors as pa_cache_and_attend_mixed.
+ */
+#define PA_NO_WORKSPACE_MAX_BYTES ((size_t)32 << 20)
+
+int pa_cache_and_attend_mixed_no_workspace(
+    void* out, const void* q, const void* key, const void* value, void* kv_cache,
+    int64_t num_blocks, int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+    int32_t dtype, const int32_t* block_table, int32_t block_table_stride,
+    const int32_t* seq_lens, const int32_t* query_start_loc,
+    const int32_t* num_computed_tokens, int64_t* slot_mapping, int32_t num_seqs,
+    int32_t num_tokens, int32_t max_query_len, int32_t max_seq_len, int32_t num_q_heads,
+    float scale, int32_t num_splits, void* stream);
 
 /*
  * pa_check_metadata -- check, on the device, the step metadata the calls

@@ -19,6 +19,7 @@ __all__ = [
     "pa_attention_workspace_size", "pa_attention_decode", "pa_attention_mixed",
     "pa_attention_decode_shared_prefix", "pa_attention_decode_shared_prefix_workspace_size",
     "pa_cache_and_attend_decode", "pa_cache_and_attend_mixed",
+    "pa_cache_and_attend_mixed_no_workspace", "NO_WORKSPACE_MAX_BYTES",
     "pa_check_metadata", "META_FLAGS", "pa_status_string", "pa_version",
     # short names: host bounds read back from the device when not given
     "compute_slot_mapping", "reshape_and_cache", "copy_blocks", "attention_decode",
@@ -89,6 +90,12 @@ lib.pa_cache_and_attend_mixed.argtypes = [
     _i32, _i32, _i32, _f32,                                   # max_q max_L Hq scale
     _vp, _sz, _i32, _vp]                                      # ws ws_bytes splits stream
 lib.pa_cache_and_attend_mixed.restype = ctypes.c_int
+lib.pa_cache_and_attend_mixed_no_workspace.argtypes = \
+    lib.pa_cache_and_attend_mixed.argtypes[:-4] + [_i32, _vp]  # no ws, ws_bytes
+lib.pa_cache_and_attend_mixed_no_workspace.restype = ctypes.c_int
+
+# size of the library's built-in scratch array (PA_NO_WORKSPACE_MAX_BYTES)
+NO_WORKSPACE_MAX_BYTES = 32 << 20
 
 lib.pa_check_metadata.argtypes = [
     _vp, _vp, _i32, _vp, _vp, _vp, _vp,       # flags bt stride seq_lens qsl nc slots
@@ -371,6 +378,33 @@ def pa_cache_and_attend_mixed(q, key, value, kv_cache, block_table, seq_lens, qu
         float(scale), _dev(ws, "workspace"), ws.numel() * ws.element_size(), int(num_splits),
         _stream())
     _check("pa_cache_and_attend_mixed", st)
+    return out
+
+
+def pa_cache_and_attend_mixed_no_workspace(q, key, value, kv_cache, block_table, seq_lens,
+                                           query_start_loc, num_computed_tokens, scale: float,
+                                           max_query_len: int, max_seq_len: int, out,
+                                           slot_mapping=None, num_splits: int = 0):
+    """pa_cache_and_attend_mixed with the split partials in the library's own
+    scratch array: allocates nothing, so ``out`` must be given; see pa.h."""
+    torch = _torch()
+    nb, bs, hkv, d = _cache_dims(kv_cache)
+    T, hq = int(q.shape[0]), int(q.shape[1])
+    R = int(seq_lens.shape[0])
+    if q.dim() != 3 or int(q.shape[2]) != d or q.dtype != kv_cache.dtype:
+        raise ValueError("q must be [num_tokens, num_q_heads, head_dim] in the cache dtype")
+    if tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype:
+        raise ValueError("out must have q's shape and dtype")
+    st = lib.pa_cache_and_attend_mixed_no_workspace(
+        _dev(out, "out"), _dev(q, "q"), _new_rows(key, "key", T, hkv, d, kv_cache),
+        _new_rows(value, "value", T, hkv, d, kv_cache), _dev(kv_cache, "kv_cache"), nb, bs,
+        hkv, d, _dtype_code(kv_cache), _dev(block_table, "block_table", torch.int32, 2),
+        int(block_table.shape[1]), _dev(seq_lens, "seq_lens", torch.int32, 1),
+        _dev(query_start_loc, "query_start_loc", torch.int32, 1),
+        _dev(num_computed_tokens, "num_computed_tokens", torch.int32, 1),
+        _slots_out(slot_mapping, T), R, T, int(max_query_len), int(max_seq_len), hq,
+        float(scale), int(num_splits), _stream())
+    _check("pa_cache_and_attend_mixed_no_workspace", st)
     return out
 
 

@@ -4,6 +4,7 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <mutex>
 
 #include "pa.h"
 #include "pa_kernels.h"
@@ -141,6 +142,7 @@ const char* pa_status_string(int status) {
     case PA_ERR_UNSUPPORTED: return "unsupported configuration";
     case PA_ERR_WORKSPACE: return "workspace missing or too small";
     case PA_ERR_HIP: return "HIP launch error";
+    case PA_ERR_SCRATCH: return "call needs more than the built-in scratch array";
     default: return "unknown status";
   }
 }
@@ -220,7 +222,9 @@ static int attention_common(void* out, const void* q, const void* kv_cache, int6
                             const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len,
                             int32_t num_q_heads, float scale, void* workspace,
                             size_t workspace_bytes, int32_t num_splits, int32_t max_query_len,
-                            int32_t shared_prefix_blocks, pa::DecodeArgs* a) {
+                            int32_t shared_prefix_blocks, pa::DecodeArgs* a,
+                            int (*scratch)(void**, size_t*) = nullptr,
+                            bool launches = true) {
   int st = check_cache(kv_cache, num_blocks, block_size, num_kv_heads, head_dim, dtype);
   if (st != PA_OK) return st;
   st = check_heads(num_q_heads, num_kv_heads);
@@ -243,8 +247,16 @@ static int attention_common(void* out, const void* q, const void* kv_cache, int6
                                  P > 0 ? num_seqs : max_query_len, dtype, head_dim, P > 0);
   const WsLayout lay = workspace_layout(num_seqs, num_q_heads, head_dim,
                                         chunks + (P > 0 ? num_seqs : 0));
-  if (!workspace || workspace_bytes < lay.total) return PA_ERR_WORKSPACE;
-  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return PA_ERR_WORKSPACE;
+  if (launches) {
+    // no workspace given: the library's own scratch array, looked up only
+    // now that every host check has passed
+    if (!workspace && scratch) {
+      const int sst = scratch(&workspace, &workspace_bytes);
+      if (sst != PA_OK) return sst;
+    }
+    if (!workspace || workspace_bytes < lay.total) return PA_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return PA_ERR_WORKSPACE;
+  }
 
   a->out = out;
   a->q = q;
@@ -308,13 +320,17 @@ int mixed_impl(void* out, const void* q, const void* kv_cache, int64_t num_block
                const int32_t* query_start_loc, const int32_t* num_computed_tokens,
                int32_t num_seqs, int32_t num_tokens, int32_t max_query_len, int32_t max_seq_len,
                int32_t num_q_heads, float scale, void* workspace, size_t workspace_bytes,
-               int32_t num_splits, const pa::NewTokens& fresh, void* stream) {
+               int32_t num_splits, const pa::NewTokens& fresh, void* stream,
+               int (*scratch)(void**, size_t*) = nullptr) {
   if (num_tokens < 0 || max_query_len < 0) return PA_ERR_INVALID_ARG;
+  // metadata pointers are checked before the workspace, whichever supplies it
+  if (num_seqs > 0 && num_tokens > 0 && (!query_start_loc || !num_computed_tokens))
+    return PA_ERR_INVALID_ARG;
   pa::DecodeArgs a{};
   const int st = attention_common(out, q, kv_cache, num_blocks, block_size, num_kv_heads, head_dim,
                                   dtype, block_table, block_table_stride, seq_lens, num_seqs,
                                   max_seq_len, num_q_heads, scale, workspace, workspace_bytes,
-                                  num_splits, max_query_len, 0, &a);
+                                  num_splits, max_query_len, 0, &a, scratch, num_tokens > 0);
   if (st <= 0) return st;
   if (num_tokens == 0) return PA_OK;
   if (!query_start_loc || !num_computed_tokens) return PA_ERR_INVALID_ARG;
@@ -528,3 +544,61 @@ int pa_attention_decode_shared_prefix(void* out, const void* q, const void* kv_c
 }
 
 }  // extern "C"
+
+// ---- pa_cache_and_attend_mixed_no_workspace ---------------------------------
+// The split-KV partials of callers that cannot allocate live in this array.
+// Host code never passes `scratch` itself to a kernel (in host code the name
+// is only a stand-in for the symbol): each device's copy is looked up once
+// with hipGetSymbolAddress and that address is what the kernels receive.
+static __device__ __align__(256) unsigned char scratch[PA_NO_WORKSPACE_MAX_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // per device, filled on the device's first call
+
+// Address and size of the current device's copy of `scratch` (looked up on
+// the first call with that device current, then cached).
+int scratch_address(void** out, size_t* bytes) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return PA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return PA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return PA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  *bytes = PA_NO_WORKSPACE_MAX_BYTES;
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" int pa_cache_and_attend_mixed_no_workspace(
+    void* out, const void* q, const void* key, const void* value, void* kv_cache,
+    int64_t num_blocks, int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+    int32_t dtype, const int32_t* block_table, int32_t block_table_stride,
+    const int32_t* seq_lens, const int32_t* query_start_loc,
+    const int32_t* num_computed_tokens, int64_t* slot_mapping, int32_t num_seqs,
+    int32_t num_tokens, int32_t max_query_len, int32_t max_seq_len, int32_t num_q_heads,
+    float scale, int32_t num_splits, void* stream) {
+  // the bound the workspace query gives for these arguments (it covers every
+  // plan the call may choose) must fit the array
+  const size_t need = pa_attention_workspace_size(num_seqs, num_tokens, num_q_heads,
+                                                  num_kv_heads, head_dim, max_seq_len,
+                                                  max_query_len, num_splits);
+  if (need > PA_NO_WORKSPACE_MAX_BYTES) return PA_ERR_SCRATCH;
+  if (num_tokens > 0 && !(key && value)) return PA_ERR_INVALID_ARG;
+  pa::NewTokens f{};
+  if (key || value) {
+    const int st = fresh_tokens(key, value, kv_cache, slot_mapping, &f);
+    if (st != PA_OK) return st;
+  }
+  return mixed_impl(out, q, kv_cache, num_blocks, block_size, num_kv_heads, head_dim, dtype,
+                    block_table, block_table_stride, seq_lens, query_start_loc,
+                    num_computed_tokens, num_seqs, num_tokens, max_query_len, max_seq_len,
+                    num_q_heads, scale, nullptr, 0, num_splits, f, stream, scratch_address);
+}

@@ -17,7 +17,7 @@ HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 pa = pytest.importorskip("paged_kv_attention_07_amd")
 lib = pa.lib
 
-OK, INVALID, UNSUPPORTED, WORKSPACE = 0, -1, -2, -3
+OK, INVALID, UNSUPPORTED, WORKSPACE, SCRATCH = 0, -1, -2, -3, -5
 FAKE = ctypes.c_void_p(0x10000)     # never dereferenced: checks fail before use
 FAKE_WS = ctypes.c_void_p(0x100000)  # 256-byte aligned
 
@@ -58,7 +58,7 @@ def test_no_torch_types_in_header():
 
 def test_status_strings():
     assert pa.pa_status_string(OK) == "ok"
-    for s in (INVALID, UNSUPPORTED, WORKSPACE, -4):
+    for s in (INVALID, UNSUPPORTED, WORKSPACE, -4, SCRATCH):
         assert pa.pa_status_string(s) not in ("", "ok", "unknown status")
     assert pa.pa_status_string(12345) == "unknown status"
     assert pa.pa_version() >= 100
@@ -202,6 +202,40 @@ def test_cache_and_attend_checks():
     assert cache_decode(R=0, k=None, v=None) == OK             # nothing to store or attend
     assert cache_mixed(T=0, k=None, v=None) == OK
     assert cache_mixed(dtype=0, wsb=8) == WORKSPACE            # fp32 chunks are accepted
+
+
+def no_workspace(**kw):
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, kv=FAKE, NB=64, B=16, Hkv=2, D=64, dtype=1,
+             bt=FAKE, stride=7, sl=FAKE, qsl=FAKE, nc=FAKE, slots=None, R=4, T=20, Q=17, L=100,
+             Hq=4, scale=0.125, S=0)
+    a.update(kw)
+    return lib.pa_cache_and_attend_mixed_no_workspace(
+        a["out"], a["q"], a["k"], a["v"], a["kv"], a["NB"], a["B"], a["Hkv"], a["D"],
+        a["dtype"], a["bt"], a["stride"], a["sl"], a["qsl"], a["nc"], a["slots"], a["R"],
+        a["T"], a["Q"], a["L"], a["Hq"], a["scale"], a["S"], None)
+
+
+def test_no_workspace_host_checks():
+    """The no-workspace step rejects a call whose workspace would exceed the
+    built-in scratch array, and every host-argument error, before it touches
+    the device (these calls need no GPU)."""
+    ws = lib.pa_attention_workspace_size
+    # 32 heads of 128 dims: a few hundred requests fit, ten thousand do not
+    assert ws(256, 256, 32, 8, 128, 4096, 1, 0) <= pa.NO_WORKSPACE_MAX_BYTES
+    assert ws(10000, 10000, 32, 8, 128, 4096, 1, 0) > pa.NO_WORKSPACE_MAX_BYTES
+    big = dict(R=10000, T=10000, Q=1, L=4096, Hq=32, Hkv=8, D=128, stride=256)
+    assert no_workspace(**big) == SCRATCH
+    assert no_workspace(**big, S=3) == SCRATCH
+    assert ws(10000, 10000, 32, 8, 128, 4096, 1, 3) > pa.NO_WORKSPACE_MAX_BYTES
+    assert no_workspace(out=None) == INVALID
+    assert no_workspace(k=None) == INVALID
+    assert no_workspace(qsl=None) == INVALID
+    assert no_workspace(B=8) == UNSUPPORTED
+    assert no_workspace(D=256) == UNSUPPORTED
+    assert no_workspace(Hq=6) == UNSUPPORTED
+    assert no_workspace(S=-1) == INVALID
+    assert no_workspace(R=0, T=0) == OK                        # nothing to launch
+    assert no_workspace(T=0, k=None, v=None) == OK
 
 
 def shared_prefix(**kw):
