@@ -20,7 +20,7 @@ __all__ = [
     "pa_attention_decode_shared_prefix", "pa_attention_decode_shared_prefix_workspace_size",
     "pa_cache_and_attend_decode", "pa_cache_and_attend_mixed",
     "pa_cache_and_attend_mixed_no_workspace", "NO_WORKSPACE_MAX_BYTES",
-    "pa_check_metadata", "META_FLAGS", "pa_status_string", "pa_version",
+    "pa_check_metadata", "META_FLAGS", "pa_status_string", "pa_version", "pa_read_probe",
     # short names: host bounds read back from the device when not given
     "compute_slot_mapping", "reshape_and_cache", "copy_blocks", "attention_decode",
     "attention_mixed", "cache_and_attend_decode", "cache_and_attend_mixed",
@@ -102,6 +102,9 @@ lib.pa_check_metadata.argtypes = [
     _i32, _i32, _i32, _i32, _i64, _i32, _i32,  # R T max_q max_L NB B prefix_blocks
     _vp]
 lib.pa_check_metadata.restype = ctypes.c_int
+
+lib.pa_read_probe.argtypes = [_vp, _sz, _vp, _i32, _vp]
+lib.pa_read_probe.restype = ctypes.c_int
 
 PA_F32, PA_BF16, PA_F16 = 0, 1, 2
 DTYPE_CODES = {"f32": PA_F32, "bf16": PA_BF16, "f16": PA_F16}
@@ -406,6 +409,16 @@ def pa_cache_and_attend_mixed_no_workspace(q, key, value, kv_cache, block_table,
         float(scale), int(num_splits), _stream())
     _check("pa_cache_and_attend_mixed_no_workspace", st)
     return out
+
+
+def pa_read_probe(buf, sink, waves_per_simd: int = 1) -> None:
+    """Stream the bytes of GPU tensor `buf` through the load units (the
+    read-bandwidth reference of include/pa_probe.h); `sink` is a one-element
+    int32 GPU tensor the kernel may write."""
+    torch = _torch()
+    st = lib.pa_read_probe(_dev(buf, "buf"), buf.numel() * buf.element_size(),
+                           _dev(sink, "sink", torch.int32, 1), int(waves_per_simd), _stream())
+    _check("pa_read_probe", st)
 
 
 # pa_meta_flag bits of pa_check_metadata (include/pa.h), in bit order
