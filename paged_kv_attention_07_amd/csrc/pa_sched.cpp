@@ -426,17 +426,20 @@ int pa_sched_schedule(pa_sched* s, pa_sched_step* st) {
     st->request_ids[i] = e.r->id;
     st->num_computed[i] = e.before;
     st->seq_lens[i] = e.before + e.num_new;
-    memcpy(st->token_ids + t, e.r->tokens.data() + e.before, sizeof(int32_t) * e.num_new);
+    if (e.num_new > 0)
+      memcpy(st->token_ids + t, e.r->tokens.data() + e.before, sizeof(int32_t) * e.num_new);
     t += e.num_new;
     st->query_start_loc[i + 1] = t;
     int32_t* row = st->block_table + (int64_t)i * st->block_table_stride;
     const size_t nb = e.r->blocks.size();
-    memcpy(row, e.r->blocks.data(), sizeof(int32_t) * nb);
+    if (nb > 0) memcpy(row, e.r->blocks.data(), sizeof(int32_t) * nb);
     for (int32_t j = (int32_t)nb; j < st->block_table_stride; ++j) row[j] = -1;
     if (e.num_new > max_q) max_q = e.num_new;
     if (e.before + e.num_new > max_L) max_L = e.before + e.num_new;
   }
-  memcpy(st->copy_pairs, copies.data(), sizeof(int32_t) * copies.size());
+  // (an empty vector's data() may be null, and memcpy from null is undefined
+  // even for zero bytes)
+  if (!copies.empty()) memcpy(st->copy_pairs, copies.data(), sizeof(int32_t) * copies.size());
   st->num_seqs = (int32_t)sched.size();
   st->num_tokens = t;
   st->max_query_len = max_q;
@@ -513,7 +516,8 @@ int pa_sched_get_request(const pa_sched* s, int64_t request_id, pa_sched_request
   out->prompt_len = r->prompt_len;
   if (blocks) {
     if (blocks_capacity < out->num_blocks) return PA_ERR_INVALID_ARG;
-    memcpy(blocks, r->blocks.data(), sizeof(int32_t) * r->blocks.size());
+    if (!r->blocks.empty())
+      memcpy(blocks, r->blocks.data(), sizeof(int32_t) * r->blocks.size());
   }
   return PA_OK;
 }

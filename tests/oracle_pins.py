@@ -439,6 +439,61 @@ def check_bf16_paths_agree(seed=8):
     assert np.array_equal(a, b, equal_nan=True)
 
 
+def check_used_slot_mask():
+    """The slots attention may read, against closed forms of the tables:
+    with private blocks, logical block j of a request with L keys holds
+    exactly its first min(16, L - 16 j) offsets and no other slot is used, so
+    the count is sum(L); with a shared prefix of P blocks the prefix blocks
+    are full and counted once, 16 P + sum(L - 16 P) in all."""
+    from workloads import make_workload
+    for name in ("tiny_f32_decode", "decode_bf16_small", "mixed_bf16_small",
+                 "prefix_shared_small"):
+        w = make_workload(name, values=False)
+        B = w.block_size
+        m = oracle.used_slot_mask(w.block_table, w.seq_lens, w.num_blocks, B)
+        assert m.shape == (w.num_blocks, B)
+        P = int(w.meta.get("shared_prefix_blocks", 0))
+        owned = set()
+        for r, L in enumerate(int(x) for x in w.seq_lens):
+            for j in range(-(-L // B)):
+                blk = int(w.block_table[r, j])
+                n = min(B, L - j * B)
+                assert m[blk, :n].all() and not m[blk, n:].any(), (name, r, j)
+                owned.add(blk)
+        others = np.setdiff1d(np.arange(w.num_blocks), np.array(sorted(owned)))
+        assert not m[others].any(), name
+        want = int(w.seq_lens.sum()) if P == 0 else \
+            B * P + int((w.seq_lens - B * P).sum())
+        assert int(m.sum()) == want, (name, int(m.sum()), want)
+
+
+def check_validate_metadata():
+    """The host-side metadata check accepts every committed workload and
+    rejects each planted violation of a precondition the kernels trust
+    ("vllm v1 源码精读（三）" §3.4 tables and slots, §4.2 packed offsets and
+    computed counts)."""
+    import meta_mutations as mm
+    from workloads import make_workload
+    for name in ("tiny_f32_decode", "decode_bf16_small", "mixed_bf16_small",
+                 "prefix_shared_small", "long_decode_small", "mixed_chunked_prefill_bf16"):
+        w = make_workload(name, values=False)
+        oracle.validate_metadata(w.block_table, w.seq_lens, w.query_start_loc, w.num_computed,
+                                 w.num_blocks, w.block_size, mm.slots_of(w))
+    for label, w, slots, _flag in mm.mutations():
+        try:
+            oracle.validate_metadata(w.block_table, w.seq_lens, w.query_start_loc,
+                                     w.num_computed, w.num_blocks, w.block_size, slots)
+        except ValueError:
+            continue
+        raise AssertionError(f"validate_metadata accepted: {label}")
+    # skipped tokens (negative slots) are not violations
+    w = mm.mixed()
+    s = mm.slots_of(w)
+    s[::3] = -1
+    oracle.validate_metadata(w.block_table, w.seq_lens, w.query_start_loc, w.num_computed,
+                             w.num_blocks, w.block_size, s)
+
+
 ALL_CHECKS = [
     check_slot_worked_example,
     check_pool_example_shapes,
@@ -454,4 +509,6 @@ ALL_CHECKS = [
     check_copy_on_write_fork,
     check_element_decoding,
     check_bf16_paths_agree,
+    check_used_slot_mask,
+    check_validate_metadata,
 ]

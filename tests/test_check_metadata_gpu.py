@@ -7,11 +7,10 @@ The check reads only the metadata arrays, each within its extent, so bad
 values are safe inputs for it.
 """
 
-import dataclasses
-
 import numpy as np
 import pytest
 
+import meta_mutations as mm
 import oracle
 from workloads import make_workload
 
@@ -53,8 +52,7 @@ def oracle_rejects(w, slots=None):
     return False
 
 
-def slots_of(w):
-    return oracle.slot_mapping(w.block_table, w.query_start_loc, w.num_computed, 16)
+slots_of = mm.slots_of
 
 
 @pytest.mark.parametrize("name", ["tiny_f32_decode", "decode_bf16_small", "mixed_bf16_small",
@@ -73,55 +71,17 @@ def test_committed_workloads_pass(name):
         assert device_check(w, s, decode=True, prefix=P) == []
 
 
-def _mixed():
-    return make_workload("mixed_bf16_small", values=False)
-
-
-def _copy(w, **arrays):
-    return dataclasses.replace(w, **{k: np.array(v) for k, v in arrays.items()})
-
-
-def _mutations():
-    """(label, metadata change, expected flag, whether the oracle covers it)."""
-    w = _mixed()
-    qlen = np.diff(w.query_start_loc)
-    long_r = int(np.argmax(qlen))
-    out = []
-
-    sl = w.seq_lens.copy(); nc = w.num_computed.copy()
-    r = int(np.argmax(w.seq_lens % 16 != 0))          # a request whose last block has room
-    sl[r] += 1
-    out.append(("seq_len != computed + q_len", _copy(w, seq_lens=sl), None, "computed", True))
-    nc = w.num_computed.copy(); nc[0] = -1
-    out.append(("negative computed", _copy(w, num_computed=nc), None, "computed", True))
-    bt = w.block_table.copy(); bt[long_r, 0] = w.num_blocks
-    out.append(("block id past the pool", _copy(w, block_table=bt), None, "block_id", True))
-    bt = w.block_table.copy(); bt[long_r, 0] = -1
-    out.append(("block id -1 inside seq_len", _copy(w, block_table=bt), None, "block_id", True))
-    q = w.query_start_loc.copy(); q[0] = 1
-    out.append(("qsl[0] != 0", _copy(w, query_start_loc=q), None, "query_start", True))
-    q = w.query_start_loc.copy(); q[2], q[3] = q[3], q[2]
-    out.append(("qsl decreasing", _copy(w, query_start_loc=q), None, "query_start", True))
-    q = w.query_start_loc.copy(); q[-1] -= 1
-    out.append(("qsl[R] != T", _copy(w, query_start_loc=q), None, "query_start", True))
-    bt = np.ascontiguousarray(w.block_table[:, :2])
-    out.append(("table narrower than seq_len", _copy(w, block_table=bt), None, "table_width",
-                True))
-    s = slots_of(w); s[5] = s[6]
-    out.append(("duplicate slot", w, s, "slot_dup", True))
-    s = slots_of(w); s[3] = w.num_blocks * 16
-    out.append(("slot past the pool", w, s, "slot_range", True))
-    return out
+_mixed = mm.mixed
+_copy = mm.copy_with
 
 
 @pytest.mark.parametrize("case", range(10))
 def test_planted_violation_sets_its_flag(case):
-    label, w, slots, flag, oracle_covers = _mutations()[case]
+    label, w, slots, flag = mm.mutations()[case]
     print(f"[case] planted: {label}", flush=True)
     got = device_check(w, slots, num_tokens=_mixed().num_tokens)  # the caller's own count
     assert flag in got, (label, got)
-    if oracle_covers:
-        assert oracle_rejects(w, slots), label
+    assert oracle_rejects(w, slots), label
     # skipped tokens (negative slots) are not violations
     if slots is not None:
         s = slots_of(w)

@@ -106,6 +106,35 @@ def _bad_copy_reversed(pool, pairs):
     return out
 
 
+_orig_mask = ref.used_slot_mask
+
+
+def _bad_mask_extra(block_table, seq_lens, num_blocks, block_size):
+    # one position past each request's end also marked
+    return _orig_mask(block_table, np.asarray(seq_lens) + 1, num_blocks, block_size)
+
+
+def _bad_mask_short(block_table, seq_lens, num_blocks, block_size):
+    return _orig_mask(block_table, np.maximum(np.asarray(seq_lens) - 1, 0), num_blocks,
+                      block_size)
+
+
+_orig_validate = ref.validate_metadata
+
+
+def _bad_validate_no_ids(block_table, seq_lens, query_start_loc, num_computed, num_blocks,
+                         block_size, slots=None):
+    # block ids not checked: a wide pool makes every id valid
+    return _orig_validate(np.abs(block_table), seq_lens, query_start_loc, num_computed,
+                          1 << 30, block_size, slots)
+
+
+def _bad_validate_no_slots(block_table, seq_lens, query_start_loc, num_computed, num_blocks,
+                           block_size, slots=None):
+    return _orig_validate(block_table, seq_lens, query_start_loc, num_computed, num_blocks,
+                          block_size, None)
+
+
 MUTATIONS = {
     "gqa_interleaved": ("kv_head_of", _bad_gqa),
     "causal_strict": ("visible", _bad_causal_strict),
@@ -123,6 +152,10 @@ MUTATIONS = {
     "k_v_swapped_on_write": ("reshape_and_cache", _bad_rac_kv_swapped),
     "copy_blocks_k_only": ("copy_blocks", _bad_copy_k_only),
     "copy_blocks_direction": ("copy_blocks", _bad_copy_reversed),
+    "used_slot_mask_one_past_end": ("used_slot_mask", _bad_mask_extra),
+    "used_slot_mask_one_short": ("used_slot_mask", _bad_mask_short),
+    "validate_ignores_block_ids": ("validate_metadata", _bad_validate_no_ids),
+    "validate_ignores_slots": ("validate_metadata", _bad_validate_no_slots),
 }
 
 
