@@ -221,7 +221,7 @@ class Stepper:
         import torch
         import paged_kv_attention_07_amd as pa
         self.pa, self.torch, self.w, self.splits = pa, torch, w, splits
-        self.fused = fused and not shared_prefix
+        self.fused = fused
         tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[w.dtype]
 
         def dev(a):
@@ -266,7 +266,12 @@ class Stepper:
 
     def _fused(self, kv):
         pa, w = self.pa, self.w
-        if self.decode:
+        if self.decode and self.shared_prefix:
+            pa.pa_cache_and_attend_decode_shared_prefix(
+                self.q, self.kn, self.vn, kv, self.bt, self.sl, w.scale, w.max_seq_len,
+                self.shared_prefix, out=self.out, slot_mapping=self.slots, workspace=self.ws,
+                num_splits=self.splits)
+        elif self.decode:
             pa.pa_cache_and_attend_decode(self.q, self.kn, self.vn, kv, self.bt, self.sl,
                                           w.scale, w.max_seq_len, out=self.out,
                                           slot_mapping=self.slots, workspace=self.ws,
@@ -449,7 +454,8 @@ def hbm_references(copy_bytes: int = 1 << 30, read_bytes: int = 4 << 30, reps: i
 
 def _entry(key, fused):
     if key == "prefix":
-        return "pa_attention_decode_shared_prefix (after slot mapping and reshape_and_cache)"
+        return ("pa_cache_and_attend_decode_shared_prefix" if fused else
+                "pa_attention_decode_shared_prefix (three calls)")
     if key in ("decode", "long", "tiny", "prefixplain"):
         return "pa_cache_and_attend_decode" if fused else "pa_attention_decode (three calls)"
     return "pa_cache_and_attend_mixed" if fused else "pa_attention_mixed (three calls)"

@@ -201,6 +201,33 @@ int pa_attention_decode_shared_prefix(void* out, const void* q, const void* kv_c
                                       size_t workspace_bytes, int32_t num_splits, void* stream);
 
 /*
+ * pa_cache_and_attend_decode_shared_prefix -- the decode step of a batch
+ * sharing prefix blocks in one attention launch (plus the merge): each
+ * request's new token gets its slot ([P4] §3.4), its K/V row is stored into
+ * the cache and the attention reads it from key / value, as in
+ * pa_cache_and_attend_decode; the prefix is attended once, as in
+ * pa_attention_decode_shared_prefix.  Results are those of
+ *     pa_compute_slot_mapping -> pa_reshape_and_cache ->
+ *     pa_attention_decode_shared_prefix
+ * with the same arguments (out, cache and slots bit for bit).
+ *
+ *   key, value, slot_mapping  as pa_cache_and_attend_decode.
+ *   Preconditions, besides those of pa_attention_decode_shared_prefix:
+ *   16 P < seq_lens[r] for every request (its new token, at position
+ *   seq_lens[r] - 1, lies past the prefix: shared blocks are never written,
+ *   [P4] §3.5), and the conditions of pa_cache_and_attend_decode.
+ *   P = 0, fp32, or a head shape without a matrix-core path runs
+ *   pa_cache_and_attend_decode.
+ */
+int pa_cache_and_attend_decode_shared_prefix(
+    void* out, const void* q, const void* key, const void* value, void* kv_cache,
+    int64_t num_blocks, int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+    int32_t dtype, const int32_t* block_table, int32_t block_table_stride,
+    const int32_t* seq_lens, int64_t* slot_mapping, int32_t num_seqs, int32_t max_seq_len,
+    int32_t num_q_heads, float scale, int32_t shared_prefix_blocks, void* workspace,
+    size_t workspace_bytes, int32_t num_splits, void* stream);
+
+/*
  * pa_attention_mixed -- attention for a chunked-prefill mixed batch.
  *   [P4] §4.2 (prefill chunks and decodes packed in one 1-D varlen batch;
  *   each sequence handled by its own bounds; a chunk attends its cached

@@ -19,6 +19,7 @@ __all__ = [
     "pa_attention_workspace_size", "pa_attention_decode", "pa_attention_mixed",
     "pa_attention_decode_shared_prefix", "pa_attention_decode_shared_prefix_workspace_size",
     "pa_cache_and_attend_decode", "pa_cache_and_attend_mixed",
+    "pa_cache_and_attend_decode_shared_prefix",
     "pa_cache_and_attend_mixed_no_workspace", "NO_WORKSPACE_MAX_BYTES",
     "pa_check_metadata", "META_FLAGS", "pa_status_string", "pa_version", "pa_read_probe",
     # short names: host bounds read back from the device when not given
@@ -84,6 +85,11 @@ lib.pa_cache_and_attend_decode.argtypes = [
     _vp, _i32, _vp, _vp, _i32, _i32, _i32, _f32,              # bt stride seq_lens slots R max_L Hq scale
     _vp, _sz, _i32, _vp]                                      # ws ws_bytes splits stream
 lib.pa_cache_and_attend_decode.restype = ctypes.c_int
+lib.pa_cache_and_attend_decode_shared_prefix.argtypes = [
+    _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32,  # out q key value kv NB B Hkv D dtype
+    _vp, _i32, _vp, _vp, _i32, _i32, _i32, _f32,              # bt stride seq_lens slots R max_L Hq scale
+    _i32, _vp, _sz, _i32, _vp]                                # prefix ws ws_bytes splits stream
+lib.pa_cache_and_attend_decode_shared_prefix.restype = ctypes.c_int
 lib.pa_cache_and_attend_mixed.argtypes = [
     _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32,  # out q key value kv NB B Hkv D dtype
     _vp, _i32, _vp, _vp, _vp, _vp, _i32, _i32,                # bt stride seq_lens qsl nc slots R T
@@ -351,6 +357,39 @@ def pa_cache_and_attend_decode(q, key, value, kv_cache, block_table, seq_lens, s
         _slots_out(slot_mapping, R), R, int(max_seq_len), hq, float(scale),
         _dev(ws, "workspace"), ws.numel() * ws.element_size(), int(num_splits), _stream())
     _check("pa_cache_and_attend_decode", st)
+    return out
+
+
+def pa_cache_and_attend_decode_shared_prefix(q, key, value, kv_cache, block_table, seq_lens,
+                                             scale: float, max_seq_len: int,
+                                             shared_prefix_blocks: int, out=None,
+                                             slot_mapping=None, workspace=None,
+                                             num_splits: int = 0):
+    """Decode step of a batch sharing its first `shared_prefix_blocks` table
+    entries, in one launch: stores key/value [R, Hkv, D] at position
+    seq_lens[r] - 1 (past the prefix) and attends, the prefix read once; see
+    pa.h."""
+    torch = _torch()
+    nb, bs, hkv, d = _cache_dims(kv_cache)
+    R, hq = int(q.shape[0]), int(q.shape[1])
+    if q.dim() != 3 or int(q.shape[2]) != d or q.dtype != kv_cache.dtype:
+        raise ValueError("q must be [num_seqs, num_q_heads, head_dim] in the cache dtype")
+    if out is None:
+        out = torch.empty_like(q)
+    need = pa_attention_decode_shared_prefix_workspace_size(R, hq, hkv, d, max_seq_len,
+                                                            shared_prefix_blocks, num_splits)
+    if need == 0:
+        raise ValueError("unsupported shared-prefix decode arguments")
+    ws = _workspace(need, q.device, workspace)
+    st = lib.pa_cache_and_attend_decode_shared_prefix(
+        _dev(out, "out"), _dev(q, "q"), _new_rows(key, "key", R, hkv, d, kv_cache),
+        _new_rows(value, "value", R, hkv, d, kv_cache), _dev(kv_cache, "kv_cache"), nb, bs,
+        hkv, d, _dtype_code(kv_cache), _dev(block_table, "block_table", torch.int32, 2),
+        int(block_table.shape[1]), _dev(seq_lens, "seq_lens", torch.int32, 1),
+        _slots_out(slot_mapping, R), R, int(max_seq_len), hq, float(scale),
+        int(shared_prefix_blocks), _dev(ws, "workspace"), ws.numel() * ws.element_size(),
+        int(num_splits), _stream())
+    _check("pa_cache_and_attend_decode_shared_prefix", st)
     return out
 
 

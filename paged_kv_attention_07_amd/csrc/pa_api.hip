@@ -494,30 +494,37 @@ size_t pa_attention_decode_shared_prefix_workspace_size(int32_t num_seqs, int32_
   return casc > plain ? casc : plain;
 }
 
-int pa_attention_decode_shared_prefix(void* out, const void* q, const void* kv_cache,
-                                      int64_t num_blocks, int32_t block_size,
-                                      int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
-                                      const int32_t* block_table, int32_t block_table_stride,
-                                      const int32_t* seq_lens, int32_t num_seqs,
-                                      int32_t max_seq_len, int32_t num_q_heads, float scale,
-                                      int32_t shared_prefix_blocks, void* workspace,
-                                      size_t workspace_bytes, int32_t num_splits, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int shared_prefix_impl(void* out, const void* q, const void* kv_cache, int64_t num_blocks,
+                       int32_t block_size, int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                       const int32_t* block_table, int32_t block_table_stride,
+                       const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len,
+                       int32_t num_q_heads, float scale, int32_t shared_prefix_blocks,
+                       void* workspace, size_t workspace_bytes, int32_t num_splits,
+                       const pa::NewTokens& fresh, void* stream) {
   const int P = shared_prefix_blocks;
   if (P < 0 || (int64_t)P * pa::kBlockSize > max_seq_len) return PA_ERR_INVALID_ARG;
   const int group = num_kv_heads > 0 && num_q_heads % num_kv_heads == 0
                         ? num_q_heads / num_kv_heads : 0;
   // no prefix, or no matrix-core path for this configuration: plain decode
   if (P == 0 || !pa::prefill_supported(dtype, head_dim, group))
-    return pa_attention_decode(out, q, kv_cache, num_blocks, block_size, num_kv_heads, head_dim,
-                               dtype, block_table, block_table_stride, seq_lens, num_seqs,
-                               max_seq_len, num_q_heads, scale, workspace, workspace_bytes,
-                               num_splits, stream);
+    return decode_impl(out, q, kv_cache, num_blocks, block_size, num_kv_heads, head_dim, dtype,
+                       block_table, block_table_stride, seq_lens, num_seqs, max_seq_len,
+                       num_q_heads, scale, workspace, workspace_bytes, num_splits, fresh,
+                       stream);
   pa::DecodeArgs a{};
   const int st = attention_common(out, q, kv_cache, num_blocks, block_size, num_kv_heads, head_dim,
                                   dtype, block_table, block_table_stride, seq_lens, num_seqs,
                                   max_seq_len, num_q_heads, scale, workspace, workspace_bytes,
                                   num_splits, 1, P, &a);
   if (st <= 0) return st;
+  // the new tokens sit past the prefix: the split over each request's
+  // suffix reads them from the input and stores them (the prefix pass reads
+  // prefix keys only)
+  a.fresh = fresh;
   pa::PrefillArgs p{};
   p.q = q;
   p.kv = kv_cache;
@@ -541,6 +548,43 @@ int pa_attention_decode_shared_prefix(void* out, const void* q, const void* kv_c
   const hipError_t e = pa::launch_fused(a, p, dtype, head_dim, group, s);
   if (e != hipSuccess) return PA_ERR_HIP;
   return hip_status(pa::launch_decode_merge(a, dtype, head_dim, group, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_attention_decode_shared_prefix(void* out, const void* q, const void* kv_cache,
+                                      int64_t num_blocks, int32_t block_size,
+                                      int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                                      const int32_t* block_table, int32_t block_table_stride,
+                                      const int32_t* seq_lens, int32_t num_seqs,
+                                      int32_t max_seq_len, int32_t num_q_heads, float scale,
+                                      int32_t shared_prefix_blocks, void* workspace,
+                                      size_t workspace_bytes, int32_t num_splits, void* stream) {
+  return shared_prefix_impl(out, q, kv_cache, num_blocks, block_size, num_kv_heads, head_dim,
+                            dtype, block_table, block_table_stride, seq_lens, num_seqs,
+                            max_seq_len, num_q_heads, scale, shared_prefix_blocks, workspace,
+                            workspace_bytes, num_splits, pa::NewTokens{}, stream);
+}
+
+int pa_cache_and_attend_decode_shared_prefix(
+    void* out, const void* q, const void* key, const void* value, void* kv_cache,
+    int64_t num_blocks, int32_t block_size, int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+    const int32_t* block_table, int32_t block_table_stride, const int32_t* seq_lens,
+    int64_t* slot_mapping, int32_t num_seqs, int32_t max_seq_len, int32_t num_q_heads,
+    float scale, int32_t shared_prefix_blocks, void* workspace, size_t workspace_bytes,
+    int32_t num_splits, void* stream) {
+  if (num_seqs > 0 && max_seq_len > 0 && !(key && value)) return PA_ERR_INVALID_ARG;
+  pa::NewTokens f{};
+  if (key || value) {
+    const int st = fresh_tokens(key, value, kv_cache, slot_mapping, &f);
+    if (st != PA_OK) return st;
+  }
+  return shared_prefix_impl(out, q, kv_cache, num_blocks, block_size, num_kv_heads, head_dim,
+                            dtype, block_table, block_table_stride, seq_lens, num_seqs,
+                            max_seq_len, num_q_heads, scale, shared_prefix_blocks, workspace,
+                            workspace_bytes, num_splits, f, stream);
 }
 
 }  // extern "C"

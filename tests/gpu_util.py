@@ -100,7 +100,8 @@ class Device:
                                      num_splits=num_splits)
 
 
-    def cache_and_attend(self, num_splits=0, force_mixed=False, slots=True):
+    def cache_and_attend(self, num_splits=0, force_mixed=False, slots=True,
+                         shared_prefix=None):
         """The one-launch step: the attention call stores the new tokens
         itself.  Returns (out, slot_mapping or None); the slot buffer starts
         at -7 so an entry the library does not write shows."""
@@ -109,7 +110,11 @@ class Device:
         w = self.w
         sm = (torch.full((w.num_tokens,), -7, dtype=torch.int64, device="cuda")
               if slots else None)
-        if w.is_decode_only and not force_mixed:
+        if shared_prefix is not None:
+            out = pa.pa_cache_and_attend_decode_shared_prefix(
+                self.q, self.k_new, self.v_new, self.kv, self.block_table, self.seq_lens,
+                w.scale, w.max_seq_len, shared_prefix, slot_mapping=sm, num_splits=num_splits)
+        elif w.is_decode_only and not force_mixed:
             out = pa.pa_cache_and_attend_decode(self.q, self.k_new, self.v_new, self.kv,
                                                 self.block_table, self.seq_lens, w.scale,
                                                 w.max_seq_len, slot_mapping=sm,
@@ -132,8 +137,8 @@ def run_step(w, *, poison=True, num_splits=0, force_mixed=False, shared_prefix=N
     pool = poisoned_pool(w) if poison else w.pool
     dev = Device(w, pool)
     if fused:
-        assert shared_prefix is None
-        out, slots = dev.cache_and_attend(num_splits=num_splits, force_mixed=force_mixed)
+        out, slots = dev.cache_and_attend(num_splits=num_splits, force_mixed=force_mixed,
+                                          shared_prefix=shared_prefix)
     else:
         slots = dev.slot_mapping()
         dev.scatter(slots)

@@ -262,6 +262,27 @@ def test_shared_prefix_checks():
     assert shared_prefix(R=0) == OK
 
 
+def test_cache_and_attend_shared_prefix_checks():
+    f = lib.pa_cache_and_attend_decode_shared_prefix
+
+    def call(**kw):
+        a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, kv=FAKE, NB=64, B=16, Hkv=2, D=64, dtype=1,
+                 bt=FAKE, stride=7, sl=FAKE, slots=None, R=4, L=100, Hq=4, scale=0.125, P=2,
+                 ws=FAKE_WS, wsb=1 << 30, S=0)
+        a.update(kw)
+        return f(a["out"], a["q"], a["k"], a["v"], a["kv"], a["NB"], a["B"], a["Hkv"], a["D"],
+                 a["dtype"], a["bt"], a["stride"], a["sl"], a["slots"], a["R"], a["L"], a["Hq"],
+                 a["scale"], a["P"], a["ws"], a["wsb"], a["S"], None)
+    assert call(k=None) == INVALID
+    assert call(v=ctypes.c_void_p(0x10008)) == INVALID          # not 16-byte aligned
+    assert call(P=-1) == INVALID
+    assert call(P=7) == INVALID                                  # prefix longer than L
+    assert call(q=None) == INVALID
+    assert call(ws=None) == WORKSPACE
+    assert call(B=8) == UNSUPPORTED
+    assert call(R=0, k=None, v=None) == OK
+
+
 def test_slot_mapping_checks():
     f = lib.pa_compute_slot_mapping
     assert f(None, FAKE, 7, FAKE, FAKE, 4, 4, 16, None) == INVALID

@@ -186,3 +186,40 @@ def test_prefill_chunk_2048_sampled():
     ref = oracle.paged_attention(sub.q, r_pool, sub.block_table, sub.seq_lens,
                                  sub.query_start_loc, sub.num_computed, w.scale, w.dtype)
     gu.check_close(w, out[rows], ref, what="prefill 2048 fused")
+
+
+# --------------------------------------------------------------------------
+# one-launch step of a batch sharing prefix blocks
+# --------------------------------------------------------------------------
+
+
+def test_shared_prefix_step_small():
+    w = workload("prefix_shared_small")
+    fused_check(w, shared_prefix=w.meta["shared_prefix_blocks"])
+
+
+@pytest.mark.parametrize("dtype,Hq,Hkv,D", [("bf16", 32, 8, 128), ("bf16", 8, 8, 128),
+                                            ("f16", 16, 2, 64), ("bf16", 8, 2, 64),
+                                            ("f32", 8, 2, 128)])
+def test_shared_prefix_step_edges(dtype, Hq, Hkv, D):
+    """New tokens right after a 5-block prefix (one suffix key), at every
+    row of a suffix block, in a partial and in a long suffix; split counts
+    auto, 1 and 3.  fp32 takes the plain one-launch decode."""
+    P = 5
+    lens = [P * 16 + 1, P * 16 + 2, P * 16 + 7, P * 16 + 16, P * 16 + 17, P * 16 + 300,
+            P * 16 + 33, 2000] + [P * 16 + 16 * k + k for k in range(1, 16)]
+    w = build_workload(f"sp1_{dtype}_{Hq}x{Hkv}x{D}", dtype=dtype, num_q_heads=Hq,
+                       num_kv_heads=Hkv, head_dim=D, num_blocks=900,
+                       requests=[(L - 1, 1) for L in lens], seed=301 + Hq + D,
+                       shared_prefix_blocks=P)
+    for splits in (0, 1, 3):
+        fused_check(w, shared_prefix=P, num_splits=splits)
+
+
+@pytest.mark.parametrize("seed", [None, 2004])
+def test_shared_prefix_step_full_config(seed):
+    """The 256-request batch sharing a 64-block prefix: slots and the whole
+    pool bit-exact, 32 sampled requests against the oracle, every output bit
+    for bit against the three calls."""
+    w = workload("prefix_shared_decode_bf16", seed)
+    fused_check(w, requests=list(range(0, 256, 8)), shared_prefix=w.meta["shared_prefix_blocks"])

@@ -306,7 +306,9 @@ def test_workspace_reused_across_calls():
     import torch
     cases = [(workload("decode_bf16_small"), 7), (workload("long_decode_small"), 0),
              (workload("decode_bf16_small"), 333), (workload("mixed_bf16_small"), 5),
-             (workload("long_decode_small"), 64)]
+             (workload("long_decode_small"), 64), (workload("tiny_f32_decode"), 0),
+             # a larger batch after small ones: its counters must still read zero
+             (workload("mixed_chunked_prefill_bf16"), 0), (workload("decode_bf16_small"), 0)]
     nbytes = max(pa.pa_attention_workspace_size(w.num_seqs, w.num_tokens, w.num_q_heads,
                                                 w.num_kv_heads, w.head_dim, w.max_seq_len,
                                                 w.max_query_len, s) for w, s in cases)
