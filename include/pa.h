@@ -123,8 +123,9 @@ int pa_copy_blocks(void* kv_cache, const int32_t* block_pairs, int32_t num_pairs
 /*
  * pa_attention_workspace_size -- bytes of fp32 scratch the attention calls
  * need for their split-KV partial results (max, sum, unnormalised output per
- * query head and partition).  Pure function of its arguments; returns 0 for
- * arguments the attention calls would reject.  `num_splits` = 0 selects the
+ * query head and partition).  A function of its arguments and of the current
+ * device's CU count (see pa_plan_decode_ranges); returns 0 for arguments the
+ * attention calls would reject.  `num_splits` = 0 selects the
  * library's own partition count; the size covers every plan the attention
  * calls may choose for these arguments.
  */
@@ -241,8 +242,8 @@ int pa_cache_and_attend_decode_shared_prefix(
  *   one other request, the tiles and the decode ranges are work-groups of
  *   one launch (one tile wave and one decode wave per SIMD), so the
  *   compute-bound and the bandwidth-bound halves overlap; the decode merge
- *   follows.  PA_MIXED_OVERLAP=0 in the environment launches them one after
- *   the other instead.  An fp32 cache has no matrix-core tiles: its chunks
+ *   follows (pa_attention_mixed_planned can keep them apart).  An fp32 cache
+ *   has no matrix-core tiles: its chunks
  *   are attended in fp32 on the vector ALU (16-token tiles), in a launch
  *   before the decode rows.
  *
@@ -348,6 +349,65 @@ int pa_cache_and_attend_mixed_no_workspace(
     const int32_t* num_computed_tokens, int64_t* slot_mapping, int32_t num_seqs,
     int32_t num_tokens, int32_t max_query_len, int32_t max_seq_len, int32_t num_q_heads,
     float scale, int32_t num_splits, void* stream);
+
+/*
+ * pa_attention_mixed_planned / pa_cache_and_attend_mixed_planned -- the
+ * mixed-batch calls with the work plan spelled out instead of chosen by the
+ * library (plan = NULL: the library's choice, as the plain calls).  Results
+ * are the same whatever the plan (to the tolerance of the attention; the
+ * cache and slots bit for bit); it changes only how the work is cut:
+ *   num_splits           as the plain calls' argument.
+ *   tile_shape           -1: library choice; 0: 16 query tokens per wave and
+ *                        two key parts per tile (short chunks); 1: 32 tokens
+ *                        per wave (long chunks).  Used when the tiles run in a
+ *                        launch of their own.
+ *   tiles_beside_decode  -1: library choice (one launch of tiles and decode
+ *                        ranges when the batch has both); 0: the tiles, then
+ *                        the decode rows, in launches of their own.
+ * Other fields out of range return PA_ERR_INVALID_ARG.  Other arguments as
+ * pa_attention_mixed / pa_cache_and_attend_mixed (whose num_splits the plan
+ * carries).
+ */
+typedef struct {
+  int32_t num_splits;
+  int32_t tile_shape;
+  int32_t tiles_beside_decode;
+} pa_mixed_plan;
+
+int pa_attention_mixed_planned(void* out, const void* q, const void* kv_cache,
+                               int64_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t dtype, const int32_t* block_table,
+                               int32_t block_table_stride, const int32_t* seq_lens,
+                               const int32_t* query_start_loc,
+                               const int32_t* num_computed_tokens, int32_t num_seqs,
+                               int32_t num_tokens, int32_t max_query_len, int32_t max_seq_len,
+                               int32_t num_q_heads, float scale, void* workspace,
+                               size_t workspace_bytes, const pa_mixed_plan* plan, void* stream);
+
+int pa_cache_and_attend_mixed_planned(
+    void* out, const void* q, const void* key, const void* value, void* kv_cache,
+    int64_t num_blocks, int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+    int32_t dtype, const int32_t* block_table, int32_t block_table_stride,
+    const int32_t* seq_lens, const int32_t* query_start_loc,
+    const int32_t* num_computed_tokens, int64_t* slot_mapping, int32_t num_seqs,
+    int32_t num_tokens, int32_t max_query_len, int32_t max_seq_len, int32_t num_q_heads,
+    float scale, void* workspace, size_t workspace_bytes, const pa_mixed_plan* plan,
+    void* stream);
+
+/*
+ * pa_plan_decode_ranges -- the split the attention calls would plan on a
+ * device with `num_cus` compute units: key ranges per KV head for the decode
+ * rows (one wavefront per SIMD, i.e. 4 per CU, beside concurrent prefill
+ * tiles the wave slots those leave; no range shorter than 4 blocks).  The
+ * calls themselves read the current device's CU and XCD counts (hipGetDevice,
+ * hipDeviceGetAttribute; 256 and 8 when no device answers), and so does
+ * pa_attention_workspace_size: compute a workspace size with the device
+ * current that the calls will run on.  Pure function; returns the range
+ * count, or a negative pa_status for arguments the calls would reject.
+ */
+int pa_plan_decode_ranges(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t dtype, int32_t max_seq_len,
+                          int32_t max_query_len, int32_t num_splits, int32_t num_cus);
 
 /*
  * pa_check_metadata -- check, on the device, the step metadata the calls

@@ -22,6 +22,7 @@ __all__ = [
     "pa_cache_and_attend_decode_shared_prefix",
     "pa_cache_and_attend_mixed_no_workspace", "NO_WORKSPACE_MAX_BYTES",
     "pa_check_metadata", "META_FLAGS", "pa_status_string", "pa_version", "pa_read_probe",
+    "pa_plan_decode_ranges",
     # short names: host bounds read back from the device when not given
     "compute_slot_mapping", "reshape_and_cache", "copy_blocks", "attention_decode",
     "attention_mixed", "cache_and_attend_decode", "cache_and_attend_mixed",
@@ -108,6 +109,19 @@ lib.pa_check_metadata.argtypes = [
     _i32, _i32, _i32, _i32, _i64, _i32, _i32,  # R T max_q max_L NB B prefix_blocks
     _vp]
 lib.pa_check_metadata.restype = ctypes.c_int
+
+class _MixedPlan(ctypes.Structure):
+    _fields_ = [("num_splits", _i32), ("tile_shape", _i32), ("tiles_beside_decode", _i32)]
+
+
+lib.pa_attention_mixed_planned.argtypes = lib.pa_attention_mixed.argtypes[:-2] + [
+    ctypes.POINTER(_MixedPlan), _vp]
+lib.pa_attention_mixed_planned.restype = ctypes.c_int
+lib.pa_cache_and_attend_mixed_planned.argtypes = lib.pa_cache_and_attend_mixed.argtypes[:-2] + [
+    ctypes.POINTER(_MixedPlan), _vp]
+lib.pa_cache_and_attend_mixed_planned.restype = ctypes.c_int
+lib.pa_plan_decode_ranges.argtypes = [_i32] * 9
+lib.pa_plan_decode_ranges.restype = ctypes.c_int
 
 lib.pa_read_probe.argtypes = [_vp, _sz, _vp, _i32, _vp]
 lib.pa_read_probe.restype = ctypes.c_int
@@ -294,10 +308,23 @@ def pa_attention_decode_shared_prefix(q, kv_cache, block_table, seq_lens, scale:
     return out
 
 
+def _plan(num_splits, tile_shape, tiles_beside_decode):
+    """A pa_mixed_plan, or None when the library chooses everything but the
+    split count (the plain entry points)."""
+    if tile_shape is None and tiles_beside_decode is None:
+        return None
+    return _MixedPlan(int(num_splits), -1 if tile_shape is None else int(tile_shape),
+                      -1 if tiles_beside_decode is None else int(tiles_beside_decode))
+
+
 def pa_attention_mixed(q, kv_cache, block_table, seq_lens, query_start_loc,
                        num_computed_tokens, scale: float, max_query_len: int,
-                       max_seq_len: int, out=None, workspace=None, num_splits: int = 0):
-    """Chunked-prefill mixed batch: q [T, Hq, D] varlen-packed -> out; see pa.h."""
+                       max_seq_len: int, out=None, workspace=None, num_splits: int = 0,
+                       tile_shape: Optional[int] = None,
+                       tiles_beside_decode: Optional[int] = None):
+    """Chunked-prefill mixed batch: q [T, Hq, D] varlen-packed -> out; see pa.h.
+    ``tile_shape`` / ``tiles_beside_decode`` spell out the plan
+    (pa_attention_mixed_planned); None leaves them to the library."""
     torch = _torch()
     nb, bs, hkv, d = _cache_dims(kv_cache)
     T, hq = int(q.shape[0]), int(q.shape[1])
@@ -308,15 +335,20 @@ def pa_attention_mixed(q, kv_cache, block_table, seq_lens, query_start_loc,
         out = torch.empty_like(q)
     need = pa_attention_workspace_size(R, T, hq, hkv, d, max_seq_len, max_query_len, num_splits)
     ws = _workspace(need, q.device, workspace)
-    st = lib.pa_attention_mixed(
-        _dev(out, "out"), _dev(q, "q"), _dev(kv_cache, "kv_cache"), nb, bs, hkv, d,
-        _dtype_code(kv_cache), _dev(block_table, "block_table", torch.int32, 2),
-        int(block_table.shape[1]), _dev(seq_lens, "seq_lens", torch.int32, 1),
-        _dev(query_start_loc, "query_start_loc", torch.int32, 1),
-        _dev(num_computed_tokens, "num_computed_tokens", torch.int32, 1), R, T,
-        int(max_query_len), int(max_seq_len), hq, float(scale), _dev(ws, "workspace"),
-        ws.numel() * ws.element_size(), int(num_splits), _stream())
-    _check("pa_attention_mixed", st)
+    args = (_dev(out, "out"), _dev(q, "q"), _dev(kv_cache, "kv_cache"), nb, bs, hkv, d,
+            _dtype_code(kv_cache), _dev(block_table, "block_table", torch.int32, 2),
+            int(block_table.shape[1]), _dev(seq_lens, "seq_lens", torch.int32, 1),
+            _dev(query_start_loc, "query_start_loc", torch.int32, 1),
+            _dev(num_computed_tokens, "num_computed_tokens", torch.int32, 1), R, T,
+            int(max_query_len), int(max_seq_len), hq, float(scale), _dev(ws, "workspace"),
+            ws.numel() * ws.element_size())
+    plan = _plan(num_splits, tile_shape, tiles_beside_decode)
+    if plan is None:
+        st = lib.pa_attention_mixed(*args, int(num_splits), _stream())
+        _check("pa_attention_mixed", st)
+    else:
+        st = lib.pa_attention_mixed_planned(*args, ctypes.byref(plan), _stream())
+        _check("pa_attention_mixed_planned", st)
     return out
 
 
@@ -396,9 +428,11 @@ def pa_cache_and_attend_decode_shared_prefix(q, key, value, kv_cache, block_tabl
 def pa_cache_and_attend_mixed(q, key, value, kv_cache, block_table, seq_lens, query_start_loc,
                               num_computed_tokens, scale: float, max_query_len: int,
                               max_seq_len: int, out=None, slot_mapping=None, workspace=None,
-                              num_splits: int = 0):
+                              num_splits: int = 0, tile_shape: Optional[int] = None,
+                              tiles_beside_decode: Optional[int] = None):
     """Mixed step in one launch: stores key/value [T, Hkv, D] of every new
-    token by its slot and attends; see pa.h."""
+    token by its slot and attends; see pa.h.  The plan arguments as
+    pa_attention_mixed."""
     torch = _torch()
     nb, bs, hkv, d = _cache_dims(kv_cache)
     T, hq = int(q.shape[0]), int(q.shape[1])
@@ -409,18 +443,35 @@ def pa_cache_and_attend_mixed(q, key, value, kv_cache, block_table, seq_lens, qu
         out = torch.empty_like(q)
     need = pa_attention_workspace_size(R, T, hq, hkv, d, max_seq_len, max_query_len, num_splits)
     ws = _workspace(need, q.device, workspace)
-    st = lib.pa_cache_and_attend_mixed(
-        _dev(out, "out"), _dev(q, "q"), _new_rows(key, "key", T, hkv, d, kv_cache),
-        _new_rows(value, "value", T, hkv, d, kv_cache), _dev(kv_cache, "kv_cache"), nb, bs,
-        hkv, d, _dtype_code(kv_cache), _dev(block_table, "block_table", torch.int32, 2),
-        int(block_table.shape[1]), _dev(seq_lens, "seq_lens", torch.int32, 1),
-        _dev(query_start_loc, "query_start_loc", torch.int32, 1),
-        _dev(num_computed_tokens, "num_computed_tokens", torch.int32, 1),
-        _slots_out(slot_mapping, T), R, T, int(max_query_len), int(max_seq_len), hq,
-        float(scale), _dev(ws, "workspace"), ws.numel() * ws.element_size(), int(num_splits),
-        _stream())
-    _check("pa_cache_and_attend_mixed", st)
+    args = (_dev(out, "out"), _dev(q, "q"), _new_rows(key, "key", T, hkv, d, kv_cache),
+            _new_rows(value, "value", T, hkv, d, kv_cache), _dev(kv_cache, "kv_cache"), nb, bs,
+            hkv, d, _dtype_code(kv_cache), _dev(block_table, "block_table", torch.int32, 2),
+            int(block_table.shape[1]), _dev(seq_lens, "seq_lens", torch.int32, 1),
+            _dev(query_start_loc, "query_start_loc", torch.int32, 1),
+            _dev(num_computed_tokens, "num_computed_tokens", torch.int32, 1),
+            _slots_out(slot_mapping, T), R, T, int(max_query_len), int(max_seq_len), hq,
+            float(scale), _dev(ws, "workspace"), ws.numel() * ws.element_size())
+    plan = _plan(num_splits, tile_shape, tiles_beside_decode)
+    if plan is None:
+        st = lib.pa_cache_and_attend_mixed(*args, int(num_splits), _stream())
+        _check("pa_cache_and_attend_mixed", st)
+    else:
+        st = lib.pa_cache_and_attend_mixed_planned(*args, ctypes.byref(plan), _stream())
+        _check("pa_cache_and_attend_mixed_planned", st)
     return out
+
+
+def pa_plan_decode_ranges(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                          dtype: str, max_seq_len: int, max_query_len: int = 1,
+                          num_splits: int = 0, num_cus: int = 256) -> int:
+    """Key ranges per KV head the split plans on a device of `num_cus`
+    compute units (a pure query; see pa.h)."""
+    st = lib.pa_plan_decode_ranges(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                   DTYPE_CODES[dtype], max_seq_len, max_query_len, num_splits,
+                                   num_cus)
+    if st < 0:
+        raise PAError("pa_plan_decode_ranges", st)
+    return st
 
 
 def pa_cache_and_attend_mixed_no_workspace(q, key, value, kv_cache, block_table, seq_lens,

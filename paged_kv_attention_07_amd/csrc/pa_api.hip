@@ -2,7 +2,6 @@
 // The public contract of every function is documented in include/pa.h.
 #include <math.h>
 #include <stdint.h>
-#include <stdlib.h>
 
 #include <mutex>
 
@@ -13,20 +12,63 @@ namespace {
 
 constexpr int kVersion = 100;  // 0.1.0
 
-// Partition plan for the balanced split: one wavefront per SIMD (256 CUs x
-// 4; one work-group of 4 waves per CU), but no range shorter than a few
-// blocks.  With each wave keeping its next block in flight this reads HBM
-// faster than two waves per SIMD on every batch of private sequences
-// measured (16-512 requests, 256-8192 keys: 2-4%); the extra waves paid only
-// on a batch whose blocks are mostly shared, i.e. read from cache, which the
-// shared-prefix entry plans for itself.  Beside concurrent prefill tiles the
-// decode rows take the slots the tiles leave: the chip's 2048 wave slots
-// minus the tiles of the longest chunk (a lower bound on the tile count),
-// between one and one and a half waves per SIMD.
-constexpr int kTargetWaves = 256 * 4;
-constexpr int kWaveSlots = 256 * 8;
-constexpr int kMinWavesBesidePrefill = 256 * 4;
-constexpr int kMaxWavesBesidePrefill = 256 * 6;
+// Geometry of the device a call runs on: compute units and XCDs (dies, each
+// with its own L2).  The kernels hold 4 waves per work-group and at most two
+// waves per SIMD (their register budget), so a CU has 4 SIMDs x 2 = 8 wave
+// slots.
+struct Geometry {
+  int cus, xcds;
+};
+constexpr Geometry kDefaultGeometry = {256, 8};  // MI355X, used when no device answers
+
+std::mutex g_geo_mu;
+Geometry g_geo[64];
+bool g_geo_known[64];
+
+// The current device's geometry, read once per device.
+Geometry device_geometry() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return kDefaultGeometry;
+  std::lock_guard<std::mutex> lock(g_geo_mu);
+  if (!g_geo_known[dev]) {
+    Geometry g = kDefaultGeometry;
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        v > 0)
+      g.cus = v;
+    v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeNumberOfXccs, dev) == hipSuccess && v > 0)
+      g.xcds = v;
+    g_geo[dev] = g;
+    g_geo_known[dev] = true;
+  }
+  return g_geo[dev];
+}
+
+// A caller's plan for a mixed batch (pa_mixed_plan); -1 fields are the
+// library's choice.
+struct Plan {
+  int num_splits = 0;
+  int tile_shape = -1;
+  int tiles_beside_decode = -1;
+};
+
+Plan splits_plan(int num_splits) {
+  Plan p;
+  p.num_splits = num_splits;
+  return p;
+}
+
+// Partition plan for the balanced split: one wavefront per SIMD (one
+// work-group of 4 waves per CU), but no range shorter than a few blocks.
+// With each wave keeping its next block in flight this reads HBM faster than
+// two waves per SIMD on every batch of private sequences measured (16-512
+// requests, 256-8192 keys: 2-4%); the extra waves paid only on a batch whose
+// blocks are mostly shared, i.e. read from cache, which the shared-prefix
+// entry plans for itself.  Beside concurrent prefill tiles the decode rows
+// take the slots the tiles leave: the chip's wave slots (8 per CU) minus the
+// tiles of the longest chunk (a lower bound on the tile count), between one
+// and one and a half waves per SIMD.
 constexpr int kMinBlocksPerRange = 4;
 
 // query heads per wave of the matrix-core prefill tiles
@@ -42,13 +84,12 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-bool overlap_enabled();
-
 // Matrix-core prefill tiles run beside the decode rows when the batch can
-// hold both: a chunk (max_query_len > 1) and at least one other request.
-// fp32 tiles (vector ALU) run before the decode rows instead.
-bool tiles_beside_decode(int num_seqs, int max_query_len, int dtype) {
-  return max_query_len > 1 && num_seqs >= 2 && dtype != PA_F32 && overlap_enabled();
+// hold both (a chunk, max_query_len > 1, and at least one other request) and
+// the plan does not keep them apart.  fp32 tiles (vector ALU) run before the
+// decode rows instead.
+bool tiles_beside_decode(int num_seqs, int max_query_len, int dtype, const Plan& plan) {
+  return max_query_len > 1 && num_seqs >= 2 && dtype != PA_F32 && plan.tiles_beside_decode != 0;
 }
 
 // Decode waves beside the tiles of a chunk of up to max_query_len tokens
@@ -56,33 +97,33 @@ bool tiles_beside_decode(int num_seqs, int max_query_len, int dtype) {
 // tokens per tile).  With exact_tiles (the shared-prefix pass: one virtual
 // request of exactly max_query_len rows) the tiles and the decode waves fill
 // the chip's wave slots exactly, so every CU holds the same number of
-// work-groups (2048 - tile waves, at least 1024); otherwise the tile count
-// is only a lower bound and the decode waves stay within 1024-1536.
-int64_t waves_beside_prefill(int num_kv_heads, int group, int max_query_len,
-                             bool exact_tiles) {
+// work-groups (slots - tile waves, at least 4 per CU); otherwise the tile
+// count is only a lower bound and the decode waves stay within 4-6 per CU.
+int64_t waves_beside_prefill(int num_kv_heads, int group, int max_query_len, bool exact_tiles,
+                             int cus) {
   const int wpw = heads_per_wave(group);
   const int64_t qt = 32 * (4 / wpw);
   const int64_t tile_waves = 4 * ceil_div(max_query_len, qt) * num_kv_heads * (group / wpw);
-  int64_t w = kWaveSlots - tile_waves;
-  if (w < kMinWavesBesidePrefill) w = kMinWavesBesidePrefill;
-  if (!exact_tiles && w > kMaxWavesBesidePrefill) w = kMaxWavesBesidePrefill;
+  int64_t w = (int64_t)cus * 8 - tile_waves;
+  if (w < (int64_t)cus * 4) w = (int64_t)cus * 4;
+  if (!exact_tiles && w > (int64_t)cus * 6) w = (int64_t)cus * 6;
   return w;
 }
 
-// Ranges per KV head.  dtype and head_dim set the waves per GQA group; the
-// workspace-size queries, which have no dtype, plan with PA_BF16: its waves
-// serve the most heads each, so its plan has the most ranges and bounds the
-// others.
+// Ranges per KV head on a device of `cus` compute units.  dtype and head_dim
+// set the waves per GQA group; the workspace-size queries, which have no
+// dtype, plan with PA_BF16: its waves serve the most heads each, so its plan
+// has the most ranges and bounds the others.
 int plan_chunks(int num_seqs, int num_kv_heads, int group, int max_seq_len, int num_splits,
-                bool beside_prefill, int max_query_len, int dtype, int head_dim,
+                bool beside_prefill, int max_query_len, int dtype, int head_dim, int cus,
                 bool exact_tiles = false) {
   if (num_splits > 0) return num_splits;
   const int hg = group / pa::decode_heads_per_wave(dtype, head_dim, group);
   const int64_t blocks_upper = (int64_t)num_seqs * ceil_div(max_seq_len, pa::kBlockSize);
   const int64_t waves = beside_prefill
                             ? waves_beside_prefill(num_kv_heads, group, max_query_len,
-                                                   exact_tiles)
-                            : kTargetWaves;
+                                                   exact_tiles, cus)
+                            : (int64_t)cus * 4;
   int64_t n = ceil_div(waves, (int64_t)num_kv_heads * hg);
   const int64_t cap = ceil_div(blocks_upper, kMinBlocksPerRange);
   if (n > cap) n = cap;
@@ -126,10 +167,6 @@ int check_heads(int32_t num_q_heads, int32_t num_kv_heads) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
 
-bool overlap_enabled() {
-  const char* v = getenv("PA_MIXED_OVERLAP");
-  return !(v && v[0] == '0');
-}
 
 }  // namespace
 
@@ -205,12 +242,12 @@ size_t pa_attention_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t
   // the buffer serves either call; beside tiles, for the shortest chunk (2
   // tokens), which leaves the decode rows the most waves: a call may pass any
   // max_query_len up to the one given here
-  const int alone =
-      plan_chunks(num_seqs, num_kv_heads, group, max_seq_len, num_splits, false, 0, PA_BF16,
-                  head_dim);
+  const int cus = device_geometry().cus;
+  const int alone = plan_chunks(num_seqs, num_kv_heads, group, max_seq_len, num_splits, false,
+                                0, PA_BF16, head_dim, cus);
   const int beside =
       max_query_len > 1 ? plan_chunks(num_seqs, num_kv_heads, group, max_seq_len, num_splits,
-                                      true, 2, PA_BF16, head_dim)
+                                      true, 2, PA_BF16, head_dim, cus)
                         : 0;
   const int chunks = alone > beside ? alone : beside;
   return workspace_layout(num_seqs, num_q_heads, head_dim, chunks).total;
@@ -221,7 +258,7 @@ static int attention_common(void* out, const void* q, const void* kv_cache, int6
                             int32_t dtype, const int32_t* block_table, int32_t bt_stride,
                             const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len,
                             int32_t num_q_heads, float scale, void* workspace,
-                            size_t workspace_bytes, int32_t num_splits, int32_t max_query_len,
+                            size_t workspace_bytes, const Plan& plan, int32_t max_query_len,
                             int32_t shared_prefix_blocks, pa::DecodeArgs* a,
                             int (*scratch)(void**, size_t*) = nullptr,
                             bool launches = true) {
@@ -229,6 +266,7 @@ static int attention_common(void* out, const void* q, const void* kv_cache, int6
   if (st != PA_OK) return st;
   st = check_heads(num_q_heads, num_kv_heads);
   if (st != PA_OK) return st;
+  const int num_splits = plan.num_splits;
   if (num_seqs < 0 || max_seq_len < 0 || bt_stride < 0 || num_splits < 0) return PA_ERR_INVALID_ARG;
   if (!isfinite(scale)) return PA_ERR_INVALID_ARG;
   if (num_seqs == 0) return PA_OK;
@@ -240,11 +278,12 @@ static int attention_common(void* out, const void* q, const void* kv_cache, int6
   // with a shared prefix the split covers the keys after it, beside the
   // prefix pass, and R more slots hold the prefix partials
   const int P = shared_prefix_blocks;
-  const int chunks = plan_chunks(num_seqs, num_kv_heads, group,
-                                 P > 0 ? max(max_seq_len - P * pa::kBlockSize, 1) : max_seq_len,
-                                 num_splits,
-                                 P > 0 || tiles_beside_decode(num_seqs, max_query_len, dtype),
-                                 P > 0 ? num_seqs : max_query_len, dtype, head_dim, P > 0);
+  const int chunks =
+      plan_chunks(num_seqs, num_kv_heads, group,
+                  P > 0 ? max(max_seq_len - P * pa::kBlockSize, 1) : max_seq_len, num_splits,
+                  P > 0 || tiles_beside_decode(num_seqs, max_query_len, dtype, plan),
+                  P > 0 ? num_seqs : max_query_len, dtype, head_dim, device_geometry().cus,
+                  P > 0);
   const WsLayout lay = workspace_layout(num_seqs, num_q_heads, head_dim,
                                         chunks + (P > 0 ? num_seqs : 0));
   if (launches) {
@@ -303,11 +342,13 @@ int decode_impl(void* out, const void* q, const void* kv_cache, int64_t num_bloc
                 int32_t num_seqs, int32_t max_seq_len, int32_t num_q_heads, float scale,
                 void* workspace, size_t workspace_bytes, int32_t num_splits,
                 const pa::NewTokens& fresh, void* stream) {
+  Plan plan;
+  plan.num_splits = num_splits;
   pa::DecodeArgs a{};
   const int st = attention_common(out, q, kv_cache, num_blocks, block_size, num_kv_heads, head_dim,
                                   dtype, block_table, block_table_stride, seq_lens, num_seqs,
                                   max_seq_len, num_q_heads, scale, workspace, workspace_bytes,
-                                  num_splits, 1, 0, &a);
+                                  plan, 1, 0, &a);
   if (st <= 0) return st;
   a.fresh = fresh;
   return hip_status(pa::launch_decode(a, dtype, head_dim, num_q_heads / num_kv_heads,
@@ -320,8 +361,11 @@ int mixed_impl(void* out, const void* q, const void* kv_cache, int64_t num_block
                const int32_t* query_start_loc, const int32_t* num_computed_tokens,
                int32_t num_seqs, int32_t num_tokens, int32_t max_query_len, int32_t max_seq_len,
                int32_t num_q_heads, float scale, void* workspace, size_t workspace_bytes,
-               int32_t num_splits, const pa::NewTokens& fresh, void* stream,
+               const Plan& plan, const pa::NewTokens& fresh, void* stream,
                int (*scratch)(void**, size_t*) = nullptr) {
+  if (plan.tile_shape < -1 || plan.tile_shape > 1 || plan.tiles_beside_decode < -1 ||
+      plan.tiles_beside_decode > 1)
+    return PA_ERR_INVALID_ARG;
   if (num_tokens < 0 || max_query_len < 0) return PA_ERR_INVALID_ARG;
   // metadata pointers are checked before the workspace, whichever supplies it
   if (num_seqs > 0 && num_tokens > 0 && (!query_start_loc || !num_computed_tokens))
@@ -330,7 +374,7 @@ int mixed_impl(void* out, const void* q, const void* kv_cache, int64_t num_block
   const int st = attention_common(out, q, kv_cache, num_blocks, block_size, num_kv_heads, head_dim,
                                   dtype, block_table, block_table_stride, seq_lens, num_seqs,
                                   max_seq_len, num_q_heads, scale, workspace, workspace_bytes,
-                                  num_splits, max_query_len, 0, &a, scratch, num_tokens > 0);
+                                  plan, max_query_len, 0, &a, scratch, num_tokens > 0);
   if (st <= 0) return st;
   if (num_tokens == 0) return PA_OK;
   if (!query_start_loc || !num_computed_tokens) return PA_ERR_INVALID_ARG;
@@ -353,9 +397,11 @@ int mixed_impl(void* out, const void* q, const void* kv_cache, int64_t num_block
     p.num_q_heads = num_q_heads;
     p.max_tiles = (int)(ceil_div(num_tokens, pa::kQueriesPerTile) + num_seqs);
     p.max_query_len = max_query_len;
+    p.tile_shape = plan.tile_shape;
+    p.num_xcds = device_geometry().xcds;
     p.scale_log2 = a.scale_log2;
     p.fresh = fresh;
-    if (tiles_beside_decode(num_seqs, max_query_len, dtype)) {
+    if (tiles_beside_decode(num_seqs, max_query_len, dtype, plan)) {
       // tiles and decode ranges in one launch, then the merge
       p.beside_decode = 1;
       const hipError_t e = pa::launch_fused(a, p, dtype, head_dim, group, s);
@@ -397,8 +443,8 @@ int pa_attention_mixed(void* out, const void* q, const void* kv_cache, int64_t n
   return mixed_impl(out, q, kv_cache, num_blocks, block_size, num_kv_heads, head_dim, dtype,
                     block_table, block_table_stride, seq_lens, query_start_loc,
                     num_computed_tokens, num_seqs, num_tokens, max_query_len, max_seq_len,
-                    num_q_heads, scale, workspace, workspace_bytes, num_splits, pa::NewTokens{},
-                    stream);
+                    num_q_heads, scale, workspace, workspace_bytes, splits_plan(num_splits),
+                    pa::NewTokens{}, stream);
 }
 
 int pa_cache_and_attend_decode(void* out, const void* q, const void* key, const void* value,
@@ -439,7 +485,74 @@ int pa_cache_and_attend_mixed(void* out, const void* q, const void* key, const v
   return mixed_impl(out, q, kv_cache, num_blocks, block_size, num_kv_heads, head_dim, dtype,
                     block_table, block_table_stride, seq_lens, query_start_loc,
                     num_computed_tokens, num_seqs, num_tokens, max_query_len, max_seq_len,
-                    num_q_heads, scale, workspace, workspace_bytes, num_splits, f, stream);
+                    num_q_heads, scale, workspace, workspace_bytes, splits_plan(num_splits), f,
+                    stream);
+}
+
+static int plan_from(const pa_mixed_plan* plan, Plan* out) {
+  if (plan) {
+    out->num_splits = plan->num_splits;
+    out->tile_shape = plan->tile_shape;
+    out->tiles_beside_decode = plan->tiles_beside_decode;
+  }
+  return PA_OK;
+}
+
+int pa_attention_mixed_planned(void* out, const void* q, const void* kv_cache,
+                               int64_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t dtype, const int32_t* block_table,
+                               int32_t block_table_stride, const int32_t* seq_lens,
+                               const int32_t* query_start_loc,
+                               const int32_t* num_computed_tokens, int32_t num_seqs,
+                               int32_t num_tokens, int32_t max_query_len, int32_t max_seq_len,
+                               int32_t num_q_heads, float scale, void* workspace,
+                               size_t workspace_bytes, const pa_mixed_plan* plan,
+                               void* stream) {
+  Plan p;
+  plan_from(plan, &p);
+  return mixed_impl(out, q, kv_cache, num_blocks, block_size, num_kv_heads, head_dim, dtype,
+                    block_table, block_table_stride, seq_lens, query_start_loc,
+                    num_computed_tokens, num_seqs, num_tokens, max_query_len, max_seq_len,
+                    num_q_heads, scale, workspace, workspace_bytes, p, pa::NewTokens{}, stream);
+}
+
+int pa_cache_and_attend_mixed_planned(
+    void* out, const void* q, const void* key, const void* value, void* kv_cache,
+    int64_t num_blocks, int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+    int32_t dtype, const int32_t* block_table, int32_t block_table_stride,
+    const int32_t* seq_lens, const int32_t* query_start_loc,
+    const int32_t* num_computed_tokens, int64_t* slot_mapping, int32_t num_seqs,
+    int32_t num_tokens, int32_t max_query_len, int32_t max_seq_len, int32_t num_q_heads,
+    float scale, void* workspace, size_t workspace_bytes, const pa_mixed_plan* plan,
+    void* stream) {
+  if (num_tokens > 0 && !(key && value)) return PA_ERR_INVALID_ARG;
+  pa::NewTokens f{};
+  if (key || value) {
+    const int st = fresh_tokens(key, value, kv_cache, slot_mapping, &f);
+    if (st != PA_OK) return st;
+  }
+  Plan p;
+  plan_from(plan, &p);
+  return mixed_impl(out, q, kv_cache, num_blocks, block_size, num_kv_heads, head_dim, dtype,
+                    block_table, block_table_stride, seq_lens, query_start_loc,
+                    num_computed_tokens, num_seqs, num_tokens, max_query_len, max_seq_len,
+                    num_q_heads, scale, workspace, workspace_bytes, p, f, stream);
+}
+
+int pa_plan_decode_ranges(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t dtype, int32_t max_seq_len,
+                          int32_t max_query_len, int32_t num_splits, int32_t num_cus) {
+  if (num_seqs <= 0 || num_kv_heads <= 0 || max_seq_len <= 0 || max_query_len < 0 ||
+      num_splits < 0 || num_cus <= 0)
+    return PA_ERR_INVALID_ARG;
+  if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (!dtype_ok(dtype)) return PA_ERR_UNSUPPORTED;
+  const int st = check_heads(num_q_heads, num_kv_heads);
+  if (st != PA_OK) return st;
+  const int group = num_q_heads / num_kv_heads;
+  return plan_chunks(num_seqs, num_kv_heads, group, max_seq_len, num_splits,
+                     tiles_beside_decode(num_seqs, max_query_len, dtype, Plan{}), max_query_len,
+                     dtype, head_dim, num_cus);
 }
 
 int pa_check_metadata(uint32_t* flags, const int32_t* block_table, int32_t block_table_stride,
@@ -489,7 +602,7 @@ size_t pa_attention_decode_shared_prefix_workspace_size(int32_t num_seqs, int32_
   const int group = num_q_heads / num_kv_heads;
   const int rest = max(max_seq_len - shared_prefix_blocks * pa::kBlockSize, 1);
   const int chunks = plan_chunks(num_seqs, num_kv_heads, group, rest, num_splits, true, num_seqs,
-                                 PA_BF16, head_dim, true);
+                                 PA_BF16, head_dim, device_geometry().cus, true);
   const size_t casc = workspace_layout(num_seqs, num_q_heads, head_dim, chunks + num_seqs).total;
   return casc > plain ? casc : plain;
 }
@@ -519,7 +632,7 @@ int shared_prefix_impl(void* out, const void* q, const void* kv_cache, int64_t n
   const int st = attention_common(out, q, kv_cache, num_blocks, block_size, num_kv_heads, head_dim,
                                   dtype, block_table, block_table_stride, seq_lens, num_seqs,
                                   max_seq_len, num_q_heads, scale, workspace, workspace_bytes,
-                                  num_splits, 1, P, &a);
+                                  splits_plan(num_splits), 1, P, &a);
   if (st <= 0) return st;
   // the new tokens sit past the prefix: the split over each request's
   // suffix reads them from the input and stores them (the prefix pass reads
@@ -536,6 +649,8 @@ int shared_prefix_impl(void* out, const void* q, const void* kv_cache, int64_t n
   p.max_tiles = (int)ceil_div(num_seqs, pa::kQueriesPerTile) + 1;
   p.max_query_len = num_seqs;
   p.beside_decode = 1;
+  p.tile_shape = -1;
+  p.num_xcds = device_geometry().xcds;
   p.scale_log2 = a.scale_log2;
   p.cascade_rows = num_seqs;
   p.cascade_keys = P * pa::kBlockSize;
@@ -644,5 +759,6 @@ extern "C" int pa_cache_and_attend_mixed_no_workspace(
   return mixed_impl(out, q, kv_cache, num_blocks, block_size, num_kv_heads, head_dim, dtype,
                     block_table, block_table_stride, seq_lens, query_start_loc,
                     num_computed_tokens, num_seqs, num_tokens, max_query_len, max_seq_len,
-                    num_q_heads, scale, nullptr, 0, num_splits, f, stream, scratch_address);
+                    num_q_heads, scale, nullptr, 0, splits_plan(num_splits), f, stream,
+                    scratch_address);
 }

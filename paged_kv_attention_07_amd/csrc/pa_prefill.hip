@@ -1,7 +1,5 @@
 // Tile-shape choice and launchers of the prefill tile kernel (device code
 // in pa_prefill_impl.h).
-#include <stdlib.h>
-
 #include "pa_prefill_impl.h"
 
 namespace pa {
@@ -14,12 +12,9 @@ namespace {
 //      fragment read from LDS feeds two products), and tiles running beside
 //      concurrent decode rows (a 4-wave work-group fits next to one decode
 //      wave per SIMD).
-// PA_PREFILL_SHAPE=0|1 overrides the choice (a tuning and testing knob).
+// A caller's plan may force either (tile_shape 0 | 1).
 int choose_shape(const PrefillArgs& a) {
-  if (const char* env = getenv("PA_PREFILL_SHAPE")) {
-    const int v = atoi(env);
-    if (v == 0 || v == 1) return v;
-  }
+  if (a.tile_shape == 0 || a.tile_shape == 1) return a.tile_shape;
   return (a.beside_decode || a.max_query_len >= 1024) ? 1 : 0;
 }
 

@@ -39,7 +39,6 @@ namespace pa {
 namespace {
 
 constexpr int kTileTokens = 16;  // query tokens per work-group
-constexpr int kXcds = 8;         // accelerator dies of the chip, each with its own L2
 
 // Request and tile (index within the request) owned by work-group `bx`:
 // requests with more than one query token contribute ceil(qlen / 16) tiles
@@ -90,8 +89,9 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(PrefillArgs a) {
   const int tiles = gridDim.x;
   const int total = tiles * gridDim.y;
   const int lin = blockIdx.y * tiles + blockIdx.x;
-  const int xcd = lin % kXcds, local = lin / kXcds;
-  const int idx = xcd * (total / kXcds) + min(xcd, total % kXcds) + local;
+  const int nx = a.num_xcds;       // the device's dies, each with its own L2
+  const int xcd = lin % nx, local = lin / nx;
+  const int idx = xcd * (total / nx) + min(xcd, total % nx) + local;
   const int h = idx / tiles;
   if (tid < kWave) {
     int r, t;

@@ -63,7 +63,6 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 }
 
 constexpr int kKeysPerIter = 64;  // keys staged per iteration (4 paged blocks)
-constexpr int kXcds = 8;          // accelerator dies of the chip, each with its own L2
 
 template <int D>
 struct TileShape {
@@ -566,15 +565,16 @@ __device__ __forceinline__ void prefill_tile_body(const PrefillArgs& a, int bx, 
 
 template <typename E, int D, int WPW, int NT, int KSPLIT>
 __global__ __launch_bounds__(256 * KSPLIT) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_tile_kernel(PrefillArgs a) {
-  // XCD-aware numbering.  Work-groups are handed to the 8 XCDs in turn
-  // (linear index x fastest); renumber them so that each XCD runs one
+  // XCD-aware numbering.  Work-groups are handed to the device's XCDs in
+  // turn (linear index x fastest); renumber them so that each XCD runs one
   // contiguous block of (head group, tile) pairs, head-major: the tiles of a
   // KV head then share one XCD's L2, where the keys they all re-read stay.
   const int tiles = gridDim.x;
   const int total = tiles * gridDim.y;
   const int lin = blockIdx.y * tiles + blockIdx.x;
-  const int xcd = lin % kXcds, local = lin / kXcds;
-  const int full = total / kXcds, rem = total % kXcds;
+  const int nx = a.num_xcds;
+  const int xcd = lin % nx, local = lin / nx;
+  const int full = total / nx, rem = total % nx;
   const int idx = xcd * full + min(xcd, rem) + local;  // a bijection of [0, total)
   prefill_tile_body<E, D, WPW, NT, KSPLIT>(a, idx % tiles, idx / tiles);
 }

@@ -85,7 +85,9 @@ class Device:
         import paged_kv_attention_07_amd as pa
         pa.pa_reshape_and_cache(self.k_new, self.v_new, self.kv, slots)
 
-    def attend(self, num_splits=0, force_mixed=False, shared_prefix=None):
+    def attend(self, num_splits=0, force_mixed=False, shared_prefix=None, plan=None):
+        """`plan`: keyword arguments spelling out a mixed batch's plan
+        (tile_shape, tiles_beside_decode) for pa_attention_mixed."""
         import paged_kv_attention_07_amd as pa
         w = self.w
         if shared_prefix is not None:
@@ -97,11 +99,11 @@ class Device:
                                           w.scale, w.max_seq_len, num_splits=num_splits)
         return pa.pa_attention_mixed(self.q, self.kv, self.block_table, self.seq_lens, self.qsl,
                                      self.num_computed, w.scale, w.max_query_len, w.max_seq_len,
-                                     num_splits=num_splits)
+                                     num_splits=num_splits, **(plan or {}))
 
 
     def cache_and_attend(self, num_splits=0, force_mixed=False, slots=True,
-                         shared_prefix=None):
+                         shared_prefix=None, plan=None):
         """The one-launch step: the attention call stores the new tokens
         itself.  Returns (out, slot_mapping or None); the slot buffer starts
         at -7 so an entry the library does not write shows."""
@@ -124,12 +126,12 @@ class Device:
                                                self.block_table, self.seq_lens, self.qsl,
                                                self.num_computed, w.scale, w.max_query_len,
                                                w.max_seq_len, slot_mapping=sm,
-                                               num_splits=num_splits)
+                                               num_splits=num_splits, **(plan or {}))
         return out, sm
 
 
 def run_step(w, *, poison=True, num_splits=0, force_mixed=False, shared_prefix=None,
-             fused=False):
+             fused=False, plan=None):
     """Slot mapping, scatter and attention on the GPU for one step of `w`
     (fused: one cache-and-attend call).  Returns (pool_before, gpu_slots,
     gpu_pool, gpu_out) as host arrays."""
@@ -138,12 +140,12 @@ def run_step(w, *, poison=True, num_splits=0, force_mixed=False, shared_prefix=N
     dev = Device(w, pool)
     if fused:
         out, slots = dev.cache_and_attend(num_splits=num_splits, force_mixed=force_mixed,
-                                          shared_prefix=shared_prefix)
+                                          shared_prefix=shared_prefix, plan=plan)
     else:
         slots = dev.slot_mapping()
         dev.scatter(slots)
         out = dev.attend(num_splits=num_splits, force_mixed=force_mixed,
-                         shared_prefix=shared_prefix)
+                         shared_prefix=shared_prefix, plan=plan)
     torch.cuda.synchronize()
     return pool, slots.cpu().numpy(), from_device(dev.kv, w.dtype), from_device(out, w.dtype)
 

@@ -283,6 +283,52 @@ def test_cache_and_attend_shared_prefix_checks():
     assert call(R=0, k=None, v=None) == OK
 
 
+def test_plan_follows_device_geometry():
+    """The split is planned from the device's CU count: one wavefront per
+    SIMD (4 per CU) over the KV heads, beside concurrent tiles the slots they
+    leave (4-6 waves per CU), never ranges under 4 blocks; a fixed split is
+    kept as given."""
+    f = pa.pa_plan_decode_ranges
+    for cus in (256, 304, 128, 80, 64, 32):
+        assert f(64, 32, 8, 128, "bf16", 4096, num_cus=cus) == cus * 4 // 8   # decode rows alone
+        beside = f(64, 32, 8, 128, "bf16", 2048, max_query_len=512, num_cus=cus)
+        assert cus * 4 // 8 <= beside <= cus * 6 // 8
+        assert f(64, 32, 8, 128, "bf16", 4096, num_splits=7, num_cus=cus) == 7
+    # the partitioned device gets proportionally fewer ranges
+    assert f(64, 32, 8, 128, "bf16", 4096, num_cus=32) * 8 == f(64, 32, 8, 128, "bf16", 4096,
+                                                               num_cus=256)
+    # fp32 rows of 128 dims take two query heads per wave: twice the waves per
+    # KV head, half the ranges
+    assert f(64, 32, 8, 128, "f32", 4096, num_cus=256) == 64
+    # short batches: no range under 4 blocks
+    assert f(2, 32, 8, 128, "bf16", 64, num_cus=256) == 2
+    with pytest.raises(pa.PAError):
+        f(64, 32, 8, 128, "bf16", 4096, num_cus=0)
+    with pytest.raises(pa.PAError):
+        f(64, 30, 8, 128, "bf16", 4096)
+
+
+def test_planned_mixed_checks():
+    """The planned mixed entries reject plan fields out of range before any
+    launch (null plan = library choice)."""
+    plan_t = pa._MixedPlan
+
+    def call(plan, **kw):
+        a = dict(out=FAKE, q=FAKE, kv=FAKE, NB=64, B=16, Hkv=2, D=64, dtype=1, bt=FAKE,
+                 stride=7, sl=FAKE, qsl=FAKE, nc=FAKE, R=4, T=20, Q=17, L=100, Hq=4,
+                 scale=0.125, ws=FAKE_WS, wsb=16)
+        a.update(kw)
+        return lib.pa_attention_mixed_planned(
+            a["out"], a["q"], a["kv"], a["NB"], a["B"], a["Hkv"], a["D"], a["dtype"], a["bt"],
+            a["stride"], a["sl"], a["qsl"], a["nc"], a["R"], a["T"], a["Q"], a["L"], a["Hq"],
+            a["scale"], a["ws"], a["wsb"], None if plan is None else ctypes.byref(plan), None)
+    assert call(plan_t(0, 2, -1)) == INVALID
+    assert call(plan_t(0, -1, 3)) == INVALID
+    assert call(plan_t(-1, -1, -1)) == INVALID
+    assert call(plan_t(0, 1, 0)) == WORKSPACE        # valid plan: gets to the workspace check
+    assert call(None) == WORKSPACE
+
+
 def test_slot_mapping_checks():
     f = lib.pa_compute_slot_mapping
     assert f(None, FAKE, 7, FAKE, FAKE, 4, 4, 16, None) == INVALID

@@ -100,17 +100,16 @@ def test_mixed_groupings(dtype, Hq, Hkv, D):
     fused_check(_variant(dtype, Hq, Hkv, D, lens, seed=51 + Hq, q_lens=q_lens))
 
 
-@pytest.mark.parametrize("overlap", ["0", "1"])
+@pytest.mark.parametrize("overlap", [0, -1])
 @pytest.mark.parametrize("shape", [0, 1])
-def test_mixed_schedules(overlap, shape, monkeypatch):
+def test_mixed_schedules(overlap, shape):
     """Tiles beside the decode ranges in one launch, or launched apart; both
     tile shapes; a one-request batch (tiles alone)."""
-    monkeypatch.setenv("PA_MIXED_OVERLAP", overlap)
-    monkeypatch.setenv("PA_PREFILL_SHAPE", str(shape))
-    fused_check(workload("mixed_bf16_small"))
+    plan = dict(tiles_beside_decode=overlap, tile_shape=shape)
+    fused_check(workload("mixed_bf16_small"), plan=plan)
     fused_check(_variant("bf16", 32, 8, 128, [300, 40, 129, 2000, 17], seed=61,
-                         q_lens=[100, 1, 64, 1, 1]))
-    fused_check(_variant("f16", 8, 2, 64, [77], seed=62, q_lens=[60]))
+                         q_lens=[100, 1, 64, 1, 1]), plan=plan)
+    fused_check(_variant("f16", 8, 2, 64, [77], seed=62, q_lens=[60]), plan=plan)
 
 
 def test_mixed_decode_rows_only_through_mixed_entry():

@@ -336,15 +336,13 @@ def test_workspace_reused_across_calls():
 # --------------------------------------------------------------------------
 
 
-def _large_prefill_check(name, shape, monkeypatch):
-    import dataclasses
-    monkeypatch.setenv("PA_PREFILL_SHAPE", str(shape))
+def _large_prefill_check(name, shape):
     w = workload(name)
     pool = gu.poisoned_pool(w)
     dev = gu.Device(w, pool)
     slots = dev.slot_mapping()
     dev.scatter(slots)
-    out = gu.from_device(dev.attend(force_mixed=True), w.dtype)
+    out = gu.from_device(dev.attend(force_mixed=True, plan=dict(tile_shape=shape)), w.dtype)
     g_pool = gu.from_device(dev.kv, w.dtype)
     r_slots = oracle.slot_mapping(w.block_table, w.query_start_loc, w.num_computed, 16)
     assert np.array_equal(slots.cpu().numpy(), r_slots)
@@ -362,25 +360,24 @@ def _large_prefill_check(name, shape, monkeypatch):
 
 @pytest.mark.parametrize("shape", [0, 1])
 @pytest.mark.parametrize("name", ["prefill_chunk_2048_bf16", "prefill_batch_4x1024_bf16"])
-def test_large_prefill_sampled(name, shape, monkeypatch):
-    _large_prefill_check(name, shape, monkeypatch)
+def test_large_prefill_sampled(name, shape):
+    _large_prefill_check(name, shape)
 
 
-def test_prefill_8k_sampled(monkeypatch):
-    _large_prefill_check("prefill_8192_bf16", 1, monkeypatch)
+def test_prefill_8k_sampled():
+    _large_prefill_check("prefill_8192_bf16", 1)
 
 
 @pytest.mark.parametrize("shape", [0, 1])
-def test_mixed_all_tile_shapes(shape, monkeypatch):
+def test_mixed_all_tile_shapes(shape):
     """Every prefill tile shape on the small mixed batch and on odd groupings
-    (tiles launched on their own, so the shape knob applies)."""
-    monkeypatch.setenv("PA_PREFILL_SHAPE", str(shape))
-    monkeypatch.setenv("PA_MIXED_OVERLAP", "0")
-    full_check(workload("mixed_bf16_small"))
+    (tiles launched on their own, so the shape applies)."""
+    plan = dict(tile_shape=shape, tiles_beside_decode=0)
+    full_check(workload("mixed_bf16_small"), plan=plan)
     lens = [40, 17, 300, 5, 64, 129, 1, 700]
     q_lens = [40, 2, 33, 1, 16, 100, 1, 64]
     for dtype, Hq, Hkv, D in (("bf16", 8, 8, 128), ("f16", 16, 2, 64), ("bf16", 16, 8, 64)):
-        full_check(_variant(dtype, Hq, Hkv, D, lens, seed=41 + Hq, q_lens=q_lens))
+        full_check(_variant(dtype, Hq, Hkv, D, lens, seed=41 + Hq, q_lens=q_lens), plan=plan)
 
 
 # --------------------------------------------------------------------------
@@ -460,17 +457,17 @@ def test_copy_on_write_parallel_sampling():
     gu.check_close(w, out, ref, what="cow samples")
 
 
-@pytest.mark.parametrize("overlap", ["0", "1"])
-def test_mixed_with_and_without_concurrent_tiles(overlap, monkeypatch):
+@pytest.mark.parametrize("overlap", [0, -1])
+def test_mixed_with_and_without_concurrent_tiles(overlap):
     """The mixed entry runs prefill tiles and decode ranges in one launch by
     default; both schedules give the oracle's rows, including the one-request
     batch (tiles alone)."""
-    monkeypatch.setenv("PA_MIXED_OVERLAP", overlap)
-    full_check(workload("mixed_bf16_small"))
+    plan = dict(tiles_beside_decode=overlap)
+    full_check(workload("mixed_bf16_small"), plan=plan)
     lens = [300, 40, 129, 2000, 17]
     q_lens = [100, 1, 64, 1, 1]
-    full_check(_variant("bf16", 32, 8, 128, lens, seed=91, q_lens=q_lens))
-    full_check(_variant("f16", 8, 2, 64, [77], seed=92, q_lens=[60]))
+    full_check(_variant("bf16", 32, 8, 128, lens, seed=91, q_lens=q_lens), plan=plan)
+    full_check(_variant("f16", 8, 2, 64, [77], seed=92, q_lens=[60]), plan=plan)
 
 
 # --------------------------------------------------------------------------
