@@ -86,14 +86,17 @@ DESCR = {
 # --------------------------------------------------------------------------
 
 
-def alg_counts(w):
+def alg_counts(w, fused: bool = True):
     """Bytes one step must move, and the attention's flops.
 
     attention: K/V of every visible key (logical: per request; unique: each
     physical slot once), q in and out, one table entry per block read and
     three int32 of metadata per request.  step: attention plus the new
     tokens' K/V read from the input and stored into the cache, and their
-    slots written (the one-launch step returns them)."""
+    slots written (the one-launch step returns them).  In the one-launch
+    step (`fused`) the attention takes the new tokens' keys and values from
+    the input rows it reads anyway, so their cache reads are not counted;
+    the three-call step stores them first and reads them back."""
     esz = 4 if w.dtype == "f32" else 2
     Hq, Hkv, D, B = w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size
     T, R = w.num_tokens, w.num_seqs
@@ -123,8 +126,10 @@ def alg_counts(w):
         pairs += n * c + n * (n + 1) // 2
         if n > 1:
             chunk_pairs += n * c + n * (n + 1) // 2
+    reread = 0 if fused else T * kb               # the new rows read back from the cache
     return dict(attn_logical=attn_logical, attn_unique=attn_unique, new_rows=new_rows,
-                step_logical=attn_logical + new_rows, step_unique=attn_unique + new_rows,
+                step_logical=attn_logical - T * kb + reread + new_rows,
+                step_unique=attn_unique - T * kb + reread + new_rows,
                 flops=4 * D * Hq * pairs, chunk_flops=4 * D * Hq * chunk_pairs,
                 kv_bytes_per_token=kb)
 
@@ -358,7 +363,8 @@ class Stepper:
         per step): the host figure is wall time between two synchronisations;
         the GPU figure comes from one pair of HIP events recorded on the
         launch stream before the first and after the last timed step, so no
-        event sits between two steps."""
+        event sits between two steps (an event pair around each step adds
+        ~2 us of event latency per step to what it brackets)."""
         torch = self.torch
         for i in range(warmup):
             self.step(i)
@@ -485,7 +491,7 @@ def measure(key, args, w=None, flushed: int = 0):
     if args.graph and st.fused:
         st.capture()
     ms_step, gpu_ms = st.run(args.steps, args.warmup)
-    c = alg_counts(w)
+    c = alg_counts(w, fused=st.fused)
     print(f"[bench] {key} ({name}): {ms_step * 1e3:.1f} us/step host, {gpu_ms * 1e3:.1f} us/step "
           f"GPU", file=sys.stderr, flush=True)
     res = dict(key=key, w=w, counts=c, ms_step=ms_step, gpu_ms=gpu_ms, fused=st.fused,
@@ -512,22 +518,26 @@ def leg_line(r):
         line["roofline"] = None
         line["note"] = "launch-bound (a 1 MiB pool): microseconds only"
         return line
+    unique = key in UNIQUE_LEGS
+    alg = c["step_unique"] if unique else c["step_logical"]
+    traffic = recorded_traffic(DOMINANT[key], w.name) if r["fused"] else None
     if key in MFMA_LEGS:
         tf = c["chunk_flops"] / gpu_s / 1e12
         line["roofline"] = {
             "bound": "mfma", "achieved": round(tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
-            "traffic": None, "kernel": DOMINANT[key],
-            "alg_flops_per_launch": int(c["chunk_flops"])}
+            "traffic": traffic, "kernel": DOMINANT[key],
+            "alg_flops_per_launch": int(c["chunk_flops"]), "alg_bytes_per_launch": int(alg)}
+    else:
+        gbs = alg / gpu_s / 1e9
+        line["roofline"] = {
+            "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": DOMINANT[key],
+            "alg_bytes_per_launch": int(alg)}
+    if traffic:
+        line["roofline"]["traffic_over_alg_bytes"] = round(traffic / alg, 4)
+    if key in MFMA_LEGS:
         return line
-    unique = key in UNIQUE_LEGS
-    alg = c["step_unique"] if unique else c["step_logical"]
-    gbs = alg / gpu_s / 1e9
-    line["roofline"] = {
-        "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-        "frac": round(gbs / HBM_PEAK_GBS, 4),
-        "traffic": recorded_traffic(DOMINANT[key], w.name), "kernel": DOMINANT[key],
-        "alg_bytes_per_launch": int(alg)}
     if unique:
         line["roofline"]["priced_on"] = "unique bytes (the shared prefix once)"
         line["effective_gbs_logical"] = round(c["step_logical"] / gpu_s / 1e9, 1)
@@ -712,7 +722,8 @@ def main():
         roofline["gpu_us_per_step"] = hl["gpu_us_per_step"]
         roofline["timing"] = ("algorithmic bytes (flops) of the step / GPU time per step from "
                               "one pair of HIP events on the launch stream around the "
-                              f"{args.steps} timed steps")
+                              f"{args.steps} timed steps (the step: the attention launch and "
+                              "its split merge)")
     if head.get("flushed_ms"):
         fm = np.asarray(head["flushed_ms"])
         alg_bytes = roofline.get("alg_bytes_per_launch")
