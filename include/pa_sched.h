@@ -27,7 +27,10 @@
  *   - Prefix caching: at admission, a request's full blocks are looked up in
  *     order until the first miss; hits are shared (reference + 1) and
  *     num_computed_tokens starts at hits * block_size ([P4] §3.5).  At least
- *     one prompt token is always left to compute.
+ *     one prompt token is always left to compute.  A hit needs the block's
+ *     hash and its own token ids (kept with each hashed block) to match, so
+ *     two blocks whose 64-bit hashes collide are never shared by mistake;
+ *     the parent chain is followed through the hashes.
  *   - A step ([P4] §4.2; [P2] §3.3; [P1] §3.2): one token budget
  *     (max_num_batched_tokens) shared by all requests.  Running requests
  *     first, in order: new tokens = min(remaining, threshold if set, budget,

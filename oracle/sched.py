@@ -48,8 +48,10 @@ notes): at least one prompt token is always computed, so a full-prompt hit
 keeps its last block out of the hit list; without chunked prefill a waiting
 request that does not fit stops admission for the step ([P4] §4.2's break;
 [P1] §3.2 shows a skip instead); waiting requests are not admitted in a step
-that preempted; hash collisions are not checked (64-bit hashes); a hash that
-is already registered keeps its first block.
+that preempted; a prefix-cache hit needs the hash and the cached block's own
+token ids to match (two blocks whose hashes collide are never taken for one
+another; the chain itself is followed through the hashes); a hash that is
+already registered keeps its first block.
 """
 
 from __future__ import annotations
@@ -87,6 +89,7 @@ class Block:
     block_id: int
     ref_cnt: int = 0
     hash: Optional[int] = None
+    tokens: Optional[Tuple[int, ...]] = None   # token ids, kept while the block is hashed
 
 
 @dataclasses.dataclass
@@ -136,6 +139,7 @@ class BlockPool:
             if self.cached.get(b.hash) == b.block_id:
                 del self.cached[b.hash]
             b.hash = None
+            b.tokens = None
         b.ref_cnt = 1
         return b.block_id
 
@@ -248,7 +252,8 @@ class Scheduler:
         for k in range(usable):
             parent = block_hash(parent, r.tokens[k * self.B:(k + 1) * self.B])
             bid = self.pool.cached.get(parent)
-            if bid is None:
+            if bid is None or self.pool.blocks[bid].tokens != tuple(
+                    r.tokens[k * self.B:(k + 1) * self.B]):
                 break
             hits.append(bid)
         return hits
@@ -346,6 +351,7 @@ class Scheduler:
             b = self.pool.blocks[r.blocks[k]]
             if b.hash is None:
                 b.hash = hashes[k]
+                b.tokens = tuple(r.tokens[k * self.B:(k + 1) * self.B])
                 self.pool.cached.setdefault(hashes[k], b.block_id)
 
     # ---- invariants ------------------------------------------------------

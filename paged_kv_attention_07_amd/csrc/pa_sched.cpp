@@ -91,6 +91,12 @@ uint64_t xxh64(const uint8_t* p, size_t len, uint64_t seed) {
   return acc;
 }
 
+// Test builds narrow the hash (e.g. -DPA_SCHED_HASH_MASK=0x3f) so that
+// different blocks collide often; the product keeps all 64 bits.
+#ifndef PA_SCHED_HASH_MASK
+#define PA_SCHED_HASH_MASK (~(uint64_t)0)
+#endif
+
 uint64_t block_hash(uint64_t parent, bool has_parent, const int32_t* tokens, int n) {
   // parent (8 bytes) + the block's tokens; blocks are small, so one buffer
   uint8_t stack_buf[8 + 4 * 64];
@@ -107,7 +113,7 @@ uint64_t block_hash(uint64_t parent, bool has_parent, const int32_t* tokens, int
     o = 8;
   }
   memcpy(buf + o, tokens, 4 * (size_t)n);
-  return xxh64(buf, bytes, 0);
+  return xxh64(buf, bytes, 0) & (uint64_t)PA_SCHED_HASH_MASK;
 }
 
 // ---------------------------------------------------------------------------
@@ -137,6 +143,7 @@ struct pa_sched {
   // block pool
   std::vector<int32_t> ref, prev, next;
   std::vector<uint64_t> hash;
+  std::vector<int32_t> tok;  // token ids of each hashed block (block_size per block)
   std::vector<uint8_t> has_hash, in_free;
   int32_t head = -1, tail = -1, num_free = 0;
   std::unordered_map<uint64_t, int32_t> cached;
@@ -254,13 +261,21 @@ struct pa_sched {
     ++preemptions;
   }
 
-  // leading run of cached full blocks, leaving at least one token to compute
+  // leading run of cached full blocks, leaving at least one token to compute;
+  // a hit needs the hash and the block's own token ids to match, so two
+  // blocks whose hashes collide are never mistaken for one another (the
+  // chain is taken on the hash alone: a cached block's parent is the block
+  // with the parent's hash)
   void prefix_hits(Request* r, std::vector<int32_t>& hits) {
     hits.clear();
-    const int usable = ((int)r->tokens.size() - 1) / cfg.block_size;
+    const int B = cfg.block_size;
+    const int usable = ((int)r->tokens.size() - 1) / B;
     for (int k = 0; k < usable; ++k) {
       auto it = cached.find(hash_of(r, k));
-      if (it == cached.end()) break;
+      if (it == cached.end() ||
+          memcmp(tok.data() + (size_t)it->second * B, r->tokens.data() + (size_t)k * B,
+                 sizeof(int32_t) * B) != 0)
+        break;
       hits.push_back(it->second);
     }
   }
@@ -273,6 +288,8 @@ struct pa_sched {
       const uint64_t h = hash_of(r, k);
       hash[b] = h;
       has_hash[b] = 1;
+      memcpy(tok.data() + (size_t)b * cfg.block_size, r->tokens.data() + (size_t)k * cfg.block_size,
+             sizeof(int32_t) * cfg.block_size);
       cached.emplace(h, b);  // an existing entry keeps its block
     }
     if (full > r->num_hashed) r->num_hashed = full;
@@ -300,6 +317,7 @@ int pa_sched_create(const pa_sched_config* config, pa_sched** out) {
   s->prev.assign(n, -1);
   s->next.assign(n, -1);
   s->hash.assign(n, 0);
+  s->tok.assign((size_t)n * config->block_size, 0);
   s->has_hash.assign(n, 0);
   s->in_free.assign(n, 0);
   for (int32_t b = 0; b < n; ++b) s->push_back(b);

@@ -14,17 +14,12 @@ C++ driver of the scheduler's C ABI instead.
 """
 
 import os
-import shutil
 import subprocess
-import sys
-import textwrap
 
 import pytest
 
-ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-CSRC = os.path.join(ROOT, "paged_kv_attention_07_amd", "csrc")
-INCLUDE = os.path.join(ROOT, "include")
-CXX = shutil.which("g++")
+import sched_build
+from sched_build import CXX
 
 pytestmark = pytest.mark.skipif(CXX is None, reason="needs the host C++ compiler")
 
@@ -40,34 +35,7 @@ def _runtime(name):
 
 def _build(tmp_path, extra_sources=(), shared=True):
     out = tmp_path / ("libpa_sched_san.so" if shared else "sched_driver")
-    cmd = [CXX, "-O1", "-g", "-std=c++17", "-fPIC", *SAN_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}",
-           os.path.join(CSRC, "pa_sched.cpp"), *extra_sources, "-o", str(out)]
-    if shared:
-        cmd.insert(1, "-shared")
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    assert r.returncode == 0, r.stderr
-    return str(out)
-
-
-CHILD = textwrap.dedent("""
-    import ctypes, sys, types
-    sys.path.insert(0, {root!r})
-    sys.path.insert(0, {tests!r})
-    # a stand-in package whose `lib` is the sanitized scheduler: the
-    # scheduler wrapper (paged_kv_attention_07_amd/sched.py) binds to it
-    pkg = types.ModuleType("paged_kv_attention_07_amd")
-    pkg.__path__ = [{pkgdir!r}]
-    pkg.lib = ctypes.CDLL({lib!r})
-    class PAError(RuntimeError):
-        def __init__(self, fn, status):
-            self.status = status
-            super().__init__(f"{{fn}}: status {{status}}")
-    pkg.PAError = PAError
-    sys.modules["paged_kv_attention_07_amd"] = pkg
-    import pytest
-    sys.exit(pytest.main(["-q", "-x", "-s", "-p", "no:cacheprovider", "-o", "addopts=",
-                          {test!r}]))
-""")
+    return sched_build.build(out, SAN_FLAGS, extra_sources, shared)
 
 
 def test_sched_parity_under_sanitizers(tmp_path):
@@ -75,14 +43,10 @@ def test_sched_parity_under_sanitizers(tmp_path):
     asan, ubsan = _runtime("libasan.so"), _runtime("libubsan.so")
     if asan is None or ubsan is None:
         pytest.skip("sanitizer runtimes not found")
-    script = CHILD.format(root=ROOT, tests=os.path.join(ROOT, "tests"),
-                          pkgdir=os.path.join(ROOT, "paged_kv_attention_07_amd"), lib=lib,
-                          test=os.path.join(ROOT, "tests", "test_sched_parity.py"))
     env = dict(os.environ, LD_PRELOAD=f"{asan}:{ubsan}",
                ASAN_OPTIONS="detect_leaks=0:abort_on_error=1:halt_on_error=1",
                UBSAN_OPTIONS="halt_on_error=1:print_stacktrace=1")
-    r = subprocess.run([sys.executable, "-c", script], capture_output=True, text=True, env=env,
-                       cwd=str(tmp_path), timeout=600)
+    r = sched_build.run_parity_child(lib, tmp_path, env)
     # the report's first lines name the fault and the scheduler's frames
     tail = r.stdout[-1500:] + "\n" + r.stderr[:3000]
     assert r.returncode == 0, tail
