@@ -273,14 +273,16 @@ __device__ __forceinline__ void prefill_tile_body(const PrefillArgs& a, int bx, 
                               fbase[1] + (int64_t)(key0 - nc) * tok_stride};
     const bool cached = key0 + 15 < min(kend, nfresh);
     const bool all_new = key0 >= nfresh && key0 + 15 < kend;
-    if (cached) {
-      // the common case, with one branch for all copies: a wave-uniform
-      // block address plus a 32-bit per-lane offset
+    if (cached || all_new) {
+      // the common cases, with one branch for all copies: a wave-uniform
+      // base (the cache block, or the new-token rows) plus a 32-bit
+      // per-lane offset
+      const uint8_t* base[2] = {cached ? blk : fblk[0], cached ? blk : fblk[1]};
 #pragma unroll
       for (int hv = 0; hv < 2; ++hv)
 #pragma unroll
         for (int i = 0; i < CPB; ++i)
-          __builtin_amdgcn_global_load_lds(blk + goff[hv][i],
+          __builtin_amdgcn_global_load_lds(base[hv] + goff[hv][i],
                                            stage + hv * S::KBUF + (16 * w4 + S::RPI * i) * S::ROWB,
                                            16, 0, 0);
       return;
@@ -291,14 +293,9 @@ __device__ __forceinline__ void prefill_tile_body(const PrefillArgs& a, int bx, 
       for (int i = 0; i < CPB; ++i) {
         const int rib = S::RPI * i + lane / S::CPR;
         const int key = key0 + rib;
-        const uint8_t* src;
-        if (all_new) {
-          src = fblk[hv] + goff[hv][i];
-        } else {
-          src = key >= kend     ? g_zero_row + zoff[hv][i]
-                : key >= nfresh ? fblk[hv] + goff[hv][i]
-                                : blk + goff[hv][i];
-        }
+        const uint8_t* src = key >= kend     ? g_zero_row + zoff[hv][i]
+                             : key >= nfresh ? fblk[hv] + goff[hv][i]
+                                             : blk + goff[hv][i];
         uint8_t* dst = stage + hv * S::KBUF + (16 * w4 + S::RPI * i) * S::ROWB;
         __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
       }
