@@ -397,8 +397,9 @@ int pa_cache_and_attend_mixed_planned(
 /*
  * pa_plan_decode_ranges -- the split the attention calls would plan on a
  * device with `num_cus` compute units: key ranges per KV head for the decode
- * rows (one wavefront per SIMD, i.e. 4 per CU, beside concurrent prefill
- * tiles the wave slots those leave; no range shorter than 4 blocks).  The
+ * rows (3 wavefronts per CU, i.e. one 4-wave work-group on three CUs in
+ * four; beside concurrent prefill tiles, the wave slots those leave, 4-6 per
+ * CU; no range shorter than 4 blocks).  The
  * calls themselves read the current device's CU and XCD counts (hipGetDevice,
  * hipDeviceGetAttribute; 256 and 8 when no device answers), and so does
  * pa_attention_workspace_size: compute a workspace size with the device

@@ -284,13 +284,13 @@ def test_cache_and_attend_shared_prefix_checks():
 
 
 def test_plan_follows_device_geometry():
-    """The split is planned from the device's CU count: one wavefront per
-    SIMD (4 per CU) over the KV heads, beside concurrent tiles the slots they
-    leave (4-6 waves per CU), never ranges under 4 blocks; a fixed split is
-    kept as given."""
+    """The split is planned from the device's CU count: 3 wavefronts per CU
+    over the KV heads, beside concurrent tiles the slots they leave (4-6
+    waves per CU), never ranges under 4 blocks; a fixed split is kept as
+    given."""
     f = pa.pa_plan_decode_ranges
     for cus in (256, 304, 128, 80, 64, 32):
-        assert f(64, 32, 8, 128, "bf16", 4096, num_cus=cus) == cus * 4 // 8   # decode rows alone
+        assert f(64, 32, 8, 128, "bf16", 4096, num_cus=cus) == cus * 3 // 8   # decode rows alone
         beside = f(64, 32, 8, 128, "bf16", 2048, max_query_len=512, num_cus=cus)
         assert cus * 4 // 8 <= beside <= cus * 6 // 8
         assert f(64, 32, 8, 128, "bf16", 4096, num_splits=7, num_cus=cus) == 7
@@ -299,7 +299,7 @@ def test_plan_follows_device_geometry():
                                                                num_cus=256)
     # fp32 rows of 128 dims take two query heads per wave: twice the waves per
     # KV head, half the ranges
-    assert f(64, 32, 8, 128, "f32", 4096, num_cus=256) == 64
+    assert f(64, 32, 8, 128, "f32", 4096, num_cus=256) == 48
     # short batches: no range under 4 blocks
     assert f(2, 32, 8, 128, "bf16", 64, num_cus=256) == 2
     with pytest.raises(pa.PAError):
