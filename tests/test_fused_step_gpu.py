@@ -159,9 +159,9 @@ def test_full_mixed_step():
     fused_check(workload("mixed_chunked_prefill_bf16"))
 
 
-def test_full_long_context_sampled():
-    w = workload("long_context_decode_bf16")
-    fused_check(w, requests=[0, 7, 15], three_calls=False)
+def test_full_long_context():
+    """All 16 requests of 32768 keys against the oracle; pool bit-exact."""
+    fused_check(workload("long_context_decode_bf16"), three_calls=False)
 
 
 def test_prefill_chunk_2048_sampled():
@@ -218,7 +218,7 @@ def test_shared_prefix_step_edges(dtype, Hq, Hkv, D):
 @pytest.mark.parametrize("seed", [None, 2004])
 def test_shared_prefix_step_full_config(seed):
     """The 256-request batch sharing a 64-block prefix: slots and the whole
-    pool bit-exact, 32 sampled requests against the oracle, every output bit
-    for bit against the three calls."""
+    pool bit-exact, every request against the oracle, every output bit for
+    bit against the three calls."""
     w = workload("prefix_shared_decode_bf16", seed)
-    fused_check(w, requests=list(range(0, 256, 8)), shared_prefix=w.meta["shared_prefix_blocks"])
+    fused_check(w, shared_prefix=w.meta["shared_prefix_blocks"])
