@@ -164,9 +164,9 @@ def test_full_long_context():
     fused_check(workload("long_context_decode_bf16"), three_calls=False)
 
 
-def test_prefill_chunk_2048_sampled():
+def test_prefill_chunk_2048():
     """A 2048-token chunk on cached history: every key of the chunk comes from
-    the input rows; pool bit-exact, sampled rows vs the oracle."""
+    the input rows; pool bit-exact, every row vs the oracle."""
     import oracle
     w = workload("prefill_chunk_2048_bf16")
     pool = gu.poisoned_pool(w)
@@ -177,14 +177,9 @@ def test_prefill_chunk_2048_sampled():
     assert np.array_equal(slots.cpu().numpy(), r_slots)
     r_pool = oracle.reshape_and_cache(pool, w.k_new, w.v_new, r_slots)
     assert np.array_equal(gu.bits(gu.from_device(dev.kv, w.dtype)), gu.bits(r_pool))
-    T = w.num_tokens
-    rng = np.random.default_rng(23)
-    rows = np.unique(np.concatenate([[0, 1, 15, 16, 63, 64, T - 1, T - 2],
-                                     rng.choice(T, 40, replace=False)]))
-    sub = gu.sampled_rows_check(w, out, rows)
-    ref = oracle.paged_attention(sub.q, r_pool, sub.block_table, sub.seq_lens,
-                                 sub.query_start_loc, sub.num_computed, w.scale, w.dtype)
-    gu.check_close(w, out[rows], ref, what="prefill 2048 fused")
+    ref = oracle.paged_attention(w.q, r_pool, w.block_table, w.seq_lens, w.query_start_loc,
+                                 w.num_computed, w.scale, w.dtype)
+    gu.check_close(w, out, ref, what="prefill 2048 fused")
 
 
 # --------------------------------------------------------------------------
