@@ -59,13 +59,14 @@ Plan splits_plan(int num_splits) {
   return p;
 }
 
-// Partition plan for the balanced split: one wavefront per SIMD (one
-// work-group of 4 waves per CU), but no range shorter than a few blocks.
-// With each wave keeping its next block in flight this reads HBM faster than
-// two waves per SIMD on every batch of private sequences measured (16-512
-// requests, 256-8192 keys: 2-4%); the extra waves paid only on a batch whose
-// blocks are mostly shared, i.e. read from cache, which the shared-prefix
-// entry plans for itself.  Beside concurrent prefill tiles the decode rows
+// Partition plan for the balanced split: three wavefronts per CU (one
+// work-group of 4 waves on three CUs in four), but no range shorter than a
+// few blocks.  With each wave keeping its next block in flight this reads
+// HBM faster than one wave per SIMD (~2%), which beat two per SIMD on every
+// batch of private sequences measured (16-512 requests, 256-8192 keys:
+// 2-4%); more waves paid only on a batch whose blocks are mostly shared,
+// i.e. read from cache, which the shared-prefix entry plans for itself.
+// Beside concurrent prefill tiles the decode rows
 // take the slots the tiles leave: the chip's wave slots (8 per CU) minus the
 // tiles of the longest chunk (a lower bound on the tile count), between one
 // and one and a half waves per SIMD.
@@ -121,9 +122,9 @@ int plan_chunks(int num_seqs, int num_kv_heads, int group, int max_seq_len, int 
   const int hg = group / pa::decode_heads_per_wave(dtype, head_dim, group);
   const int64_t blocks_upper = (int64_t)num_seqs * ceil_div(max_seq_len, pa::kBlockSize);
   // decode rows alone: 3 waves per CU (one 4-wave work-group on each of
-  // three CUs in four); measured faster than one wave per SIMD on every
-  // bf16 decode batch here (64 requests: 116.2 -> 114.1 us; 16 x 32K:
-  // 359 -> 352 us), and both beat two per SIMD
+  // three CUs in four); measured faster than one wave per SIMD on the bf16
+  // decode batches tried (64 requests: 116.2 -> 114.1 us; 16 x 32K: 359 ->
+  // 352 us), and both beat two per SIMD
   const int64_t waves = beside_prefill
                             ? waves_beside_prefill(num_kv_heads, group, max_query_len,
                                                    exact_tiles, cus)
