@@ -404,6 +404,7 @@ int mixed_impl(void* out, const void* q, const void* kv_cache, int64_t num_block
     p.max_query_len = max_query_len;
     p.tile_shape = plan.tile_shape;
     p.num_xcds = device_geometry().xcds;
+    p.cus_per_xcd = std::max(1, device_geometry().cus / p.num_xcds);
     p.scale_log2 = a.scale_log2;
     p.fresh = fresh;
     if (tiles_beside_decode(num_seqs, max_query_len, dtype, plan)) {
@@ -656,6 +657,7 @@ int shared_prefix_impl(void* out, const void* q, const void* kv_cache, int64_t n
   p.beside_decode = 1;
   p.tile_shape = -1;
   p.num_xcds = device_geometry().xcds;
+  p.cus_per_xcd = std::max(1, device_geometry().cus / p.num_xcds);
   p.scale_log2 = a.scale_log2;
   p.cascade_rows = num_seqs;
   p.cascade_keys = P * pa::kBlockSize;

@@ -67,6 +67,7 @@ struct PrefillArgs {
   int32_t beside_decode;      // (host) 1: runs concurrently with decode rows
   int32_t tile_shape;         // (host) -1: chosen from the chunk; 0 | 1: forced
   int32_t num_xcds;           // dies of the device, each with its own L2 (>= 1)
+  int32_t cus_per_xcd;        // compute units of one die (>= 1)
   float scale_log2;
   // Shared-prefix pass (cascade_rows > 0): one virtual request whose queries
   // are rows 0 .. cascade_rows - 1 of q and whose keys are the first

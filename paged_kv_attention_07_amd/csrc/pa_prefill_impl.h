@@ -572,7 +572,26 @@ __global__ __launch_bounds__(256 * KSPLIT) __attribute__((amdgpu_waves_per_eu(2,
   const int nx = a.num_xcds;
   const int xcd = lin % nx, local = lin / nx;
   const int full = total / nx, rem = total % nx;
-  const int idx = xcd * full + min(xcd, rem) + local;  // a bijection of [0, total)
+  // Pairing.  A die's dispatcher hands its work-groups to its C compute units
+  // in turn; with D = 128 and one key part two fit on a CU (LDS and
+  // registers), so local k and local k + C run side by side.  The die's
+  // block is heaviest-first, and taken in order CU k would hold the k-th
+  // and the (k + C)-th heaviest: the first CUs get the two heaviest loads
+  // and the last the two lightest.  Taking the second C in reverse gives
+  // CU k the k-th heaviest beside the k-th lightest of the first 2C, and the
+  // CUs' loads even out (the 2048-token chunk's slowest CU finishes ~9%
+  // sooner).  Only where the die's block fits that one round of two slots
+  // per CU (the grid holds up to one empty slot per request beyond the
+  // tiles): with more work-groups the later ones go wherever a slot frees,
+  // heaviest first, and the first round's order measured no better reversed.
+  int slot = local;
+  if (D == 128 && KSPLIT == 1) {
+    const int C = a.cus_per_xcd;
+    const int here = full + (xcd < rem ? 1 : 0);      // this die's work-groups
+    if (here <= 2 * C + a.num_seqs && local >= C && local < 2 * C)
+      slot = C + min(2 * C, here) - 1 - local;
+  }
+  const int idx = xcd * full + min(xcd, rem) + slot;  // a bijection of [0, total)
   prefill_tile_body<E, D, WPW, NT, KSPLIT>(a, idx % tiles, idx / tiles);
 }
 
