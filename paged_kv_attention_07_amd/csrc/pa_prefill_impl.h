@@ -302,11 +302,16 @@ __device__ __forceinline__ void prefill_tile_body(const PrefillArgs& a, int bx, 
     }
   };
 
+  // The running max starts at a finite stand-in for -inf: a token's first
+  // visible key raises it (the rescale of the zero sums and outputs then
+  // multiplies by exp2(-1e30 - m) = 0), and the exponent x * scale - m of a
+  // masked score (-inf) stays -inf even before that, with no guard for an
+  // infinite max on every trip.
   f32x4_t acc[NT][S::NMT];
   float m[NT], lsum[NT];
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
-    m[j] = -INFINITY;
+    m[j] = -1e30f;
     lsum[j] = 0.f;
 #pragma unroll
     for (int mt = 0; mt < S::NMT; ++mt) acc[j][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -368,7 +373,7 @@ __device__ __forceinline__ void prefill_tile_body(const PrefillArgs& a, int bx, 
         for (int mt = 0; mt < S::NMT; ++mt) acc[j][mt] *= alpha;
         m[j] = mu;
       }
-      const float ms = (m[j] == -INFINITY) ? 0.f : m[j];
+      const float ms = m[j];
       float p[4][4];
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt)
@@ -514,7 +519,8 @@ __device__ __forceinline__ void prefill_tile_body(const PrefillArgs& a, int bx, 
       const float m1 = xm[2 * j], l1 = xm[2 * j + 1];
       const float M = fmaxf(m[j], m1);         // m is finite: key 0 is visible
       const float a0 = __builtin_amdgcn_exp2f(m[j] - M);
-      const float a1 = (m1 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m1 - M);
+      // a part that saw no visible key still holds the -1e30 stand-in: weight 0
+      const float a1 = __builtin_amdgcn_exp2f(m1 - M);
       lsum[j] = lsum[j] * a0 + l1 * a1;
       m[j] = M;
 #pragma unroll
