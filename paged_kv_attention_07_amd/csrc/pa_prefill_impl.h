@@ -361,11 +361,16 @@ __device__ __forceinline__ void prefill_tile_body(const PrefillArgs& a, int bx, 
       for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) mx = fmaxf(mx, x[tt][i]);
-      mx = max_over_rows(mx);
-      mx *= a.scale_log2;  // scale > 0: max of scaled = scaled max
-      const float mn = fmaxf(m[j], mx);
-      const bool grow = mn > m[j] + 8.f;
-      if (__any(grow)) {
+      // A token's 64 scores of the trip sit in lanes l, l ^ 16, l ^ 32, l ^ 48
+      // (16 each).  The running max only has to move when the token's max
+      // passes it by more than 8 (lazy rescale), and that happens iff one of
+      // the four lanes' own max does: so the lanes compare their own max,
+      // and the max over the four lanes is formed only in the (rare) trips
+      // where some lane of the wavefront passes (the branch is wavefront-
+      // uniform, so every lane takes part in the exchange).
+      if (__any(mx * a.scale_log2 > m[j] + 8.f)) {  // scale > 0: max of scaled = scaled max
+        const float mn = fmaxf(m[j], max_over_rows(mx) * a.scale_log2);
+        const bool grow = mn > m[j] + 8.f;       // the same in the token's four lanes
         const float mu = grow ? mn : m[j];
         const float alpha = (mu == m[j]) ? 1.f : __builtin_amdgcn_exp2f(m[j] - mu);
         lsum[j] *= alpha;
