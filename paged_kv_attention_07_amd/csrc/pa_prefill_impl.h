@@ -213,6 +213,10 @@ __device__ __forceinline__ void prefill_tile_body(const PrefillArgs& a, int bx, 
     for (int s = 0; s < S::NKS; ++s) {
       const u32x4_t z = {0u, 0u, 0u, 0u};
       qf[j][s] = ok ? load16(qp + s * 64) : z;
+      // the score product works in log2 units: Q carries scale * log2(e)
+      // (rounded once to the element type; see the running max below)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) qf[j][s][w] = scale_pair<E>(qf[j][s][w], a.scale_log2);
     }
   }
 
@@ -302,16 +306,20 @@ __device__ __forceinline__ void prefill_tile_body(const PrefillArgs& a, int bx, 
     }
   };
 
-  // The running max starts at a finite stand-in for -inf: a token's first
-  // visible key raises it (the rescale of the zero sums and outputs then
-  // multiplies by exp2(-1e30 - m) = 0), and the exponent x * scale - m of a
-  // masked score (-inf) stays -inf even before that, with no guard for an
-  // infinite max on every trip.
+  // Running max m of each token, in log2 units.  The score product starts
+  // its accumulator at -m (negm holds -m in all four elements), so the
+  // scores come out as s * scale * log2(e) - m, ready for the exponential.
+  // m is set exactly from the part's first trip (every token that sees any
+  // key of the part sees its first one) and afterwards moves only when a
+  // score passes it by more than 8 (lazy rescale: probabilities stay below
+  // 2^8 and the largest so far at least 1).  A token that sees no key of
+  // the part keeps m = 0 and zero sums.
   f32x4_t acc[NT][S::NMT];
-  float m[NT], lsum[NT];
+  f32x4_t negm[NT];
+  float lsum[NT];
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
-    m[j] = -1e30f;
+    negm[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     lsum[j] = 0.f;
 #pragma unroll
     for (int mt = 0; mt < S::NMT; ++mt) acc[j][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -330,7 +338,7 @@ __device__ __forceinline__ void prefill_tile_body(const PrefillArgs& a, int bx, 
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
 #pragma unroll
-      for (int j = 0; j < NT; ++j) st[j][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < NT; ++j) st[j][tt] = negm[j];
 #pragma unroll
       for (int s = 0; s < S::NKS; ++s) {
         const int row = 16 * tt + n;
@@ -341,11 +349,11 @@ __device__ __forceinline__ void prefill_tile_body(const PrefillArgs& a, int bx, 
       }
     }
     const int key0 = it * kKeysPerIter;
+    const bool first = it == it_begin;         // the part's first trip
     u32x4_t pb[NT][2];
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-      // ---- causal mask on diagonal tiles; scores stay unscaled (the scale,
-      // with log2(e) folded in, is applied inside the exponent below)
+      // ---- causal mask on diagonal tiles (x: the score in log2 units less m)
       float (&x)[4][4] = *reinterpret_cast<float (*)[4][4]>(&st[j][0]);
       if (key0 + kKeysPerIter - 1 > min(nc + sub_start[j], kend - 1)) {
 #pragma unroll
@@ -362,29 +370,33 @@ __device__ __forceinline__ void prefill_tile_body(const PrefillArgs& a, int bx, 
 #pragma unroll
         for (int i = 0; i < 4; ++i) mx = fmaxf(mx, x[tt][i]);
       // A token's 64 scores of the trip sit in lanes l, l ^ 16, l ^ 32, l ^ 48
-      // (16 each).  The running max only has to move when the token's max
-      // passes it by more than 8 (lazy rescale), and that happens iff one of
-      // the four lanes' own max does: so the lanes compare their own max,
-      // and the max over the four lanes is formed only in the (rare) trips
-      // where some lane of the wavefront passes (the branch is wavefront-
-      // uniform, so every lane takes part in the exchange).
-      if (__any(mx * a.scale_log2 > m[j] + 8.f)) {  // scale > 0: max of scaled = scaled max
-        const float mn = fmaxf(m[j], max_over_rows(mx) * a.scale_log2);
-        const bool grow = mn > m[j] + 8.f;       // the same in the token's four lanes
-        const float mu = grow ? mn : m[j];
-        const float alpha = (mu == m[j]) ? 1.f : __builtin_amdgcn_exp2f(m[j] - mu);
-        lsum[j] *= alpha;
+      // (16 each).  m has to move when the token's max passes it by more
+      // than 8, which happens iff one of the four lanes' own max does: so
+      // the lanes test their own max, and the max over the four lanes is
+      // formed only in the (rare) trips where some lane of the wavefront
+      // passes, and in the part's first trip, which sets m (the branch is
+      // wavefront-uniform, so every lane takes part in the exchange).
+      if (first || __any(mx > 8.f)) {
+        const float cmx = max_over_rows(mx);    // the same in the token's four lanes
+        const float d = first ? (cmx == -INFINITY ? 0.f : cmx) : (cmx > 8.f ? cmx : 0.f);
+        if (!first) {                           // first trip: sums and outputs are still 0
+          const float alpha = __builtin_amdgcn_exp2f(-d);
+          lsum[j] *= alpha;
 #pragma unroll
-        for (int mt = 0; mt < S::NMT; ++mt) acc[j][mt] *= alpha;
-        m[j] = mu;
+          for (int mt = 0; mt < S::NMT; ++mt) acc[j][mt] *= alpha;
+        }
+        negm[j] -= d;
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) x[tt][i] -= d;
       }
-      const float ms = m[j];
       float p[4][4];
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          p[tt][i] = __builtin_amdgcn_exp2f(fmaf(x[tt][i], a.scale_log2, -ms));
+          p[tt][i] = __builtin_amdgcn_exp2f(x[tt][i]);
           lsum[j] += p[tt][i];
         }
       // lane group g holds keys 32s2 + 4g + (0..3) and 32s2 + 16 + 4g + (0..3)
@@ -494,9 +506,11 @@ __device__ __forceinline__ void prefill_tile_body(const PrefillArgs& a, int bx, 
   }
   if constexpr (KSPLIT == 2) __syncthreads();  // stages are reused for the merge
 
+  float m[NT];
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
     lsum[j] = sum_over_rows(lsum[j]);
+    m[j] = -negm[j][0];
   }
   if constexpr (KSPLIT == 2) {
     // ---- merge the parts: part 1 leaves (max, row sum, O^T) in its LDS stages
@@ -521,11 +535,13 @@ __device__ __forceinline__ void prefill_tile_body(const PrefillArgs& a, int bx, 
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
       const float* src = xa + j * S::NMT * 4;
+      // part 0 holds key 0, which every token sees; part 1 may hold none of
+      // a token's keys (then its sum is 0 and its m a placeholder)
       const float m1 = xm[2 * j], l1 = xm[2 * j + 1];
-      const float M = fmaxf(m[j], m1);         // m is finite: key 0 is visible
+      const bool has1 = l1 > 0.f;
+      const float M = has1 ? fmaxf(m[j], m1) : m[j];
       const float a0 = __builtin_amdgcn_exp2f(m[j] - M);
-      // a part that saw no visible key still holds the -1e30 stand-in: weight 0
-      const float a1 = __builtin_amdgcn_exp2f(m1 - M);
+      const float a1 = has1 ? __builtin_amdgcn_exp2f(m1 - M) : 0.f;
       lsum[j] = lsum[j] * a0 + l1 * a1;
       m[j] = M;
 #pragma unroll
