@@ -19,6 +19,9 @@
  *     ([P4] §3.2/§3.3); kv_cache[b][0] is block b's K, kv_cache[b][1] its V.
  *     block_size must be 16; head_dim 64 or 128; dtype one of pa_dtype.
  *     Queries, new keys/values and outputs have the cache's dtype.
+ *   - `scale` (the softmax scale, 1/sqrt(head_dim) on the pages) must be a
+ *     finite number > 0; zero, negative or non-finite scales return
+ *     PA_ERR_INVALID_ARG.
  *   - Host-visible arguments (sizes, dtype, alignment, workspace size) are
  *     checked before anything is launched; a failed check launches nothing
  *     and returns a negative pa_status.  Device-resident metadata (tables,
@@ -44,7 +47,8 @@ typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_F16 = 2 } pa_dtype;
 
 typedef enum {
   PA_OK = 0,
-  PA_ERR_INVALID_ARG = -1, /* null pointer, negative size, bad stride/shape   */
+  PA_ERR_INVALID_ARG = -1, /* null pointer, negative size, bad stride/shape,
+                              scale not finite and > 0                        */
   PA_ERR_UNSUPPORTED = -2, /* block_size != 16, head_dim, dtype, head grouping */
   PA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required      */
   PA_ERR_HIP = -4,         /* a HIP launch reported an error                  */

@@ -273,7 +273,7 @@ static int attention_common(void* out, const void* q, const void* kv_cache, int6
   if (st != PA_OK) return st;
   const int num_splits = plan.num_splits;
   if (num_seqs < 0 || max_seq_len < 0 || bt_stride < 0 || num_splits < 0) return PA_ERR_INVALID_ARG;
-  if (!isfinite(scale)) return PA_ERR_INVALID_ARG;
+  if (!isfinite(scale) || !(scale > 0.f)) return PA_ERR_INVALID_ARG;  // a softmax temperature
   if (num_seqs == 0) return PA_OK;
   if (!out || !q || !block_table || !seq_lens) return PA_ERR_INVALID_ARG;
   if (!aligned16(out) || !aligned16(q)) return PA_ERR_INVALID_ARG;

@@ -72,14 +72,6 @@ __device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float acc) {
                                 __builtin_bit_cast(f16x2_t, b), acc, false);
 }
 
-// Both halves of a packed 16-bit pair of element type E times c (fp32
-// product, rounded once to E).
-template <typename E>
-__device__ __forceinline__ uint32_t scale_pair(uint32_t w, float c) {
-  if constexpr (E::kind == BF16::kind) return pack_bf16(bf16_lo(w) * c, bf16_hi(w) * c);
-  else return pack_f16(f16_lo(w) * c, f16_hi(w) * c);
-}
-
 // (lo16(a), lo16(b)) and (hi16(a), hi16(b)) as packed pairs.
 __device__ __forceinline__ uint32_t pair_lo(uint32_t a, uint32_t b) {
   return __builtin_amdgcn_perm(b, a, 0x05040100u);

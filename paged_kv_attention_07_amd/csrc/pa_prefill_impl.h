@@ -213,10 +213,6 @@ __device__ __forceinline__ void prefill_tile_body(const PrefillArgs& a, int bx, 
     for (int s = 0; s < S::NKS; ++s) {
       const u32x4_t z = {0u, 0u, 0u, 0u};
       qf[j][s] = ok ? load16(qp + s * 64) : z;
-      // the score product works in log2 units: Q carries scale * log2(e)
-      // (rounded once to the element type; see the running max below)
-#pragma unroll
-      for (int w = 0; w < 4; ++w) qf[j][s][w] = scale_pair<E>(qf[j][s][w], a.scale_log2);
     }
   }
 
@@ -306,17 +302,22 @@ __device__ __forceinline__ void prefill_tile_body(const PrefillArgs& a, int bx, 
     }
   };
 
-  // Running max m of each token, in log2 units.  The score product starts
-  // its accumulator at -m (negm holds -m in all four elements), so the
-  // scores come out as s * scale * log2(e) - m, ready for the exponential.
-  // m is set exactly from the part's first trip (every token that sees any
-  // key of the part sees its first one) and afterwards moves only when a
-  // score passes it by more than 8 (lazy rescale: probabilities stay below
-  // 2^8 and the largest so far at least 1).  A token that sees no key of
-  // the part keeps m = 0 and zero sums.
+  // Running max m of each token's raw scores <q, k>.  The score product
+  // starts its accumulator at -m (negm holds -m in all four elements), so the
+  // scores come out as s - m; the exponent is (s - m) * scale * log2(e),
+  // formed in fp32 (Q stays as given: a Q pre-multiplied by the scale and
+  // rounded to 16 bits would err in proportion to the score's size).  m is
+  // set exactly from the part's first trip (every token that sees any key
+  // of the part sees its first one) and afterwards moves only when a score
+  // passes it by more than 8 / (scale * log2(e)) (lazy rescale:
+  // probabilities stay below 2^8 and the largest so far at least 1).  A
+  // token that sees no key of the part keeps m = 0 and zero sums.  The
+  // scale is positive (checked by the caller).
   f32x4_t acc[NT][S::NMT];
   f32x4_t negm[NT];
   float lsum[NT];
+  const float c = a.scale_log2;
+  const float thr = 8.f / c;                   // a lazy-rescale step in raw score units
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
     negm[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -353,7 +354,7 @@ __device__ __forceinline__ void prefill_tile_body(const PrefillArgs& a, int bx, 
     u32x4_t pb[NT][2];
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-      // ---- causal mask on diagonal tiles (x: the score in log2 units less m)
+      // ---- causal mask on diagonal tiles (x: the raw score less m)
       float (&x)[4][4] = *reinterpret_cast<float (*)[4][4]>(&st[j][0]);
       if (key0 + kKeysPerIter - 1 > min(nc + sub_start[j], kend - 1)) {
 #pragma unroll
@@ -371,16 +372,16 @@ __device__ __forceinline__ void prefill_tile_body(const PrefillArgs& a, int bx, 
         for (int i = 0; i < 4; ++i) mx = fmaxf(mx, x[tt][i]);
       // A token's 64 scores of the trip sit in lanes l, l ^ 16, l ^ 32, l ^ 48
       // (16 each).  m has to move when the token's max passes it by more
-      // than 8, which happens iff one of the four lanes' own max does: so
+      // than thr, which happens iff one of the four lanes' own max does: so
       // the lanes test their own max, and the max over the four lanes is
       // formed only in the (rare) trips where some lane of the wavefront
       // passes, and in the part's first trip, which sets m (the branch is
       // wavefront-uniform, so every lane takes part in the exchange).
-      if (first || __any(mx > 8.f)) {
+      if (first || __any(mx > thr)) {
         const float cmx = max_over_rows(mx);    // the same in the token's four lanes
-        const float d = first ? (cmx == -INFINITY ? 0.f : cmx) : (cmx > 8.f ? cmx : 0.f);
+        const float d = first ? (cmx == -INFINITY ? 0.f : cmx) : (cmx > thr ? cmx : 0.f);
         if (!first) {                           // first trip: sums and outputs are still 0
-          const float alpha = __builtin_amdgcn_exp2f(-d);
+          const float alpha = __builtin_amdgcn_exp2f(-d * c);
           lsum[j] *= alpha;
 #pragma unroll
           for (int mt = 0; mt < S::NMT; ++mt) acc[j][mt] *= alpha;
@@ -396,7 +397,7 @@ __device__ __forceinline__ void prefill_tile_body(const PrefillArgs& a, int bx, 
       for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          p[tt][i] = __builtin_amdgcn_exp2f(x[tt][i]);
+          p[tt][i] = __builtin_amdgcn_exp2f(x[tt][i] * c);
           lsum[j] += p[tt][i];
         }
       // lane group g holds keys 32s2 + 4g + (0..3) and 32s2 + 16 + 4g + (0..3)
@@ -510,7 +511,7 @@ __device__ __forceinline__ void prefill_tile_body(const PrefillArgs& a, int bx, 
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
     lsum[j] = sum_over_rows(lsum[j]);
-    m[j] = -negm[j][0];
+    m[j] = -negm[j][0] * c;                    // in log2 units, as the partials carry it
   }
   if constexpr (KSPLIT == 2) {
     // ---- merge the parts: part 1 leaves (max, row sum, O^T) in its LDS stages

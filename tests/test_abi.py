@@ -137,6 +137,9 @@ def test_decode_checks():
     assert decode(Hq=32, Hkv=2) == UNSUPPORTED            # group 16
     assert decode(stride=3) == INVALID                    # table narrower than max_seq_len
     assert decode(scale=float("nan")) == INVALID
+    assert decode(scale=float("inf")) == INVALID
+    assert decode(scale=0.0) == INVALID                   # the scale is a positive temperature
+    assert decode(scale=-0.125) == INVALID
     assert decode(S=-1) == INVALID
     assert decode(ws=None) == WORKSPACE
     assert decode(wsb=16) == WORKSPACE

@@ -383,6 +383,55 @@ def test_prefill_8k_rows_as_own_requests():
     _large_prefill_check("prefill_8192_bf16", 1, sampled=True)
 
 
+@pytest.mark.parametrize("scale", [0.01, 0.25, 0.5, 1.0, 2.0])
+def test_softmax_scales(scale):
+    """Softmax scales other than the pages' 1/sqrt(d_k) (0.088 at D = 128):
+    nearly uniform weights, and scales large enough that the scores span
+    tens of log2 units and the running max moves on most trips.  Decode
+    rows, both tile shapes, tiles beside decode rows, f16 tiles and the fp32
+    vector-ALU tiles.
+
+    Bound: up to 0.5 the bf16/f16 bound of the other tests.  From 1.0 on one
+    key carries most of a row's weight, so the matrix-core tiles' 16-bit
+    probabilities (relative rounding 2^-9 each) no longer average out: the
+    error approaches 2^-9 * max|V| (~4.5 here) plus the output's own rounding
+    (half an ulp of |out|, up to 2^-7 at |out| ~ 4), so max-abs 3e-2 there;
+    the mean-abs bound is unchanged.  fp32: the bound grows with the scale
+    from 0.25 on (see below).  The error must not grow with the
+    scores' size beyond that (a Q pre-multiplied by the scale and rounded to
+    16 bits did: 0.08 at scale 1, 0.16 at 2)."""
+    import dataclasses
+    lens = [40, 17, 300, 5, 64, 129, 1, 700]
+    q_lens = [40, 2, 33, 1, 16, 100, 1, 64]
+    cases = [(workload("mixed_bf16_small"), None)]
+    cases += [(workload("mixed_bf16_small"), dict(tile_shape=sh, tiles_beside_decode=0))
+              for sh in (0, 1)]
+    cases += [(workload("decode_bf16_small"), None)]
+    cases += [(_variant(dt, Hq, Hkv, D, lens, seed=61 + Hq, q_lens=q_lens), None)
+              for dt, Hq, Hkv, D in (("f32", 8, 2, 64), ("f16", 16, 2, 64))]
+    for base, plan in cases:
+        w = dataclasses.replace(base, scale=scale)
+        print(f"[case] scale {scale} {w.name} plan={plan}", flush=True)
+        pool, g_slots, g_pool, g_out = gu.run_step(w, plan=plan)
+        r_slots, r_pool, r_out = gu.oracle_step(w, pool)
+        assert np.array_equal(g_slots, r_slots)
+        assert np.array_equal(gu.bits(g_pool), gu.bits(r_pool))
+        got = oracle.decode_bits(g_out, w.dtype)
+        assert np.all(np.isfinite(got))
+        err = np.abs(got - r_out)
+        tol = gu.TOL[w.dtype]
+        if w.dtype == "f32":
+            # fp32 throughout: the exponent's rounding grows with the score's
+            # size in log2 units, linearly in the scale (the bound of the other
+            # tests holds up to ~0.25)
+            max_abs = mean_abs = tol["max_abs"] * max(1.0, 4.0 * scale)
+        else:
+            max_abs = tol["max_abs"] if scale <= 0.5 else 3e-2
+            mean_abs = tol["mean_abs"]
+        assert err.max() <= max_abs, f"{w.name} scale {scale}: max abs err {err.max():.3g}"
+        assert err.mean() <= mean_abs, f"{w.name} scale {scale}: mean abs err {err.mean():.3g}"
+
+
 @pytest.mark.parametrize("shape", [0, 1])
 def test_mixed_all_tile_shapes(shape):
     """Every prefill tile shape on the small mixed batch and on odd groupings
