@@ -7,7 +7,9 @@
   them shorter than a block;
 - a 256-request mixed batch (192 decode rows of up to 1,024 tokens beside
   64 chunks of 2-100 tokens on up to 2,000 cached ones) in one launch: 256 is
-  the largest max_num_seqs of the sweep in "vLLM 架构源码解析（一）" §5.2.
+  the largest max_num_seqs of the sweep in "vLLM 架构源码解析（一）" §5.2;
+- a 130-token chunk on 32,768 cached tokens: matrix-core tiles whose key
+  loop runs ~515 trips.
 
 Each runs the one-launch step and the three calls; slots and the whole pool
 bit-exact, outputs to the bf16 tolerance of the other parity tests.
@@ -51,7 +53,15 @@ def _wide_mixed():
                           requests=[reqs[i] for i in order], seed=6103)
 
 
-CASES = {"longest": _longest, "many_short": _many_short, "wide_mixed": _wide_mixed}
+def _long_history_chunk():
+    # a 130-token chunk on 32,768 cached tokens beside two decode rows: ~515
+    # key trips per tile, the running max carried across all of them
+    return build_workload("chunk_on_32k_history", **LLAMA3, num_blocks=4200,
+                          requests=[(32768, 130), (5000, 1), (4375, 1)], seed=6104)
+
+
+CASES = {"longest": _longest, "many_short": _many_short, "wide_mixed": _wide_mixed,
+         "long_history_chunk": _long_history_chunk}
 _REF = {}
 
 
