@@ -35,6 +35,12 @@ struct F16 {
 __device__ __forceinline__ u32x4_t load16(const void* p) {
   return *reinterpret_cast<const u32x4_t*>(p);
 }
+// A 16-byte load marked non-temporal (the load's nt bit): for data a launch
+// reads once, such as decode's stream of K/V blocks, so it is not kept in the
+// caches at the expense of data that is reused.
+__device__ __forceinline__ u32x4_t load16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+}
 __device__ __forceinline__ void store16(void* p, u32x4_t v) {
   *reinterpret_cast<u32x4_t*>(p) = v;
 }

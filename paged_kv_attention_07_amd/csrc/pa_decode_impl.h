@@ -180,13 +180,13 @@ __device__ __forceinline__ void load_rows(BlockRegs<E, D, HPW>& b, const uint8_t
   using S = Shape<E, D, HPW>;
 #pragma unroll
   for (int c = 0; c < S::NCH; ++c) {
-    b.k0[c] = load16(k0 + c * 128);
-    b.k1[c] = load16(k1 + c * 128);
+    b.k0[c] = load16_stream(k0 + c * 128);
+    b.k1[c] = load16_stream(k1 + c * 128);
   }
 #pragma unroll
   for (int c = 0; c < S::NCH; ++c) {
-    b.v0[c] = load16(v0 + c * 128);
-    b.v1[c] = load16(v1 + c * 128);
+    b.v0[c] = load16_stream(v0 + c * 128);
+    b.v1[c] = load16_stream(v1 + c * 128);
   }
 }
 

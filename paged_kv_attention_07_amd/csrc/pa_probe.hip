@@ -1,5 +1,6 @@
 // Read-bandwidth probe (pa_read_probe): a plain streaming read of a device
-// buffer, the achievable-bandwidth reference of the decode kernels.
+// buffer, the achievable-bandwidth reference of the decode kernels.  Its
+// loads carry the non-temporal hint, as the decode kernels' K/V loads do.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -26,12 +27,13 @@ __global__ __launch_bounds__(256) void read_probe_kernel(const u32x4_t* src, int
   for (; i + kStep <= end; i += kStep) {
     u32x4_t v[kInFlight];
 #pragma unroll
-    for (int k = 0; k < kInFlight; ++k) v[k] = src[i + (wave * kInFlight + k) * 64 + lane];
+    for (int k = 0; k < kInFlight; ++k)
+      v[k] = __builtin_nontemporal_load(src + i + (wave * kInFlight + k) * 64 + lane);
 #pragma unroll
     for (int k = 0; k < kInFlight; ++k) acc ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
   }
   for (int64_t j = i + threadIdx.x; j < end; j += 256) {
-    const u32x4_t v = src[j];
+    const u32x4_t v = __builtin_nontemporal_load(src + j);
     acc ^= v.x ^ v.y ^ v.z ^ v.w;
   }
   if (acc == 0x9E3779B9u) sink[0] = acc;  // keeps the loads; practically never taken
