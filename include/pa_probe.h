@@ -23,6 +23,8 @@ extern "C" {
  * vector load units and discard them: each work-group of 4 wavefronts reads
  * one contiguous slice, every lane 16 bytes per load with 8 loads in flight,
  * so each load instruction of a wavefront covers 1 KiB of consecutive bytes.
+ * The loads carry the non-temporal hint, as the decode kernels' K/V loads do
+ * (data read once).
  * The grid holds `waves_per_simd` wavefronts per SIMD of the device (1, 2 or
  * 4; the CU count is read from the device).  `sink` (device, 4 bytes) is
  * written only when a checksum of the data equals a value no buffer
